@@ -1,0 +1,256 @@
+"""CPU oracle for the MoE dispatch/combine hot path -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It wraps ``cdl_oracle.c`` (plain C,
+single-threaded, built with gcc) through ctypes and works on numpy arrays;
+it imports nothing from the HIP library's package and shares no code with it.
+
+Every function follows the passage cited in ``cdl_oracle.c``.  All functions
+here are pinned by ``tests/test_oracle_*.py`` (brute force on tiny inputs,
+library routines, closed forms, format-definition tables and invariants); none
+is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "cdl_oracle.c")
+_LIB = os.path.join(_HERE, "libcdl_oracle.so")
+
+GCC_FLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+             "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/libcdl_oracle.so``."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+_i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(dtype=np.int64, flags="C_CONTIGUOUS")
+_u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(dtype=np.uint8, flags="C_CONTIGUOUS")
+_f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+def lib():
+    """Load the oracle library, building it first if nothing is built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_bf16_rne.argtypes = [ctypes.c_float]
+        L.oracle_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_e4m3fn_to_f32.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3fn_to_f32.restype = ctypes.c_float
+        L.oracle_e4m3fn_rne.argtypes = [ctypes.c_float]
+        L.oracle_e4m3fn_rne.restype = ctypes.c_uint8
+        L.oracle_layout.argtypes = [_i32p, _i64, _i32, _i32, _i32, _i32p, _i64p,
+                                    _i32p, _i32p]
+        L.oracle_layout.restype = _i64
+        L.oracle_dispatch.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _u16p]
+        L.oracle_dispatch.restype = None
+        L.oracle_dispatch_ll.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _i32,
+                                         _i32, _i64, _u16p, _i32p, _i32p]
+        L.oracle_dispatch_ll.restype = _i32
+        L.oracle_quant_group_fp8.argtypes = [_u16p, _i64, _u8p,
+                                             ctypes.POINTER(ctypes.c_float)]
+        L.oracle_quant_group_fp8.restype = None
+        L.oracle_dispatch_fp8.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _i64,
+                                          _u8p, _f32p]
+        L.oracle_dispatch_fp8.restype = _i32
+        L.oracle_combine.argtypes = [_u16p, _i64, _i64, _i32p, _f32p, _i64, _i32,
+                                     _u16p]
+        L.oracle_combine.restype = _i64
+        L.oracle_combine_f64.argtypes = [_u16p, _i64, _i64, _i32p, _f32p, _i64,
+                                         _i32, _f64p]
+        L.oracle_combine_f64.restype = None
+        L.oracle_expected_m.argtypes = [_i64, _i32, _i32, _i32]
+        L.oracle_expected_m.restype = _i64
+        L.oracle_bf16_rne_n.argtypes = [_f32p, _i64, _u16p]
+        L.oracle_bf16_rne_n.restype = None
+        L.oracle_bf16_to_f32_n.argtypes = [_u16p, _i64, _f32p]
+        L.oracle_bf16_to_f32_n.restype = None
+        L.oracle_e4m3fn_rne_n.argtypes = [_f32p, _i64, _u8p]
+        L.oracle_e4m3fn_rne_n.restype = None
+        L.oracle_e4m3fn_to_f32_n.argtypes = [_u8p, _i64, _f32p]
+        L.oracle_e4m3fn_to_f32_n.restype = None
+        _lib = L
+    return _lib
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --------------------------------------------------------------------------
+# scalar codecs (format definitions)
+# --------------------------------------------------------------------------
+
+def bf16_to_f32(b: int) -> float:
+    return lib().oracle_bf16_to_f32(int(b))
+
+
+def bf16_rne(v: float) -> int:
+    return int(lib().oracle_bf16_rne(float(v)))
+
+
+def e4m3fn_to_f32(b: int) -> float:
+    return lib().oracle_e4m3fn_to_f32(int(b))
+
+
+def e4m3fn_rne(v: float) -> int:
+    return int(lib().oracle_e4m3fn_rne(float(v)))
+
+
+def bf16_rne_array(v: np.ndarray) -> np.ndarray:
+    v = _c(v, np.float32).reshape(-1)
+    out = np.zeros(v.size, np.uint16)
+    lib().oracle_bf16_rne_n(v, v.size, out)
+    return out
+
+
+def bf16_to_f32_array(b: np.ndarray) -> np.ndarray:
+    b = _c(b, np.uint16).reshape(-1)
+    out = np.zeros(b.size, np.float32)
+    lib().oracle_bf16_to_f32_n(b, b.size, out)
+    return out
+
+
+def e4m3fn_rne_array(v: np.ndarray) -> np.ndarray:
+    v = _c(v, np.float32).reshape(-1)
+    out = np.zeros(v.size, np.uint8)
+    lib().oracle_e4m3fn_rne_n(v, v.size, out)
+    return out
+
+
+def e4m3fn_to_f32_array(b: np.ndarray) -> np.ndarray:
+    b = _c(b, np.uint8).reshape(-1)
+    out = np.zeros(b.size, np.float32)
+    lib().oracle_e4m3fn_to_f32_n(b, b.size, out)
+    return out
+
+
+# --------------------------------------------------------------------------
+# hot-path steps
+# --------------------------------------------------------------------------
+
+def layout(topk_ids: np.ndarray, expert_begin: int, L: int):
+    """Stable counting-sort layout. Returns counts[L] i32, seg_indptr[L+1] i64,
+    src2dst[T*k] i32, reorder_topk_ids[R] i32."""
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    counts = np.zeros(L, np.int32)
+    seg = np.zeros(L + 1, np.int64)
+    src2dst = np.zeros(T * k, np.int32)
+    reorder = np.zeros(max(T * k, 1), np.int32)
+    R = lib().oracle_layout(ids.reshape(-1), T, k, expert_begin, L, counts, seg,
+                            src2dst, reorder)
+    if R < 0:
+        raise MemoryError("oracle_layout failed")
+    return counts, seg, src2dst, reorder[:R].copy()
+
+
+def dispatch(x_bits: np.ndarray, src2dst: np.ndarray, k: int, rows: int,
+             fill: int = 0) -> np.ndarray:
+    """Normal-mode scatter of bf16 rows (uint16 patterns) into [rows, H]."""
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    P = np.full((rows, H), fill, np.uint16)
+    lib().oracle_dispatch(x.reshape(-1), T, H, k, _c(src2dst, np.int32),
+                          P.reshape(-1))
+    return P
+
+
+def dispatch_ll(x_bits: np.ndarray, topk_ids: np.ndarray, expert_begin: int,
+                L: int, cap: int, fill: int = 0):
+    """Low-latency scatter into [L, cap, H]. Returns (B, masked_m, ll_src2dst,
+    overflow)."""
+    x = _c(x_bits, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    T, H = x.shape
+    k = ids.shape[1]
+    B = np.full((L, cap, H), fill, np.uint16)
+    masked_m = np.zeros(L, np.int32)
+    ll = np.zeros(T * k, np.int32)
+    ovf = lib().oracle_dispatch_ll(x.reshape(-1), T, H, k, ids.reshape(-1),
+                                   expert_begin, L, cap, B.reshape(-1), masked_m,
+                                   ll)
+    if ovf < 0:
+        raise MemoryError("oracle_dispatch_ll failed")
+    return B, masked_m, ll, int(ovf)
+
+
+def quant_group_fp8(x_bits: np.ndarray) -> Tuple[np.ndarray, float]:
+    x = _c(x_bits, np.uint16).reshape(-1)
+    q = np.zeros(x.size, np.uint8)
+    s = ctypes.c_float(0.0)
+    lib().oracle_quant_group_fp8(x, x.size, q, ctypes.byref(s))
+    return q, s.value
+
+
+def dispatch_fp8(x_bits: np.ndarray, src2dst: np.ndarray, k: int, rows: int,
+                 group: int = 128):
+    """fp8 normal dispatch: Q [rows, H] u8 and S [rows, H/group] f32."""
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    if H % group:
+        raise ValueError("group must divide H")
+    Q = np.zeros((rows, H), np.uint8)
+    S = np.zeros((rows, H // group), np.float32)
+    rc = lib().oracle_dispatch_fp8(x.reshape(-1), T, H, k, _c(src2dst, np.int32),
+                                   group, Q.reshape(-1), S.reshape(-1))
+    if rc != 0:
+        raise RuntimeError("oracle_dispatch_fp8 failed: %d" % rc)
+    return Q, S
+
+
+def combine(y_bits: np.ndarray, map_: np.ndarray, weights: np.ndarray,
+            T: int, k: int) -> np.ndarray:
+    """Weighted gather-combine; returns bf16 patterns [T, H]."""
+    y = _c(y_bits, np.uint16)
+    H = y.shape[-1]
+    y2 = y.reshape(-1, H) if y.size else np.zeros((0, H), np.uint16)
+    out = np.zeros((T, H), np.uint16)
+    bad = lib().oracle_combine(y2.reshape(-1), y2.shape[0], H, _c(map_, np.int32),
+                               _c(weights, np.float32).reshape(-1), T, k,
+                               out.reshape(-1))
+    if bad < 0:
+        raise MemoryError("oracle_combine failed")
+    if bad:
+        raise ValueError("map holds %d entries beyond y_rows" % bad)
+    return out
+
+
+def combine_f64(y_bits: np.ndarray, map_: np.ndarray, weights: np.ndarray,
+                T: int, k: int) -> np.ndarray:
+    y = _c(y_bits, np.uint16)
+    H = y.shape[-1]
+    y2 = y.reshape(-1, H) if y.size else np.zeros((0, H), np.uint16)
+    out = np.zeros((T, H), np.float64)
+    lib().oracle_combine_f64(y2.reshape(-1), y2.shape[0], H, _c(map_, np.int32),
+                             _c(weights, np.float32).reshape(-1), T, k,
+                             out.reshape(-1))
+    return out
+
+
+def expected_m(T: int, num_ranks: int, k: int, E: int) -> int:
+    return int(lib().oracle_expected_m(T, num_ranks, k, E))

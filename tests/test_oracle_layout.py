@@ -1,0 +1,157 @@
+"""Pins of the oracle's routing layout (CPU only).
+
+The layout is a stable counting sort of the flat top-k slots by local expert.
+It is pinned by: a hand-worked example (tests/golden/layout_worked.txt); a
+pure-Python brute force of the definition, exhaustively over small id grids;
+independent library routines (numpy bincount / cumsum / stable argsort); and
+the invariants of the layout on every workload's router ids.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from combine_dispatch_layout_amd import workloads as W
+
+
+def brute_layout(ids, b, L):
+    """The definition written out, O((T*k)^2)."""
+    flat = [int(v) for v in np.asarray(ids).reshape(-1)]
+    loc = [(v - b) if b <= v < b + L else -1 for v in flat]
+    counts = [sum(1 for e in loc if e == x) for x in range(L)]
+    seg = [0]
+    for c in counts:
+        seg.append(seg[-1] + c)
+    src2dst = []
+    for i, e in enumerate(loc):
+        if e < 0:
+            src2dst.append(-1)
+        else:
+            src2dst.append(seg[e] + sum(1 for i2 in range(i) if loc[i2] == e))
+    R = seg[-1]
+    reorder = [None] * R
+    for i, e in enumerate(loc):
+        if e >= 0:
+            reorder[src2dst[i]] = e
+    return counts, seg, src2dst, reorder
+
+
+def check_same(ids, b, L):
+    c, s, d, r = oracle.layout(np.asarray(ids, np.int32), b, L)
+    bc, bs, bd, br = brute_layout(ids, b, L)
+    assert c.tolist() == bc
+    assert s.tolist() == bs
+    assert d.tolist() == bd
+    assert r.tolist() == br
+
+
+def test_layout_golden(golden):
+    g = {row[0]: row[1:] for row in golden("layout_worked.txt")}
+    T, k, b, L = (int(g[n][0]) for n in ("T", "k", "expert_begin", "L"))
+    ids = np.array([int(v) for v in g["topk_ids"]], np.int32).reshape(T, k)
+    c, s, d, r = oracle.layout(ids, b, L)
+    assert c.tolist() == [int(v) for v in g["counts"]]
+    assert s.tolist() == [int(v) for v in g["seg_indptr"]]
+    assert d.tolist() == [int(v) for v in g["src2dst"]]
+    assert r.tolist() == [int(v) for v in g["reorder_topk_ids"]]
+
+
+def test_layout_exhaustive_small_grids():
+    """Every id assignment over {-1, 0..3} with local range [1, 3) for
+    T*k <= 4 slots (k in 1, 2)."""
+    values = [-1, 0, 1, 2, 3]
+    n_cases = 0
+    for k in (1, 2):
+        for T in range(0, 4 // k + 1):
+            for combo in itertools.product(values, repeat=T * k):
+                check_same(np.array(combo, np.int32).reshape(T, k), 1, 2)
+                n_cases += 1
+    assert n_cases > 700
+
+
+def test_layout_random_tiny_bruteforce():
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        T = int(rng.integers(0, 17))
+        k = int(rng.integers(1, 4))
+        E = int(rng.integers(1, 7))
+        L = int(rng.integers(1, E + 1))
+        b = int(rng.integers(0, E - L + 1))
+        ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+        check_same(ids, b, L)
+
+
+def library_layout(ids, b, L):
+    """counts by bincount, seg_indptr by cumsum, src2dst by inverting a stable
+    argsort on the local expert key (invalid keys sort last)."""
+    flat = np.asarray(ids, np.int64).reshape(-1)
+    loc = flat - b
+    valid = (loc >= 0) & (loc < L)
+    counts = np.bincount(loc[valid], minlength=L).astype(np.int32)
+    seg = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    key = np.where(valid, loc, L)
+    order = np.argsort(key, kind="stable")
+    R = int(valid.sum())
+    src2dst = np.full(flat.size, -1, np.int64)
+    src2dst[order[:R]] = np.arange(R)
+    reorder = key[order[:R]]
+    return counts, seg, src2dst.astype(np.int32), reorder.astype(np.int32)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_layout_matches_library_routines(name):
+    w = W.WORKLOADS[name]
+    ids = W.make_topk_ids(w).numpy()
+    got = oracle.layout(ids, w.expert_begin, w.L)
+    want = library_layout(ids, w.expert_begin, w.L)
+    for a, b_ in zip(got, want):
+        assert np.array_equal(a, b_)
+
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_layout_invariants(name):
+    w = W.WORKLOADS[name]
+    ids = W.make_topk_ids(w).numpy()
+    counts, seg, src2dst, reorder = oracle.layout(ids, w.expert_begin, w.L)
+    loc = ids.reshape(-1).astype(np.int64) - w.expert_begin
+    valid = (loc >= 0) & (loc < w.L)
+    R = int(seg[-1])
+    assert counts.sum() == valid.sum() == R
+    if w.L == w.E:
+        assert R == w.T * w.k                         # every slot is local
+    assert seg[0] == 0 and np.all(np.diff(seg) >= 0)
+    # valid slots map bijectively onto [0, R)
+    d = src2dst[valid]
+    assert np.array_equal(np.sort(d), np.arange(R))
+    assert np.all(src2dst[~valid] == -1)
+    # reorder is nondecreasing and agrees with the segments
+    assert reorder.size == R and np.all(np.diff(reorder) >= 0)
+    for e in range(w.L):
+        assert np.all(reorder[seg[e]:seg[e + 1]] == e)
+    # stability: source slot indices increase within each segment
+    src_of_row = np.empty(R, np.int64)
+    src_of_row[d] = np.nonzero(valid)[0]
+    for e in range(w.L):
+        assert np.all(np.diff(src_of_row[seg[e]:seg[e + 1]]) > 0)
+
+
+def test_layout_empty_batch():
+    c, s, d, r = oracle.layout(np.zeros((0, 8), np.int32), 0, 32)
+    assert c.tolist() == [0] * 32 and s.tolist() == [0] * 33
+    assert d.size == 0 and r.size == 0
+
+
+def test_layout_all_invalid_and_one_hot():
+    ids = np.full((5, 3), -1, np.int32)
+    c, s, d, r = oracle.layout(ids, 0, 4)
+    assert s[-1] == 0 and np.all(d == -1)
+    ids = np.full((5, 3), 2, np.int32)                   # duplicate ids in a token
+    c, s, d, r = oracle.layout(ids, 0, 4)
+    assert c.tolist() == [0, 0, 15, 0]
+    assert d.tolist() == list(range(15))
+
+
+def test_expected_m_golden(golden):
+    for T, n, k, E, want in golden("expected_m.txt"):
+        assert oracle.expected_m(int(T), int(n), int(k), int(E)) == int(want)
