@@ -1,0 +1,24 @@
+"""MI355X (gfx950) hot path of MoE token dispatch and combine for one
+expert-parallel rank: routing layout, normal / low-latency / fp8 row scatter
+and the top-k-weighted gather-combine, as HIP kernels behind the C ABI in
+``include/cdl.h``.  ``api`` is the thin Python binding; ``workloads`` draws
+seeded synthetic inputs.
+"""
+from .api import (  # noqa: F401
+    CDL_STATUS_LL_OVERFLOW,
+    CDL_STATUS_MAP_RANGE,
+    CDL_STATUS_ROWS_OVERFLOW,
+    FP8_GROUP,
+    LIB_PATH,
+    CdlError,
+    Layout,
+    combine,
+    dispatch,
+    dispatch_fp8,
+    dispatch_layout,
+    dispatch_ll,
+    layout_workspace_size,
+    library,
+    ll_expected_m,
+    status_string,
+)

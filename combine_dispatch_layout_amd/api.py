@@ -1,0 +1,279 @@
+"""Python binding of libcdl (argument marshalling only).
+
+Every step of the hot path runs in the HIP kernels of ``libcdl.so``; this
+module checks tensor devices, dtypes and shapes, allocates outputs with torch
+(device memory only) and passes raw pointers and the current HIP stream to
+the C ABI declared in ``include/cdl.h``.  There is no CPU fallback: if the
+library is not built, or a tensor is not on a GPU, the call raises.
+
+The calls mirror the dispatcher pages' flow ([0.4.4 diff]
+_DeepEPDispatcherImplNormal: preprocess -> permute -> post-reorder combine;
+[deepep.py] _DeepEPDispatcherImplLowLatency: low-latency dispatch returning
+masked_m, and combine with the top-k weights):
+
+    lay = dispatch_layout(topk_ids, expert_begin, num_local_experts)
+    rows = dispatch(x, lay)                      # [R, H] bf16, expert-major
+    q, scales = dispatch_fp8(x, lay)             # [R, H] e4m3fn + [R, H/128] f32
+    buf, masked_m, ll_map = dispatch_ll(x, lay, cap)   # [L, cap, H]
+    out = combine(expert_out, lay.src2dst, topk_weights)  # [T, H] bf16
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcdl.so")
+
+CDL_OK = 0
+CDL_STATUS_ROWS_OVERFLOW = 1
+CDL_STATUS_LL_OVERFLOW = 2
+CDL_STATUS_MAP_RANGE = 4
+FP8_GROUP = 128
+
+_lib = None
+
+
+class CdlError(RuntimeError):
+    """A libcdl call returned a negative status code."""
+
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__("%s: %s (code %d)" % (what, status_string(code), code))
+
+
+def library():
+    """Load libcdl.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libcdl.so is not built at %s; run __graft_entry__.build() or "
+                "python -m combine_dispatch_layout_amd.build" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        L.cdl_dispatch_layout_workspace_size.argtypes = [i64, i32, i32]
+        L.cdl_dispatch_layout_workspace_size.restype = sz
+        L.cdl_dispatch_layout.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.cdl_dispatch_layout.restype = ctypes.c_int
+        L.cdl_dispatch.argtypes = [vp, i64, i64, i32, vp, vp, i64, vp, vp]
+        L.cdl_dispatch.restype = ctypes.c_int
+        L.cdl_dispatch_fp8.argtypes = [vp, i64, i64, i32, vp, vp, vp, i64, vp, vp]
+        L.cdl_dispatch_fp8.restype = ctypes.c_int
+        L.cdl_dispatch_ll.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, i64, vp, vp,
+                                      vp, vp, vp]
+        L.cdl_dispatch_ll.restype = ctypes.c_int
+        L.cdl_combine.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, vp, vp]
+        L.cdl_combine.restype = ctypes.c_int
+        L.cdl_ll_expected_m.argtypes = [i64, i32, i32, i32]
+        L.cdl_ll_expected_m.restype = i64
+        L.cdl_status_string.argtypes = [ctypes.c_int]
+        L.cdl_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return library().cdl_status_string(int(code)).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != CDL_OK:
+        raise CdlError(rc, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need_gpu(t: torch.Tensor, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (libcdl has no CPU path)" % name)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None) -> None:
+    _need_gpu(t, name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+
+
+@dataclasses.dataclass
+class Layout:
+    """Caller-owned routing layout: the explicit form of the pages' dispatch
+    ``handle``.  Device tensors; nothing here is synchronised."""
+    T: int
+    k: int
+    expert_begin: int
+    num_local_experts: int
+    topk_ids: torch.Tensor          # [T, k] int32 (global ids)
+    counts: torch.Tensor            # [L] int32
+    seg_indptr: torch.Tensor        # [L+1] int64
+    src2dst: torch.Tensor           # [T*k] int32
+    reorder_buf: torch.Tensor       # [T*k] int32 (first R entries valid)
+
+    def num_rows(self) -> int:
+        """R, the number of dispatched rows (synchronises with the device)."""
+        return int(self.seg_indptr[self.num_local_experts].item())
+
+    @property
+    def reorder_topk_ids(self) -> torch.Tensor:
+        """Local expert of every dispatched row (synchronises for R)."""
+        return self.reorder_buf[: self.num_rows()]
+
+
+def layout_workspace_size(T: int, k: int, L: int) -> int:
+    n = library().cdl_dispatch_layout_workspace_size(T, k, L)
+    if n == 0:
+        raise CdlError(-2, "cdl_dispatch_layout_workspace_size")
+    return int(n)
+
+
+def dispatch_layout(topk_ids: torch.Tensor, expert_begin: int, num_local_experts: int,
+                    workspace: Optional[torch.Tensor] = None) -> Layout:
+    """Per-expert counts, seg_indptr, src2dst and reorder_topk_ids of the
+    rank's slots (global ids outside [expert_begin, expert_begin+L) are
+    invalid).  int64 ids are narrowed to int32 here."""
+    _need_gpu(topk_ids, "topk_ids")
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, k]")
+    if topk_ids.dtype != torch.int32:
+        topk_ids = topk_ids.to(torch.int32)
+    topk_ids = topk_ids.contiguous()
+    T, k = topk_ids.shape
+    L = int(num_local_experts)
+    dev = topk_ids.device
+    ws_bytes = layout_workspace_size(T, k, L)
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    elif workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError("workspace too small: need %d bytes" % ws_bytes)
+    counts = torch.empty(L, dtype=torch.int32, device=dev)
+    seg = torch.empty(L + 1, dtype=torch.int64, device=dev)
+    src2dst = torch.empty(T * k, dtype=torch.int32, device=dev)
+    reorder = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    rc = library().cdl_dispatch_layout(_ptr(topk_ids), T, k, int(expert_begin), L, _ptr(counts),
+                                       _ptr(seg), _ptr(src2dst), _ptr(reorder), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(rc, "cdl_dispatch_layout")
+    return Layout(T, k, int(expert_begin), L, topk_ids, counts, seg, src2dst, reorder)
+
+
+def dispatch(x: torch.Tensor, layout: Layout, out: Optional[torch.Tensor] = None,
+             rows: Optional[int] = None, status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Normal-mode scatter: out[src2dst[t*k+j]] = x[t].  Allocates [R, H]
+    (reading R from the device) unless `out` or `rows` is given."""
+    T, k = layout.T, layout.k
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T = %d" % T)
+    H = x.shape[1]
+    if out is None:
+        n = layout.num_rows() if rows is None else int(rows)
+        out = torch.empty(n, H, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16)
+    if out.dim() != 2 or out.shape[1] != H:
+        raise ValueError("out must be [rows, H]")
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_dispatch(_ptr(x), T, H, k, _ptr(layout.src2dst), _ptr(out), out.shape[0],
+                                _ptr(status), _stream(x.device))
+    _check(rc, "cdl_dispatch")
+    return out
+
+
+def dispatch_fp8(x: torch.Tensor, layout: Layout, out_q: Optional[torch.Tensor] = None,
+                 out_scales: Optional[torch.Tensor] = None, rows: Optional[int] = None,
+                 status: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Normal-mode scatter with per-token groups of 128 quantised to
+    e4m3fn.  Returns (q [rows, H] uint8 holding e4m3fn bytes, scales
+    [rows, H/128] fp32); ``q.view(torch.float8_e4m3fn)`` reinterprets."""
+    T, k = layout.T, layout.k
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T = %d" % T)
+    H = x.shape[1]
+    if H % FP8_GROUP:
+        raise CdlError(-3, "dispatch_fp8 (H must be a multiple of 128)")
+    if out_q is None:
+        n = layout.num_rows() if rows is None else int(rows)
+        out_q = torch.empty(n, H, dtype=torch.uint8, device=x.device)
+    if out_scales is None:
+        out_scales = torch.empty(out_q.shape[0], H // FP8_GROUP, dtype=torch.float32,
+                                 device=x.device)
+    _need(out_q, "out_q", torch.uint8)
+    _need(out_scales, "out_scales", torch.float32, (out_q.shape[0], H // FP8_GROUP))
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_dispatch_fp8(_ptr(x), T, H, k, _ptr(layout.src2dst), _ptr(out_q),
+                                    _ptr(out_scales), out_q.shape[0], _ptr(status),
+                                    _stream(x.device))
+    _check(rc, "cdl_dispatch_fp8")
+    return out_q, out_scales
+
+
+def dispatch_ll(x: torch.Tensor, layout: Layout, cap: int, out: Optional[torch.Tensor] = None,
+                status: Optional[torch.Tensor] = None):
+    """Low-latency dispatch into a padded [L, cap, H] buffer.  Returns (out,
+    masked_m [L] int32, ll_src2dst [T*k] int32).  Rows at or beyond
+    masked_m[e] are left as they were (never cleared)."""
+    T, k, L = layout.T, layout.k, layout.num_local_experts
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T = %d" % T)
+    H = x.shape[1]
+    if out is None:
+        out = torch.empty(L, cap, H, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (L, cap, H))
+    masked_m = torch.empty(L, dtype=torch.int32, device=x.device)
+    ll_map = torch.empty(T * k, dtype=torch.int32, device=x.device)
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_dispatch_ll(_ptr(x), T, H, k, _ptr(layout.topk_ids), layout.expert_begin,
+                                   L, _ptr(layout.src2dst), _ptr(layout.seg_indptr),
+                                   _ptr(layout.counts), int(cap), _ptr(out), _ptr(masked_m),
+                                   _ptr(ll_map), _ptr(status), _stream(x.device))
+    _check(rc, "cdl_dispatch_ll")
+    return out, masked_m, ll_map
+
+
+def combine(y: torch.Tensor, map_: torch.Tensor, topk_weights: torch.Tensor,
+            out: Optional[torch.Tensor] = None,
+            status: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """out[t] = bf16(sum over valid j of w[t,j] * y[map[t*k+j]]) with fp32
+    accumulation.  `y` is [rows, H] or the low-latency [L, cap, H] buffer;
+    `map_` is src2dst or ll_src2dst."""
+    _need_gpu(y, "y")
+    if y.dtype != torch.bfloat16 or not y.is_contiguous():
+        raise TypeError("y must be a contiguous bfloat16 tensor")
+    H = y.shape[-1]
+    y_rows = y.numel() // H if H else 0
+    _need(topk_weights, "topk_weights", torch.float32)
+    if topk_weights.dim() != 2:
+        raise ValueError("topk_weights must be [T, k]")
+    T, k = topk_weights.shape
+    _need(map_, "map", torch.int32, (T * k,))
+    if out is None:
+        out = torch.empty(T, H, dtype=torch.bfloat16, device=y.device)
+    _need(out, "out", torch.bfloat16, (T, H))
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_combine(_ptr(y), y_rows, H, _ptr(map_), _ptr(topk_weights), T, k,
+                               _ptr(out), _ptr(status), _stream(y.device))
+    _check(rc, "cdl_combine")
+    return out
+
+
+def ll_expected_m(T: int, num_ranks: int, k: int, num_experts: int) -> int:
+    return int(library().cdl_ll_expected_m(T, num_ranks, k, num_experts))

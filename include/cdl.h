@@ -1,0 +1,219 @@
+/*
+ * cdl.h -- C ABI of libcdl, the MI355X (gfx950) hot path of MoE token
+ * dispatch and combine for one expert-parallel rank.
+ *
+ * The operations follow the dispatcher pages' statement of the problem:
+ *   [deepep.py]   SGLang python/sglang/srt/layers/moe/token_dispatcher/deepep.py
+ *   [0.4.4 diff]  sglang 0.4.4.post2 -> 0.4.4.post4 wheel diff,
+ *                 sglang/srt/layers/moe/ep_moe/token_dispatcher.py
+ *   [flashinfer.py] SGLang .../token_dispatcher/flashinfer.py
+ *
+ *   layout  (routing histogram, prefix sum, stable slot ranks)
+ *     -> dispatch (row scatter: normal / low-latency padded / fp8 groups)
+ *     -> [expert computation, outside this library]
+ *     -> combine (gather + top-k-weighted sum per token, fp32 accumulation)
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers (hipMalloc'd or equivalent) to
+ *     row-major, densely packed arrays, unless stated otherwise.  bf16 values
+ *     are passed as their 16-bit patterns (uint16_t); fp8 values are OCP
+ *     E4M3FN bytes (uint8_t).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on that stream and returns; nothing is
+ *     synchronised and no host copy of a device value is made.
+ *   - The library never allocates or frees memory and holds no global state;
+ *     the caller owns every buffer (including the layout workspace) and the
+ *     "handle" that links a dispatch to its combine is the caller-owned set of
+ *     arrays (src2dst, seg_indptr, counts, ll_src2dst).  Calls are
+ *     thread-safe; calls that write the same buffers must be ordered by the
+ *     caller (same stream or events).
+ *   - Sizes: T = tokens held by this rank, H = hidden size, k = top-k
+ *     (1..CDL_MAX_TOPK), L = local experts (1..CDL_MAX_LOCAL_EXPERTS),
+ *     flat slot i = t*k + j.  T*k must be below 2^31.
+ *   - A slot is valid for this rank iff expert_begin <= topk_ids[i] <
+ *     expert_begin + L; its local expert is e_i = topk_ids[i] - expert_begin.
+ *     Every other id (-1 as DeepEP marks unrouted slots, num_experts as
+ *     FlashInfer's invalid id, other ranks' experts) is invalid and is
+ *     dropped.
+ *   - Return value: CDL_OK (0) or a negative CDL_ERR_* code.  Argument errors
+ *     are detected on the host before any HIP call, so no work is enqueued.
+ *     CDL_ERR_HIP means a launch failed.
+ *   - Data-dependent faults (too few output rows, low-latency capacity
+ *     overflow, combine map beyond the expert-output rows) never write out of
+ *     bounds: the offending row is dropped and a CDL_STATUS_* bit is OR-ed into
+ *     the caller's device int32 `status` word (the caller zeroes it; a NULL
+ *     status pointer disables the report, not the check).
+ */
+#ifndef CDL_H
+#define CDL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define CDL_OK 0
+#define CDL_ERR_NULL_POINTER (-1)   /* a required pointer is NULL */
+#define CDL_ERR_BAD_SIZE (-2)       /* negative size, k or L out of range */
+#define CDL_ERR_UNSUPPORTED (-3)    /* shape the operation does not support */
+#define CDL_ERR_WORKSPACE (-4)      /* workspace smaller than required */
+#define CDL_ERR_TOO_LARGE (-5)      /* T*k (or a row index) needs >= 2^31 */
+#define CDL_ERR_HIP (-6)            /* a kernel launch failed */
+
+/* device status bits */
+#define CDL_STATUS_ROWS_OVERFLOW 1  /* a destination row >= cap_rows */
+#define CDL_STATUS_LL_OVERFLOW 2    /* an expert received more than cap rows */
+#define CDL_STATUS_MAP_RANGE 4      /* a combine map entry >= y_rows */
+
+#define CDL_MAX_TOPK 64
+#define CDL_MAX_LOCAL_EXPERTS 2048
+#define CDL_FP8_GROUP 128
+
+/*
+ * cdl_dispatch_layout_workspace_size -- bytes of device workspace that
+ * cdl_dispatch_layout needs for T tokens, top-k k and L local experts
+ * (per-tile expert counts).  Returns 0 for sizes the layout rejects.
+ * Workspace sizing is the one-GPU counterpart of the pages' buffer size
+ * hints ([deepep.py], DeepEPBuffer.get_deepep_buffer).
+ */
+size_t cdl_dispatch_layout_workspace_size(int64_t T, int32_t k, int32_t L);
+
+/*
+ * cdl_dispatch_layout -- the routing layout of the received tokens.
+ *
+ * Defined by the permute's preprocess ([0.4.4 diff],
+ * _DeepEPDispatcherImplNormal._deepep_permute: deepep_run_moe_deep_preprocess
+ * returns reorder_topk_ids, src2dst and seg_indptr, and the permuted buffer has
+ * reorder_topk_ids.numel() rows) and the per-expert token counts of the
+ * dispatch layout ([deepep.py], _DeepEPDispatcherImplNormal._dispatch_core:
+ * get_dispatch_layout's num_tokens_per_expert).
+ *
+ *   topk_ids         in   [T, k] int32 global expert ids
+ *   counts           out  [L] int32:  counts[e] = #{i : e_i = e}
+ *   seg_indptr       out  [L+1] int64: exclusive prefix sum of counts;
+ *                         seg_indptr[L] = R, the number of dispatched rows
+ *   src2dst          out  [T*k] int32: destination row of each valid slot,
+ *                         seg_indptr[e_i] + #{i' < i : e_i' = e_i} (rows of
+ *                         one expert keep the flat slot order); -1 if invalid
+ *   reorder_topk_ids out  [T*k] int32 capacity; the first R entries receive
+ *                         the local expert of each dispatched row (so they are
+ *                         nondecreasing); the rest are left untouched
+ *   ws, ws_bytes          workspace of at least
+ *                         cdl_dispatch_layout_workspace_size(T, k, L) bytes;
+ *                         its contents need no initialisation
+ * T == 0 is allowed: counts and seg_indptr are zero-filled (as the pages'
+ * empty-batch path), topk_ids/src2dst/reorder may be NULL.
+ */
+int cdl_dispatch_layout(const int32_t *topk_ids, int64_t T, int32_t k,
+                        int32_t expert_begin, int32_t L, int32_t *counts,
+                        int64_t *seg_indptr, int32_t *src2dst,
+                        int32_t *reorder_topk_ids, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/*
+ * cdl_dispatch -- normal-mode bf16 row scatter ([0.4.4 diff],
+ * _deepep_permute: the PreReorder permute copies every token row to the
+ * destination rows src2dst names; it takes no weights).
+ *
+ *   x        in   [T, H] bf16 token rows
+ *   src2dst  in   [T*k] int32 from cdl_dispatch_layout
+ *   out      out  [cap_rows, H] bf16; out[src2dst[t*k+j], :] = x[t, :] bit for
+ *                 bit for every valid slot; no other row is written
+ *   cap_rows      rows allocated in `out` (normally R); a destination at or
+ *                 beyond it is dropped and sets CDL_STATUS_ROWS_OVERFLOW
+ *   status   out  device int32 status word (may be NULL)
+ * Any H >= 1 is accepted (H % 8 == 0 with 16-byte aligned rows takes the
+ * vector path).
+ */
+int cdl_dispatch(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                 const int32_t *src2dst, uint16_t *out, int64_t cap_rows,
+                 int32_t *status, void *stream);
+
+/*
+ * cdl_dispatch_fp8 -- normal-mode scatter with per-token, per-group fp8
+ * quantisation on the way ([deepep.py], _DeepEPDispatcherImplNormal.dispatch_a:
+ * the per-token group quant with a hard-coded group of 128 before a normal
+ * fp8 dispatch; scales row-major fp32).
+ *
+ * For every token row with at least one valid slot and every group g of
+ * CDL_FP8_GROUP contiguous elements: a = max |x|, s = a / 448 (IEEE binary32
+ * division), q = e4m3fn_rne(clamp(x / s, -448, 448)) (a = 0 gives s = 0 and
+ * the signed zero of each element).  The (q, s) row is written to every
+ * destination row.
+ *
+ *   out_q       out  [cap_rows, H] E4M3FN bytes
+ *   out_scales  out  [cap_rows, H / 128] fp32
+ * Requires H % 128 == 0 (CDL_ERR_UNSUPPORTED otherwise) and 16-byte aligned
+ * rows.
+ */
+int cdl_dispatch_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                     const int32_t *src2dst, uint8_t *out_q, float *out_scales,
+                     int64_t cap_rows, int32_t *status, void *stream);
+
+/*
+ * cdl_dispatch_ll -- low-latency dispatch into a padded per-expert buffer
+ * ([deepep.py], _DeepEPDispatcherImplLowLatency._dispatch_core:
+ * low_latency_dispatch returns the packed receive buffer and its per-expert
+ * counts, which DeepEPLLDispatchOutput carries as masked_m).
+ *
+ *   topk_ids, expert_begin, L   as for cdl_dispatch_layout
+ *   src2dst, seg_indptr, counts from cdl_dispatch_layout on the same ids
+ *   cap         rows per expert in `out`
+ *   out         out [L, cap, H] bf16; the slot of valid (t, j) in expert e_i's
+ *               block is src2dst[i] - seg_indptr[e_i] (ascending token order);
+ *               rows at or beyond masked_m[e] are never written
+ *   masked_m    out [L] int32: min(counts[e], cap)
+ *   ll_src2dst  out [T*k] int32: e_i*cap + slot, or -1 (invalid or dropped)
+ *   status      out device int32 (may be NULL): CDL_STATUS_LL_OVERFLOW when an
+ *               expert has more than cap rows (the extra rows are dropped)
+ */
+int cdl_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                    const int32_t *topk_ids, int32_t expert_begin, int32_t L,
+                    const int32_t *src2dst, const int64_t *seg_indptr,
+                    const int32_t *counts, int64_t cap, uint16_t *out,
+                    int32_t *masked_m, int32_t *ll_src2dst, int32_t *status,
+                    void *stream);
+
+/*
+ * cdl_combine -- gather the expert outputs back and form each token's
+ * top-k-weighted sum ([0.4.4 diff], _DeepEPDispatcherImplNormal.combine_a: the
+ * post-reorder takes the expert outputs, src2dst, topk_ids and topk_weights and
+ * writes [T, H] in the input dtype; [deepep.py],
+ * _DeepEPDispatcherImplLowLatency._combine_core: low_latency_combine takes the
+ * weights too).
+ *
+ *   y             in  [y_rows, H] bf16 expert outputs (the normal buffer, or
+ *                     the low-latency buffer viewed as [L*cap, H])
+ *   map           in  [T*k] int32: src2dst (normal) or ll_src2dst (low latency)
+ *   topk_weights  in  [T, k] fp32
+ *   out           out [T, H] bf16:
+ *                     out[t, h] = bf16_rne(fma chain over valid j ascending of
+ *                     w[t, j] * y[map[t*k+j], h], from +0 in fp32);
+ *                     a token with no valid slot gets +0
+ *   status        out device int32 (may be NULL): CDL_STATUS_MAP_RANGE for a
+ *                     map entry >= y_rows (that slot is skipped)
+ * `out` must not overlap `y`.
+ */
+int cdl_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32_t *map,
+                const float *topk_weights, int64_t T, int32_t k, uint16_t *out,
+                int32_t *status, void *stream);
+
+/*
+ * cdl_ll_expected_m -- host-side hint for the masked grouped GEMM after a
+ * low-latency dispatch ([deepep.py], _DeepEPDispatcherImplLowLatency.dispatch_a):
+ * (T * num_ranks * k + E) / E with integer division.  Returns -1 for E <= 0 or
+ * negative sizes.  Pure host function.
+ */
+int64_t cdl_ll_expected_m(int64_t T, int32_t num_ranks, int32_t k, int32_t E);
+
+/* cdl_status_string -- static text for a CDL_OK / CDL_ERR_* return code. */
+const char *cdl_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CDL_H */

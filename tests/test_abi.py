@@ -1,0 +1,149 @@
+"""The C ABI on the CPU: the library loads, exports every entry point that
+include/cdl.h declares, and rejects bad arguments before any HIP call (so
+these tests run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_dispatch_layout_amd as cdl
+import oracle
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "cdl.h")
+
+OK, ENULL, ESIZE, EUNSUP, EWS, EBIG = 0, -1, -2, -3, -4, -5
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+NULL = None
+
+
+def declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cdl_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = cdl.library()
+    names = declared()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    for name, val in [("CDL_STATUS_ROWS_OVERFLOW", cdl.CDL_STATUS_ROWS_OVERFLOW),
+                      ("CDL_STATUS_LL_OVERFLOW", cdl.CDL_STATUS_LL_OVERFLOW),
+                      ("CDL_STATUS_MAP_RANGE", cdl.CDL_STATUS_MAP_RANGE),
+                      ("CDL_FP8_GROUP", cdl.FP8_GROUP)]:
+        m = re.search(r"#define\s+%s\s+\(?(-?\d+)\)?" % name, src)
+        assert m and int(m.group(1)) == val, name
+
+
+def test_status_strings():
+    for code in (OK, ENULL, ESIZE, EUNSUP, EWS, EBIG, -6):
+        s = cdl.status_string(code)
+        assert s and "unknown" not in s
+    assert "unknown" in cdl.status_string(-99)
+
+
+def test_workspace_size():
+    lib = cdl.library()
+    assert lib.cdl_dispatch_layout_workspace_size(4096, 8, 32) >= 32 * 32 * 4
+    assert lib.cdl_dispatch_layout_workspace_size(0, 8, 32) > 0
+    assert lib.cdl_dispatch_layout_workspace_size(-1, 8, 32) == 0
+    assert lib.cdl_dispatch_layout_workspace_size(10, 0, 32) == 0
+    assert lib.cdl_dispatch_layout_workspace_size(10, 8, 0) == 0
+    assert lib.cdl_dispatch_layout_workspace_size(10, 8, 2049) == 0
+    assert lib.cdl_dispatch_layout_workspace_size(1 << 28, 8, 32) == 0
+
+
+def test_expected_m_matches_oracle(golden):
+    for T, n, k, E, want in golden("expected_m.txt"):
+        assert cdl.ll_expected_m(int(T), int(n), int(k), int(E)) == int(want)
+        assert oracle.expected_m(int(T), int(n), int(k), int(E)) == int(want)
+    assert cdl.ll_expected_m(5, 1, 1, 0) == -1
+
+
+def layout_call(T=16, k=2, L=4, ids=FAKE, counts=FAKE, seg=FAKE, s2d=FAKE, reorder=FAKE,
+                ws=FAKE, ws_bytes=1 << 20):
+    return cdl.library().cdl_dispatch_layout(ids, T, k, 0, L, counts, seg, s2d, reorder, ws,
+                                             ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), ESIZE), (dict(k=0), ESIZE), (dict(k=65), ESIZE), (dict(L=0), ESIZE),
+    (dict(L=2049), ESIZE), (dict(T=1 << 28, k=8), EBIG), (dict(counts=NULL), ENULL),
+    (dict(seg=NULL), ENULL), (dict(ids=NULL), ENULL), (dict(s2d=NULL), ENULL),
+    (dict(reorder=NULL), ENULL), (dict(ws=NULL), ENULL), (dict(ws_bytes=16), EWS),
+])
+def test_layout_rejects(kw, code):
+    assert layout_call(**kw) == code
+
+
+def test_dispatch_rejects():
+    lib = cdl.library()
+    # x, T, H, k, src2dst, out, cap_rows, status, stream
+    assert lib.cdl_dispatch(FAKE, 4, 0, 2, FAKE, FAKE, 8, NULL, NULL) == ESIZE
+    assert lib.cdl_dispatch(FAKE, 4, 8, 0, FAKE, FAKE, 8, NULL, NULL) == ESIZE
+    assert lib.cdl_dispatch(FAKE, 4, 8, 2, FAKE, FAKE, -1, NULL, NULL) == ESIZE
+    assert lib.cdl_dispatch(NULL, 4, 8, 2, FAKE, FAKE, 8, NULL, NULL) == ENULL
+    assert lib.cdl_dispatch(FAKE, 4, 8, 2, NULL, FAKE, 8, NULL, NULL) == ENULL
+    assert lib.cdl_dispatch(FAKE, 4, 8, 2, FAKE, NULL, 8, NULL, NULL) == ENULL
+    assert lib.cdl_dispatch(FAKE, 4, 8, 2, FAKE, FAKE, 1 << 31, NULL, NULL) == EBIG
+    assert lib.cdl_dispatch(NULL, 0, 8, 2, NULL, NULL, 0, NULL, NULL) == OK  # empty: no launch
+
+
+def test_dispatch_fp8_rejects():
+    lib = cdl.library()
+    f = lib.cdl_dispatch_fp8
+    assert f(FAKE, 4, 200, 2, FAKE, FAKE, FAKE, 8, NULL, NULL) == EUNSUP
+    assert f(FAKE, 4, 256, 2, FAKE, NULL, FAKE, 8, NULL, NULL) == ENULL
+    assert f(FAKE, 4, 256, 2, FAKE, FAKE, NULL, 8, NULL, NULL) == ENULL
+    assert f(ctypes.c_void_p(0x1008), 4, 256, 2, FAKE, FAKE, FAKE, 8, NULL, NULL) == EUNSUP
+    assert f(NULL, 0, 256, 2, NULL, NULL, NULL, 0, NULL, NULL) == OK
+
+
+def test_dispatch_ll_rejects():
+    lib = cdl.library()
+    f = lib.cdl_dispatch_ll
+    args = [FAKE, 4, 256, 2, FAKE, 0, 8, FAKE, FAKE, FAKE, 16, FAKE, FAKE, FAKE, NULL, NULL]
+
+    def call(**over):
+        a = list(args)
+        names = ["x", "T", "H", "k", "ids", "b", "L", "s2d", "seg", "counts", "cap", "out",
+                 "mm", "ll", "status", "stream"]
+        for n, v in over.items():
+            a[names.index(n)] = v
+        return f(*a)
+
+    assert call(H=100) == EUNSUP
+    assert call(L=0) == ESIZE
+    assert call(cap=-1) == ESIZE
+    assert call(cap=1 << 28, L=16) == EBIG
+    assert call(mm=NULL) == ENULL
+    assert call(ll=NULL) == ENULL
+    assert call(out=NULL) == ENULL
+    assert call(x=ctypes.c_void_p(0x1002)) == EUNSUP
+
+
+def test_combine_rejects():
+    lib = cdl.library()
+    f = lib.cdl_combine
+    # y, y_rows, H, map, w, T, k, out, status, stream
+    assert f(FAKE, 8, 0, FAKE, FAKE, 4, 2, FAKE, NULL, NULL) == ESIZE
+    assert f(FAKE, -1, 8, FAKE, FAKE, 4, 2, FAKE, NULL, NULL) == ESIZE
+    assert f(FAKE, 8, 8, NULL, FAKE, 4, 2, FAKE, NULL, NULL) == ENULL
+    assert f(FAKE, 8, 8, FAKE, NULL, 4, 2, FAKE, NULL, NULL) == ENULL
+    assert f(FAKE, 8, 8, FAKE, FAKE, 4, 2, NULL, NULL, NULL) == ENULL
+    assert f(NULL, 8, 8, FAKE, FAKE, 4, 2, FAKE, NULL, NULL) == ENULL
+    assert f(FAKE, 8, 8, FAKE, FAKE, 4, 99, FAKE, NULL, NULL) == ESIZE
+    assert f(NULL, 0, 8, NULL, NULL, 0, 2, NULL, NULL, NULL) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        cdl.dispatch_layout(torch.zeros(4, 2, dtype=torch.int32), 0, 4)

@@ -1,0 +1,347 @@
+"""GPU parity of the HIP path against the CPU oracle (MI355X only).
+
+Every test calls the C ABI through the Python binding and compares with the
+oracle on the same seeded inputs:
+  * layout (counts, seg_indptr, src2dst, reorder_topk_ids): bit-exact;
+  * normal / low-latency dispatch rows, masked_m, ll_src2dst: bit-exact;
+  * fp8 payload bytes and fp32 scales: bit-exact;
+  * combine: within one bf16 ulp (max |gpu - oracle| / |oracle| <= 7.9e-3,
+    with an absolute allowance of 2^-22 * sum|w*y| where cancellation makes
+    |oracle| tiny); the kernels follow the oracle's fp32 fma order, so the
+    results are also expected to be bit-exact and that is asserted too.
+Sizes span several layout tiles (1024 slots) with a ragged tail; the full
+workload sizes are checked as well (in the launch configuration the
+benchmark uses).
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import combine_dispatch_layout_amd as cdl
+import oracle
+from combine_dispatch_layout_amd import workloads as W
+from gpu_util import DEV, announce, bf16_filled, bits16, npy, status_word, u8
+
+pytestmark = pytest.mark.gpu
+
+REL_TOL = 7.9e-3
+
+
+def combine_close(got_bits, want_bits, mag):
+    g = oracle.bf16_to_f32_array(got_bits).astype(np.float64)
+    w = oracle.bf16_to_f32_array(want_bits).astype(np.float64)
+    err = np.abs(g - w)
+    ok = err <= np.maximum(REL_TOL * np.abs(w), 2.0 ** -22 * mag.reshape(-1))
+    return bool(ok.all()), float((err / np.maximum(np.abs(w), 1e-30)).max(initial=0.0))
+
+
+def magnitude(Ybits, map_, wts, T, k):
+    """sum_j |w_j * y_j| per output element, in fp64 (for the cancellation
+    allowance)."""
+    H = Ybits.shape[-1]
+    y = oracle.bf16_to_f32_array(Ybits).reshape(-1, H).astype(np.float64)
+    mag = np.zeros((T, H))
+    for j in range(k):
+        r = map_.reshape(T, k)[:, j]
+        ok = r >= 0
+        mag[ok] += np.abs(wts[ok, j:j + 1].astype(np.float64)) * np.abs(y[r[ok]])
+    return mag
+
+
+def run_normal(w, x, ids, wts, canary_rows=4):
+    """GPU: layout, dispatch into a canaried buffer, combine of the rows."""
+    xd, idd, wd = x.to(DEV), ids.to(DEV), wts.to(DEV)
+    lay = cdl.dispatch_layout(idd, w.expert_begin, w.L)
+    R = lay.num_rows()
+    buf = bf16_filled(R + canary_rows, w.H, 0x7F7F)
+    st = status_word()
+    cdl.dispatch(xd, lay, out=buf[:R], status=st)
+    outbuf = bf16_filled(w.T + canary_rows, w.H, 0x7F7F)
+    cdl.combine(buf[:R], lay.src2dst, wd, out=outbuf[:w.T], status=st)
+    torch.cuda.synchronize()
+    return lay, R, buf, outbuf, int(st.item())
+
+
+def check_layout(lay, ids, b, L):
+    c, s, d, r = oracle.layout(ids.numpy(), b, L)
+    assert np.array_equal(npy(lay.counts), c)
+    assert np.array_equal(npy(lay.seg_indptr), s)
+    assert np.array_equal(npy(lay.src2dst), d)
+    assert np.array_equal(npy(lay.reorder_topk_ids), r)
+    return c, s, d, r
+
+
+PARITY = [
+    W.WORKLOADS["tiny"],
+    W.WORKLOADS["dsv3_prefill"].scaled(T=1000),                 # 8 tiles, ragged
+    W.WORKLOADS["zipf_prefill"].scaled(T=2000, H=1024),         # 16 tiles, skewed
+    W.WORKLOADS["zipf_prefill"].scaled(T=300, H=4096),
+    W.WORKLOADS["dsv3_prefill"].scaled(T=777, expert_begin=64, H=2048),  # rank 2 of 8
+]
+
+
+@pytest.mark.parametrize("w", PARITY, ids=lambda w: "%s_T%d_H%d_b%d" % (w.name, w.T, w.H, w.expert_begin))
+def test_normal_path_parity(w):
+    announce("normal %s T=%d H=%d b=%d" % (w.name, w.T, w.H, w.expert_begin))
+    x, ids, wts = W.make_inputs(w)
+    lay, R, buf, outbuf, st = run_normal(w, x, ids, wts)
+    assert st == 0
+    c, s, d, r = check_layout(lay, ids, w.expert_begin, w.L)
+    xb = W.bf16_bits(x)
+    P = oracle.dispatch(xb, d, w.k, R)
+    got = bits16(buf)
+    assert np.array_equal(got[:R], P)
+    assert np.all(got[R:] == 0x7F7F)                          # canary rows untouched
+    want = oracle.combine(P, d, wts.numpy(), w.T, w.k)
+    out = bits16(outbuf)
+    assert np.all(out[w.T:] == 0x7F7F)
+    ok, worst = combine_close(out[:w.T], want, magnitude(P, d, wts.numpy(), w.T, w.k))
+    assert ok, worst
+    assert np.array_equal(out[:w.T], want)                   # same fp32 fma order
+
+
+@pytest.mark.parametrize("w", [W.WORKLOADS["fp8_dispatch"].scaled(T=1000),
+                               W.WORKLOADS["fp8_dispatch"].scaled(T=130, H=384, expert_begin=32)],
+                         ids=lambda w: "T%d_H%d" % (w.T, w.H))
+def test_fp8_dispatch_parity(w):
+    announce("fp8 T=%d H=%d" % (w.T, w.H))
+    x, ids, wts = W.make_inputs(w)
+    lay = cdl.dispatch_layout(ids.to(DEV), w.expert_begin, w.L)
+    R = lay.num_rows()
+    G = w.H // 128
+    q = torch.full((R + 2, w.H), 0xA5, dtype=torch.uint8, device=DEV)
+    sc = torch.full((R + 2, G), -7.0, dtype=torch.float32, device=DEV)
+    st = status_word()
+    cdl.dispatch_fp8(x.to(DEV), lay, out_q=q[:R], out_scales=sc[:R], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    _, _, d, _ = check_layout(lay, ids, w.expert_begin, w.L)
+    Q, S = oracle.dispatch_fp8(W.bf16_bits(x), d, w.k, R)
+    gq, gs = u8(q), npy(sc)
+    assert np.array_equal(gq[:R], Q)
+    assert np.array_equal(gs[:R].view(np.uint32), S.view(np.uint32))
+    assert np.all(gq[R:] == 0xA5) and np.all(gs[R:] == -7.0)
+
+
+def test_fp8_every_bf16_value_with_unit_scale():
+    """Groups whose amax is 448 have s = 1, so the GPU's e4m3 conversion sees
+    every bf16 value in [-448, 448] unchanged: all ties, subnormals, signs."""
+    announce("fp8 exhaustive bf16 through s=1 groups")
+    b = np.arange(1 << 16, dtype=np.uint32)
+    v = oracle.bf16_to_f32_array(b.astype(np.uint16))
+    keep = np.isfinite(v) & (np.abs(v) <= 448.0)
+    vals = b[keep].astype(np.uint16)
+    per = 127
+    ngroups = -(-vals.size // per)
+    pad = np.zeros(ngroups * per, np.uint16)
+    pad[:vals.size] = vals
+    rows = np.concatenate([pad.reshape(ngroups, per), np.full((ngroups, 1), 0x43E0, np.uint16)], 1)
+    H = 128 * 8
+    T = -(-ngroups // 8)
+    xb = np.zeros((T * 8, 128), np.uint16)
+    xb[:ngroups] = rows
+    xb = xb.reshape(T, H)
+    ids = torch.arange(T, dtype=torch.int32).reshape(T, 1)
+    lay = cdl.dispatch_layout(ids.to(DEV), 0, T)
+    q, s = cdl.dispatch_fp8(W.bits_to_bf16(xb).to(DEV), lay)
+    torch.cuda.synchronize()
+    _, _, d, _ = oracle.layout(ids.numpy(), 0, T)
+    Q, S = oracle.dispatch_fp8(xb, d, 1, T)
+    assert np.array_equal(u8(q), Q)
+    assert np.array_equal(npy(s).view(np.uint32), S.view(np.uint32))
+    assert np.all(S.reshape(-1)[:ngroups] == 1.0)
+
+
+@pytest.mark.parametrize("cap_mode", ["full", "tight"])
+def test_low_latency_parity(cap_mode):
+    w = W.WORKLOADS["ll_decode"]
+    if cap_mode == "tight":
+        w = w.scaled(T=96, H=512, cap=3)                       # forces overflow
+    announce("ll %s T=%d H=%d cap=%d" % (cap_mode, w.T, w.H, w.cap))
+    x, ids, wts = W.make_inputs(w)
+    xd, idd, wd = x.to(DEV), ids.to(DEV), wts.to(DEV)
+    lay = cdl.dispatch_layout(idd, w.expert_begin, w.L)
+    st = status_word()
+    B = bf16_filled(w.L * w.cap, w.H, 0x7F7F).view(w.L, w.cap, w.H)
+    B, mm, llmap = cdl.dispatch_ll(xd, lay, w.cap, out=B, status=st)
+    out = cdl.combine(B, llmap, wd, status=st)
+    torch.cuda.synchronize()
+    xb = W.bf16_bits(x)
+    OB, omm, oll, ovf = oracle.dispatch_ll(xb, ids.numpy(), w.expert_begin, w.L, w.cap,
+                                           fill=0x7F7F)
+    assert np.array_equal(npy(mm), omm)
+    assert np.array_equal(npy(llmap), oll)
+    assert (int(st.item()) & cdl.CDL_STATUS_LL_OVERFLOW) == (cdl.CDL_STATUS_LL_OVERFLOW if ovf else 0)
+    assert (int(st.item()) & ~cdl.CDL_STATUS_LL_OVERFLOW) == 0
+    # compare the written rows and the first padding rows of every expert
+    gB = B.view(w.L * w.cap, w.H)
+    for e in range(w.L):
+        n = min(int(omm[e]) + 2, w.cap)
+        rows = np.arange(e * w.cap, e * w.cap + n)
+        assert np.array_equal(bits16(gB[torch.from_numpy(rows).to(DEV)]),
+                              OB.reshape(-1, w.H)[rows])
+    want = oracle.combine(OB.reshape(-1, w.H), oll, wts.numpy(), w.T, w.k)
+    assert np.array_equal(bits16(out), want)
+
+
+def test_full_size_dsv3_prefill():
+    """The benchmark's workload at full size: everything compared."""
+    w = W.WORKLOADS["dsv3_prefill"]
+    announce("full dsv3_prefill")
+    x, ids, wts = W.make_inputs(w)
+    lay, R, buf, outbuf, st = run_normal(w, x, ids, wts, canary_rows=2)
+    assert st == 0
+    _, _, d, _ = check_layout(lay, ids, w.expert_begin, w.L)
+    xb = W.bf16_bits(x)
+    P = oracle.dispatch(xb, d, w.k, R)
+    assert np.array_equal(bits16(buf[:R]), P)
+    want = oracle.combine(P, d, wts.numpy(), w.T, w.k)
+    assert np.array_equal(bits16(outbuf[:w.T]), want)
+
+
+def test_full_size_zipf_prefill_sampled():
+    """T=16384, H=4096, E=L=128, Zipf experts: exact layout, sampled rows and
+    sampled combined tokens (the oracle computes them one by one), and the
+    all-local softmax round trip combine(dispatch(x)) == x everywhere."""
+    w = W.WORKLOADS["zipf_prefill"]
+    announce("full zipf_prefill")
+    x, ids, wts = W.make_inputs(w)
+    lay, R, buf, outbuf, st = run_normal(w, x, ids, wts, canary_rows=2)
+    assert st == 0 and R == w.T * w.k
+    _, _, d, _ = check_layout(lay, ids, w.expert_begin, w.L)
+    xb = W.bf16_bits(x)
+    rng = np.random.default_rng(1)
+    slots = rng.choice(w.T * w.k, 4096, replace=False)
+    rows = d[slots]
+    got = bits16(buf[torch.from_numpy(rows.astype(np.int64)).to(DEV)])
+    assert np.array_equal(got, xb[slots // w.k])
+    toks = np.sort(rng.choice(w.T, 512, replace=False))
+    sub_map = d.reshape(w.T, w.k)[toks]
+    sub_rows = np.unique(sub_map[sub_map >= 0])
+    remap = {int(r): i for i, r in enumerate(sub_rows)}
+    # the oracle's row r is x[token of r]; build the sampled rows directly
+    src_tok = np.empty(R, np.int64)
+    src_tok[d] = np.arange(w.T * w.k) // w.k
+    sub_y = xb[src_tok[sub_rows]]
+    m2 = np.array([remap[int(r)] if r >= 0 else -1 for r in sub_map.reshape(-1)], np.int32)
+    want = oracle.combine(sub_y, m2, wts.numpy()[toks], toks.size, w.k)
+    out = bits16(outbuf[:w.T])
+    assert np.array_equal(out[toks], want)
+    assert np.array_equal(out, xb)                            # softmax round trip
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+def test_empty_batch():
+    announce("T=0")
+    ids = torch.zeros(0, 8, dtype=torch.int32, device=DEV)
+    lay = cdl.dispatch_layout(ids, 0, 32)
+    torch.cuda.synchronize()
+    assert npy(lay.counts).tolist() == [0] * 32
+    assert npy(lay.seg_indptr).tolist() == [0] * 33
+    x = torch.zeros(0, 256, dtype=torch.bfloat16, device=DEV)
+    P = cdl.dispatch(x, lay)
+    assert P.shape == (0, 256)
+    out = cdl.combine(P, lay.src2dst, torch.zeros(0, 8, device=DEV))
+    assert out.shape == (0, 256)
+    B, mm, ll = cdl.dispatch_ll(x, lay, 4)
+    torch.cuda.synchronize()
+    assert npy(mm).tolist() == [0] * 32 and ll.numel() == 0
+
+
+@pytest.mark.parametrize("case", ["T1_k1", "all_invalid", "one_hot_expert", "duplicates",
+                                  "odd_H", "H8", "max_L", "max_k"])
+def test_edge_cases(case):
+    announce("edge " + case)
+    g = torch.Generator().manual_seed(zlib.crc32(case.encode()))
+    b, L, E = 0, 16, 64
+    T, k, H = 300, 4, 256
+    if case == "T1_k1":
+        T, k = 1, 1
+        ids = torch.tensor([[3]], dtype=torch.int32)
+    elif case == "all_invalid":
+        ids = torch.randint(L, E, (T, k), generator=g, dtype=torch.int32)
+        ids[::7] = -1
+    elif case == "one_hot_expert":
+        ids = torch.full((T, k), -1, dtype=torch.int32)
+        ids[:, 0] = 5
+    elif case == "duplicates":
+        ids = torch.randint(-1, L + 2, (T, k), generator=g, dtype=torch.int32)
+        ids[:, 1] = ids[:, 0]
+    elif case == "odd_H":
+        H = 100
+        ids = torch.randint(-1, E + 1, (T, k), generator=g, dtype=torch.int32)
+    elif case == "H8":
+        H = 8
+        ids = torch.randint(0, L, (T, k), generator=g, dtype=torch.int32)
+    elif case == "max_L":
+        T, k, L, E, H = 700, 8, 2048, 2048, 64
+        ids = torch.multinomial(torch.ones(T, E), k, generator=g).to(torch.int32)
+    elif case == "max_k":
+        T, k, L, E, H = 200, 64, 128, 128, 128
+        ids = torch.multinomial(torch.ones(T, E), k, generator=g).to(torch.int32)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    wts = torch.randn(T, k, generator=g).softmax(-1)
+    w = W.Workload(case, T=T, H=H, E=E, L=L, k=k, expert_begin=b)
+    lay, R, buf, outbuf, st = run_normal(w, x, ids, wts)
+    assert st == 0
+    _, _, d, _ = check_layout(lay, ids, b, L)
+    P = oracle.dispatch(W.bf16_bits(x), d, k, R)
+    got = bits16(buf)
+    assert np.array_equal(got[:R], P) and np.all(got[R:] == 0x7F7F)
+    want = oracle.combine(P, d, wts.numpy(), T, k)
+    out = bits16(outbuf)
+    assert np.array_equal(out[:T], want) and np.all(out[T:] == 0x7F7F)
+
+
+def test_rows_overflow_flag_and_no_out_of_bounds_write():
+    announce("dispatch cap_rows < R")
+    w = W.WORKLOADS["tiny"]
+    x, ids, wts = W.make_inputs(w)
+    lay = cdl.dispatch_layout(ids.to(DEV), 0, w.L)
+    R = lay.num_rows()
+    cap = R // 2
+    buf = bf16_filled(R, w.H, 0x7F7F)
+    st = status_word()
+    cdl.dispatch(x.to(DEV), lay, out=buf[:cap], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == cdl.CDL_STATUS_ROWS_OVERFLOW
+    _, _, d, _ = oracle.layout(ids.numpy(), 0, w.L)
+    P = oracle.dispatch(W.bf16_bits(x), d, w.k, R)
+    got = bits16(buf)
+    assert np.array_equal(got[:cap], P[:cap]) and np.all(got[cap:] == 0x7F7F)
+
+
+def test_combine_map_range_flag():
+    announce("combine map beyond y_rows")
+    y = torch.randn(4, 64).to(torch.bfloat16).to(DEV)
+    m = torch.tensor([0, 9, 3, -1], dtype=torch.int32, device=DEV)
+    wts = torch.ones(2, 2, device=DEV)
+    st = status_word()
+    out = cdl.combine(y, m, wts, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == cdl.CDL_STATUS_MAP_RANGE
+    assert np.array_equal(bits16(out[0]), bits16(y[0]))
+    assert np.array_equal(bits16(out[1]), bits16(y[3]))
+
+
+def test_fp8_rejects_ragged_groups():
+    ids = torch.zeros(2, 1, dtype=torch.int32, device=DEV)
+    lay = cdl.dispatch_layout(ids, 0, 1)
+    with pytest.raises(cdl.CdlError):
+        cdl.dispatch_fp8(torch.zeros(2, 200, dtype=torch.bfloat16, device=DEV), lay, rows=2)
+
+
+def test_deterministic_repeats():
+    announce("determinism zipf T=4000")
+    w = W.WORKLOADS["zipf_prefill"].scaled(T=4000, H=512)
+    x, ids, wts = W.make_inputs(w)
+    a = run_normal(w, x, ids, wts)
+    b = run_normal(w, x, ids, wts)
+    assert np.array_equal(npy(a[0].src2dst), npy(b[0].src2dst))
+    assert np.array_equal(bits16(a[2]), bits16(b[2]))
+    assert np.array_equal(bits16(a[3]), bits16(b[3]))
