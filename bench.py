@@ -1,0 +1,407 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE token dispatch + combine on one MI355X (one EP rank's share).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_prefill]
+
+A step is one pass of the hot path over one batch of synthetic input already
+resident in HBM: routing layout (counts, seg_indptr, src2dst, reorder ids) ->
+normal bf16 dispatch (row scatter) -> combine (top-k-weighted gather-sum)
+of the dispatched rows (identity expert).  The default workload is the
+DeepSeek-V3-shaped prefill share: T=4096 tokens, H=7168, 256 experts of
+which 32 are local, top-8.
+
+Reported (one JSON line on stdout):
+  value        algorithmic GB/s of the whole step (bytes of the step's
+               definition / measured step time), unit GB/s
+  tokens_per_s T / step time
+  roofline     the dominant kernel (combine): algorithmic bytes per launch /
+               its average launch time from HIP events on the launch stream,
+               against the 8 TB/s HBM3E peak; `traffic` = HBM bytes per launch
+               from rocprofv3 FETCH_SIZE + WRITE_SIZE when a summary taken on
+               the current kernel source is committed, else null
+  cpu_baseline the CPU oracle (single-threaded C) on host copies of the same
+               input, over a bounded number of full steps
+Input/output sets rotate between steps (default 6 sets, > 1 GB in total) so
+that no step finds its input in the 256 MB Infinity Cache; the warm
+(single-set) rate is reported beside it for context.
+
+Only one GPU is supported: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = ("dispatch+combine HBM GB/s and tokens/sec at T=4096,H=7168,k=8 "
+          "(fraction of peak)")
+KERNEL_SOURCE = os.path.join(ROOT, "combine_dispatch_layout_amd", "csrc", "cdl.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "combine_dsv3_prefill_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="dsv3_prefill")
+    p.add_argument("--sets", type=int, default=6,
+                   help="rotating input/output sets (defeats the 256 MB Infinity Cache)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-modes", action="store_true",
+                   help="skip the fp8 / low-latency / Zipf side measurements")
+    return p.parse_args()
+
+
+def source_digest() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per combine launch from a committed rocprofv3 summary, if it
+    was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_sha256") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# one input/output set with pre-bound C calls
+# ---------------------------------------------------------------------------
+
+class NormalSet:
+    """Device buffers of one batch and the three C calls of a step, with
+    every pointer argument bound up front (ctypes overhead only)."""
+
+    def __init__(self, torch, cdl, W, w, dev):
+        self.torch = torch
+        lib = cdl.library()
+        self.lib = lib
+        x, ids, wts = W.make_inputs(w)
+        T, k, L, H = w.T, w.k, w.L, w.H
+        self.T, self.k, self.L, self.H = T, k, L, H
+        self.x_host, self.ids_host, self.w_host = x, ids, wts
+        self.x = x.to(dev)
+        self.ids = ids.to(dev)
+        self.wts = wts.to(dev)
+        i32, i64 = torch.int32, torch.int64
+        self.counts = torch.empty(L, dtype=i32, device=dev)
+        self.seg = torch.empty(L + 1, dtype=i64, device=dev)
+        self.src2dst = torch.empty(T * k, dtype=i32, device=dev)
+        self.reorder = torch.empty(max(T * k, 1), dtype=i32, device=dev)
+        wsb = cdl.layout_workspace_size(T, k, L)
+        self.ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+        self.status = torch.zeros(1, dtype=i32, device=dev)
+        stream = torch.cuda.current_stream(dev).cuda_stream
+        P = ctypes.c_void_p
+        self.stream = P(stream)
+        self.a_layout = (P(self.ids.data_ptr()), T, k, w.expert_begin, L,
+                         P(self.counts.data_ptr()), P(self.seg.data_ptr()),
+                         P(self.src2dst.data_ptr()), P(self.reorder.data_ptr()),
+                         P(self.ws.data_ptr()), wsb, self.stream)
+        self.layout()
+        torch.cuda.synchronize()
+        self.R = int(self.seg[L].item())
+        valid = (self.src2dst.view(T, k) >= 0).any(dim=1)
+        self.U = int(valid.sum().item())
+        self.P = torch.empty(max(self.R, 1), H, dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+        self.a_dispatch = (P(self.x.data_ptr()), T, H, k, P(self.src2dst.data_ptr()),
+                           P(self.P.data_ptr()), self.R, P(self.status.data_ptr()), self.stream)
+        self.a_combine = (P(self.P.data_ptr()), self.R, H, P(self.src2dst.data_ptr()),
+                          P(self.wts.data_ptr()), T, k, P(self.out.data_ptr()),
+                          P(self.status.data_ptr()), self.stream)
+
+    def layout(self):
+        rc = self.lib.cdl_dispatch_layout(*self.a_layout)
+        if rc:
+            raise RuntimeError("cdl_dispatch_layout failed: %d" % rc)
+
+    def dispatch(self):
+        rc = self.lib.cdl_dispatch(*self.a_dispatch)
+        if rc:
+            raise RuntimeError("cdl_dispatch failed: %d" % rc)
+
+    def combine(self):
+        rc = self.lib.cdl_combine(*self.a_combine)
+        if rc:
+            raise RuntimeError("cdl_combine failed: %d" % rc)
+
+    def step(self):
+        self.layout()
+        self.dispatch()
+        self.combine()
+
+    # algorithmic bytes (definitions of the steps; per instance R, U)
+    def bytes_layout(self):
+        T, k, L = self.T, self.k, self.L
+        return 4 * T * k + 4 * T * k + 4 * self.R + 4 * L + 8 * (L + 1)
+
+    def bytes_scatter(self):
+        return 4 * self.T * self.k + 2 * self.U * self.H + 2 * self.R * self.H
+
+    def bytes_combine(self):
+        T, k, H = self.T, self.k, self.H
+        return 4 * T * k + 4 * T * k + 2 * self.R * H + 2 * T * H
+
+    def bytes_step(self):
+        # dispatch (layout + scatter, the ids read once) + combine
+        return (self.bytes_layout() + 2 * self.U * self.H + 2 * self.R * self.H
+                + self.bytes_combine())
+
+
+def time_steps(torch, sets, fn, steps, warmup):
+    """Average ms per call of fn(set) over `steps` calls rotating the sets,
+    bracketed by synchronisations; events on the launch stream."""
+    n = len(sets)
+    for i in range(warmup):
+        fn(sets[i % n])
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        fn(sets[i % n])
+    end.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3
+    return start.elapsed_time(end) / steps, wall / steps
+
+
+def time_kernels(torch, sets, steps, warmup):
+    """Per-kernel average launch time (µs) from events around each call."""
+    n = len(sets)
+    for i in range(warmup):
+        sets[i % n].step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for i in range(steps):
+        s = sets[i % n]
+        e = ev[i]
+        e[0].record()
+        s.layout()
+        e[1].record()
+        s.dispatch()
+        e[2].record()
+        s.combine()
+        e[3].record()
+    torch.cuda.synchronize()
+    lay = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+    dis = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    com = [e[2].elapsed_time(e[3]) * 1e3 for e in ev]
+    return {"layout_us": statistics.mean(lay), "dispatch_us": statistics.mean(dis),
+            "combine_us": statistics.mean(com), "combine_us_median": statistics.median(com),
+            "dispatch_us_median": statistics.median(dis)}
+
+
+# ---------------------------------------------------------------------------
+# side measurements: fp8 dispatch, low latency, Zipf prefill
+# ---------------------------------------------------------------------------
+
+def measure_fp8(torch, cdl, sets, steps):
+    lib = cdl.library()
+    bufs = []
+    for s in sets:
+        q = torch.empty(max(s.R, 1), s.H, dtype=torch.uint8, device=s.x.device)
+        sc = torch.empty(max(s.R, 1), s.H // 128, dtype=torch.float32, device=s.x.device)
+        P = ctypes.c_void_p
+        bufs.append((s, (P(s.x.data_ptr()), s.T, s.H, s.k, P(s.src2dst.data_ptr()),
+                         P(q.data_ptr()), P(sc.data_ptr()), s.R, P(s.status.data_ptr()),
+                         s.stream), q, sc))
+
+    def fn(b):
+        rc = lib.cdl_dispatch_fp8(*b[1])
+        if rc:
+            raise RuntimeError("cdl_dispatch_fp8 failed: %d" % rc)
+
+    ms, _ = time_steps(torch, bufs, fn, steps, 5)
+    s = sets[0]
+    byts = statistics.mean(4 * x.T * x.k + 2 * x.U * x.H + x.R * (x.H + 4 * x.H // 128)
+                           for x in sets)
+    return {"workload": "fp8_dispatch (T=4096, H=7168, 32 of 256 experts, top-8; "
+                        "dispatch kernel only)",
+            "us": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9}
+
+
+def measure_ll(torch, cdl, W, dev, steps):
+    w = W.WORKLOADS["ll_decode"]
+    lib = cdl.library()
+    P = ctypes.c_void_p
+    runs = []
+    for s in range(2):
+        base = NormalSet(torch, cdl, W, w.scaled(seed_base=w.seed_base + 7919 * s), dev)
+        B = torch.empty(w.L, w.cap, w.H, dtype=torch.bfloat16, device=dev)
+        mm = torch.empty(w.L, dtype=torch.int32, device=dev)
+        llm = torch.empty(w.T * w.k, dtype=torch.int32, device=dev)
+        a_ll = (P(base.x.data_ptr()), w.T, w.H, w.k, P(base.ids.data_ptr()), w.expert_begin,
+                w.L, P(base.src2dst.data_ptr()), P(base.seg.data_ptr()),
+                P(base.counts.data_ptr()), w.cap, P(B.data_ptr()), P(mm.data_ptr()),
+                P(llm.data_ptr()), P(base.status.data_ptr()), base.stream)
+        a_cb = (P(B.data_ptr()), w.L * w.cap, w.H, P(llm.data_ptr()), P(base.wts.data_ptr()),
+                w.T, w.k, P(base.out.data_ptr()), P(base.status.data_ptr()), base.stream)
+        runs.append((base, a_ll, a_cb, B, mm, llm))
+
+    def fn(r):
+        r[0].layout()
+        if lib.cdl_dispatch_ll(*r[1]) or lib.cdl_combine(*r[2]):
+            raise RuntimeError("low-latency step failed")
+
+    ms, _ = time_steps(torch, runs, fn, steps, 5)
+    b = runs[0][0]
+    byts = (b.bytes_layout() + 4 * w.L + 4 * w.T * w.k + 2 * b.U * w.H + 2 * b.R * w.H
+            + b.bytes_combine())
+    return {"workload": "ll_decode (T=128, H=7168, 32 of 256 experts, top-8, cap 1024; "
+                        "layout + padded dispatch + combine)",
+            "us_per_step": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9,
+            "expected_m": cdl.ll_expected_m(w.T, w.num_ranks, w.k, w.E)}
+
+
+def measure_zipf(torch, cdl, W, dev, steps):
+    w = W.WORKLOADS["zipf_prefill"]
+    sets = [NormalSet(torch, cdl, W, w.scaled(seed_base=w.seed_base + 7919 * s), dev)
+            for s in range(2)]
+    ms, _ = time_steps(torch, sets, NormalSet.step, steps, 3)
+    byts = statistics.mean(s.bytes_step() for s in sets)
+    counts = sets[0].counts.cpu()
+    return {"workload": "zipf_prefill (T=16384, H=4096, 128 local experts, top-8 Zipf 1.2; "
+                        "layout + dispatch + combine)",
+            "us_per_step": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9,
+            "tokens_per_s": w.T / (ms * 1e-3),
+            "expert_rows_max": int(counts.max()), "expert_rows_min": int(counts.min())}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle as it stands)
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(W, s, budget_s=12.0, max_reps=8):
+    import numpy as np  # noqa: F401
+    import oracle
+
+    xb = W.bf16_bits(s.x_host)
+    ids = s.ids_host.numpy()
+    wts = s.w_host.numpy()
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_reps and (not times or time.perf_counter() - t_start < budget_s):
+        t0 = time.perf_counter()
+        c, seg, d, r = oracle.layout(ids, 0, s.L)
+        P = oracle.dispatch(xb, d, s.k, int(seg[-1]))
+        oracle.combine(P, d, wts, s.T, s.k)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": s.bytes_step() / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "tokens_per_s": s.T / t, "ms_per_step": t * 1e3,
+            "sample": "%d full steps (layout+dispatch+combine) of the same T=%d workload, "
+                      "single-threaded C oracle, median" % (len(times), s.T)}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only (one expert-parallel rank's share); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import combine_dispatch_layout_amd as cdl
+    from combine_dispatch_layout_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]
+    if w.mode != "normal":
+        raise SystemExit("the timed step is the normal-mode path; pick a normal workload")
+    log("building %d input sets of %s ..." % (args.sets, w.name))
+    sets = [NormalSet(torch, cdl, W, w.scaled(seed_base=w.seed_base + 7919 * i), dev)
+            for i in range(args.sets)]
+    log("sets ready: R=%s U=%s" % ([s.R for s in sets], [s.U for s in sets]))
+
+    ms, wall_ms = time_steps(torch, sets, NormalSet.step, args.steps, args.warmup)
+    log("cold step: %.2f us (wall %.2f us)" % (ms * 1e3, wall_ms * 1e3))
+    warm_ms, _ = time_steps(torch, sets[:1], NormalSet.step, args.steps, args.warmup)
+    kern = time_kernels(torch, sets, args.steps, args.warmup)
+    log("kernels: %s" % kern)
+    st = int(sum(int(s.status.item()) for s in sets))
+    if st:
+        raise SystemExit("device status word set: %d" % st)
+
+    step_bytes = statistics.mean(s.bytes_step() for s in sets)
+    gbps = step_bytes / (ms * 1e-3) / 1e9
+    comb_bytes = statistics.mean(s.bytes_combine() for s in sets)
+    comb_gbps = comb_bytes / (kern["combine_us"] * 1e-6) / 1e9
+    traffic = committed_traffic()
+
+    result = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "L": w.L, "k": w.k,
+                   "expert_begin": w.expert_begin, "rotating_sets": args.sets,
+                   "step": "layout + bf16 dispatch + weighted combine (identity expert)"},
+        "tokens_per_s": round(w.T / (ms * 1e-3), 1),
+        "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "warm_single_set": {"ms_per_step": round(warm_ms, 6),
+                            "gbps": round(step_bytes / (warm_ms * 1e-3) / 1e9, 2)},
+        "kernels_us": {k_: round(v, 3) for k_, v in kern.items()},
+        "roofline": {"kernel": "combine_rows_v16", "bound": "hbm",
+                     "achieved": round(comb_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(comb_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(comb_bytes)},
+    }
+    if not args.no_modes:
+        result["modes"] = {
+            "fp8_dispatch": measure_fp8(torch, cdl, sets, args.steps),
+            "ll_decode": measure_ll(torch, cdl, W, dev, args.steps),
+            "zipf_prefill": measure_zipf(torch, cdl, W, dev, max(args.steps // 4, 10)),
+        }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(W, sets[0])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
