@@ -4,9 +4,11 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload dsv3_prefill]
 
 A step is one pass of the hot path over one batch of synthetic input already
-resident in HBM: routing layout (counts, seg_indptr, src2dst, reorder ids) ->
-normal bf16 dispatch (row scatter) -> combine (top-k-weighted gather-sum)
-of the dispatched rows (identity expert).  The default workload is the
+resident in HBM: the permute (routing layout -- counts, seg_indptr, src2dst,
+reorder ids -- and the normal bf16 row scatter, one call of two kernels) ->
+combine (top-k-weighted gather-sum) of the dispatched rows (identity
+expert).  The same step through the separate layout / dispatch calls is
+timed too, for comparison.  The default workload is the
 DeepSeek-V3-shaped prefill share: T=4096 tokens, H=7168, 256 experts of
 which 32 are local, top-8.
 
@@ -64,6 +66,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-modes", action="store_true",
                    help="skip the fp8 / low-latency / Zipf side measurements")
+    p.add_argument("--calibration-copy", type=int, default=0, metavar="MB",
+                   help="first run 5 plain device copies of MB MiB (torch copy_), the "
+                        "known-size reference for scaling rocprofv3 byte counters")
     return p.parse_args()
 
 
@@ -134,6 +139,11 @@ class NormalSet:
         self.out = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
         self.a_dispatch = (P(self.x.data_ptr()), T, H, k, P(self.src2dst.data_ptr()),
                            P(self.P.data_ptr()), self.R, P(self.status.data_ptr()), self.stream)
+        self.a_permute = (P(self.x.data_ptr()), T, H, k, P(self.ids.data_ptr()), w.expert_begin, L,
+                          P(self.counts.data_ptr()), P(self.seg.data_ptr()),
+                          P(self.src2dst.data_ptr()), P(self.reorder.data_ptr()),
+                          P(self.P.data_ptr()), self.R, P(self.status.data_ptr()),
+                          P(self.ws.data_ptr()), wsb, self.stream)
         self.a_combine = (P(self.P.data_ptr()), self.R, H, P(self.src2dst.data_ptr()),
                           P(self.wts.data_ptr()), T, k, P(self.out.data_ptr()),
                           P(self.status.data_ptr()), self.stream)
@@ -153,7 +163,16 @@ class NormalSet:
         if rc:
             raise RuntimeError("cdl_combine failed: %d" % rc)
 
+    def permute(self):
+        rc = self.lib.cdl_permute(*self.a_permute)
+        if rc:
+            raise RuntimeError("cdl_permute failed: %d" % rc)
+
     def step(self):
+        self.permute()
+        self.combine()
+
+    def step_unfused(self):
         self.layout()
         self.dispatch()
         self.combine()
@@ -196,29 +215,26 @@ def time_steps(torch, sets, fn, steps, warmup):
 
 
 def time_kernels(torch, sets, steps, warmup):
-    """Per-kernel average launch time (µs) from events around each call."""
+    """Per-call average time (µs) from HIP events recorded on the launch
+    stream around the permute (two kernels) and the combine of each step."""
     n = len(sets)
     for i in range(warmup):
         sets[i % n].step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     for i in range(steps):
         s = sets[i % n]
         e = ev[i]
         e[0].record()
-        s.layout()
+        s.permute()
         e[1].record()
-        s.dispatch()
-        e[2].record()
         s.combine()
-        e[3].record()
+        e[2].record()
     torch.cuda.synchronize()
-    lay = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
-    dis = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
-    com = [e[2].elapsed_time(e[3]) * 1e3 for e in ev]
-    return {"layout_us": statistics.mean(lay), "dispatch_us": statistics.mean(dis),
-            "combine_us": statistics.mean(com), "combine_us_median": statistics.median(com),
-            "dispatch_us_median": statistics.median(dis)}
+    per = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
+    com = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
+    return {"permute_us": statistics.mean(per), "combine_us": statistics.mean(com),
+            "permute_us_median": statistics.median(per), "combine_us_median": statistics.median(com)}
 
 
 # ---------------------------------------------------------------------------
@@ -226,28 +242,40 @@ def time_kernels(torch, sets, steps, warmup):
 # ---------------------------------------------------------------------------
 
 def measure_fp8(torch, cdl, sets, steps):
+    """fp8 dispatch on the same-shaped sets: the fused permute (layout + fp8
+    quantise-on-scatter) and the scatter kernel alone from a given layout."""
     lib = cdl.library()
+    P = ctypes.c_void_p
     bufs = []
     for s in sets:
         q = torch.empty(max(s.R, 1), s.H, dtype=torch.uint8, device=s.x.device)
         sc = torch.empty(max(s.R, 1), s.H // 128, dtype=torch.float32, device=s.x.device)
-        P = ctypes.c_void_p
-        bufs.append((s, (P(s.x.data_ptr()), s.T, s.H, s.k, P(s.src2dst.data_ptr()),
-                         P(q.data_ptr()), P(sc.data_ptr()), s.R, P(s.status.data_ptr()),
-                         s.stream), q, sc))
+        a_scatter = (P(s.x.data_ptr()), s.T, s.H, s.k, P(s.src2dst.data_ptr()), P(q.data_ptr()),
+                     P(sc.data_ptr()), s.R, P(s.status.data_ptr()), s.stream)
+        a_perm = (P(s.x.data_ptr()), s.T, s.H, s.k, P(s.ids.data_ptr()), 0, s.L,
+                  P(s.counts.data_ptr()), P(s.seg.data_ptr()), P(s.src2dst.data_ptr()),
+                  P(s.reorder.data_ptr()), P(q.data_ptr()), P(sc.data_ptr()), s.R,
+                  P(s.status.data_ptr()), P(s.ws.data_ptr()), s.ws.numel(), s.stream)
+        bufs.append((s, a_scatter, a_perm, q, sc))
 
-    def fn(b):
-        rc = lib.cdl_dispatch_fp8(*b[1])
-        if rc:
-            raise RuntimeError("cdl_dispatch_fp8 failed: %d" % rc)
+    def scatter(b):
+        if lib.cdl_dispatch_fp8(*b[1]):
+            raise RuntimeError("cdl_dispatch_fp8 failed")
 
-    ms, _ = time_steps(torch, bufs, fn, steps, 5)
-    s = sets[0]
-    byts = statistics.mean(4 * x.T * x.k + 2 * x.U * x.H + x.R * (x.H + 4 * x.H // 128)
-                           for x in sets)
-    return {"workload": "fp8_dispatch (T=4096, H=7168, 32 of 256 experts, top-8; "
-                        "dispatch kernel only)",
-            "us": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9}
+    def perm(b):
+        if lib.cdl_permute_fp8(*b[2]):
+            raise RuntimeError("cdl_permute_fp8 failed")
+
+    ms_s, _ = time_steps(torch, bufs, scatter, steps, 5)
+    ms_p, _ = time_steps(torch, bufs, perm, steps, 5)
+    scat_bytes = statistics.mean(4 * x.T * x.k + 2 * x.U * x.H + x.R * (x.H + 4 * x.H // 128)
+                                 for x in sets)
+    perm_bytes = statistics.mean(x.bytes_layout() + 2 * x.U * x.H + x.R * (x.H + 4 * x.H // 128)
+                                 for x in sets)
+    return {"workload": "fp8_dispatch (T=4096, H=7168, 32 of 256 experts, top-8, e4m3fn "
+                        "groups of 128)",
+            "permute_fp8_us": ms_p * 1e3, "permute_fp8_gbps": perm_bytes / (ms_p * 1e-3) / 1e9,
+            "scatter_fp8_us": ms_s * 1e3, "scatter_fp8_gbps": scat_bytes / (ms_s * 1e-3) / 1e9}
 
 
 def measure_ll(torch, cdl, W, dev, steps):
@@ -341,6 +369,15 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibration_copy:
+        nbytes = args.calibration_copy << 20
+        a = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("calibration copies: 5 x %d bytes read + %d bytes written" % (nbytes, nbytes))
+        del a, b
     w = W.WORKLOADS[args.workload]
     if w.mode != "normal":
         raise SystemExit("the timed step is the normal-mode path; pick a normal workload")
@@ -352,6 +389,7 @@ def main():
     ms, wall_ms = time_steps(torch, sets, NormalSet.step, args.steps, args.warmup)
     log("cold step: %.2f us (wall %.2f us)" % (ms * 1e3, wall_ms * 1e3))
     warm_ms, _ = time_steps(torch, sets[:1], NormalSet.step, args.steps, args.warmup)
+    unfused_ms, _ = time_steps(torch, sets, NormalSet.step_unfused, args.steps, args.warmup)
     kern = time_kernels(torch, sets, args.steps, args.warmup)
     log("kernels: %s" % kern)
     st = int(sum(int(s.status.item()) for s in sets))
@@ -379,12 +417,15 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "H": w.H, "E": w.E, "L": w.L, "k": w.k,
                    "expert_begin": w.expert_begin, "rotating_sets": args.sets,
-                   "step": "layout + bf16 dispatch + weighted combine (identity expert)"},
+                   "step": "permute (layout + bf16 scatter) + weighted combine (identity expert)"},
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(step_bytes),
         "warm_single_set": {"ms_per_step": round(warm_ms, 6),
                             "gbps": round(step_bytes / (warm_ms * 1e-3) / 1e9, 2)},
+        "unfused_step": {"ms_per_step": round(unfused_ms, 6),
+                         "gbps": round(step_bytes / (unfused_ms * 1e-3) / 1e9, 2),
+                         "calls": "dispatch_layout + dispatch + combine"},
         "kernels_us": {k_: round(v, 3) for k_, v in kern.items()},
         "roofline": {"kernel": "combine_rows_v16", "bound": "hbm",
                      "achieved": round(comb_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

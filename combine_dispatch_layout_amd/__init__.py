@@ -20,5 +20,7 @@ from .api import (  # noqa: F401
     layout_workspace_size,
     library,
     ll_expected_m,
+    permute,
+    permute_fp8,
     status_string,
 )

@@ -13,6 +13,7 @@ masked_m, and combine with the top-k weights):
 
     lay = dispatch_layout(topk_ids, expert_begin, num_local_experts)
     rows = dispatch(x, lay)                      # [R, H] bf16, expert-major
+    lay, rows = permute(x, topk_ids, expert_begin, num_local_experts)  # both
     q, scales = dispatch_fp8(x, lay)             # [R, H] e4m3fn + [R, H/128] f32
     buf, masked_m, ll_map = dispatch_ll(x, lay, cap)   # [L, cap, H]
     out = combine(expert_out, lay.src2dst, topk_weights)  # [T, H] bf16
@@ -60,6 +61,12 @@ def library():
         L.cdl_dispatch_layout_workspace_size.restype = sz
         L.cdl_dispatch_layout.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.cdl_dispatch_layout.restype = ctypes.c_int
+        L.cdl_permute.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, vp, vp, i64, vp,
+                                  vp, sz, vp]
+        L.cdl_permute.restype = ctypes.c_int
+        L.cdl_permute_fp8.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp,
+                                      i64, vp, vp, sz, vp]
+        L.cdl_permute_fp8.restype = ctypes.c_int
         L.cdl_dispatch.argtypes = [vp, i64, i64, i32, vp, vp, i64, vp, vp]
         L.cdl_dispatch.restype = ctypes.c_int
         L.cdl_dispatch_fp8.argtypes = [vp, i64, i64, i32, vp, vp, vp, i64, vp, vp]
@@ -145,6 +152,19 @@ def dispatch_layout(topk_ids: torch.Tensor, expert_begin: int, num_local_experts
     """Per-expert counts, seg_indptr, src2dst and reorder_topk_ids of the
     rank's slots (global ids outside [expert_begin, expert_begin+L) are
     invalid).  int64 ids are narrowed to int32 here."""
+    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace)
+    rc = library().cdl_dispatch_layout(_ptr(lay.topk_ids), lay.T, lay.k, lay.expert_begin,
+                                       lay.num_local_experts, _ptr(lay.counts),
+                                       _ptr(lay.seg_indptr), _ptr(lay.src2dst),
+                                       _ptr(lay.reorder_buf), _ptr(ws),
+                                       ws.numel() * ws.element_size(),
+                                       _stream(lay.topk_ids.device))
+    _check(rc, "cdl_dispatch_layout")
+    return lay
+
+
+def _new_layout(topk_ids: torch.Tensor, expert_begin: int, num_local_experts: int,
+                workspace: Optional[torch.Tensor]):
     _need_gpu(topk_ids, "topk_ids")
     if topk_ids.dim() != 2:
         raise ValueError("topk_ids must be [T, k]")
@@ -159,15 +179,74 @@ def dispatch_layout(topk_ids: torch.Tensor, expert_begin: int, num_local_experts
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < ws_bytes:
         raise ValueError("workspace too small: need %d bytes" % ws_bytes)
-    counts = torch.empty(L, dtype=torch.int32, device=dev)
-    seg = torch.empty(L + 1, dtype=torch.int64, device=dev)
-    src2dst = torch.empty(T * k, dtype=torch.int32, device=dev)
-    reorder = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
-    rc = library().cdl_dispatch_layout(_ptr(topk_ids), T, k, int(expert_begin), L, _ptr(counts),
-                                       _ptr(seg), _ptr(src2dst), _ptr(reorder), _ptr(workspace),
-                                       workspace.numel() * workspace.element_size(), _stream(dev))
-    _check(rc, "cdl_dispatch_layout")
-    return Layout(T, k, int(expert_begin), L, topk_ids, counts, seg, src2dst, reorder)
+    lay = Layout(T, k, int(expert_begin), L, topk_ids,
+                 torch.empty(L, dtype=torch.int32, device=dev),
+                 torch.empty(L + 1, dtype=torch.int64, device=dev),
+                 torch.empty(T * k, dtype=torch.int32, device=dev),
+                 torch.empty(max(T * k, 1), dtype=torch.int32, device=dev))
+    return lay, workspace
+
+
+def permute(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int, num_local_experts: int,
+            out: Optional[torch.Tensor] = None, rows: Optional[int] = None,
+            status: Optional[torch.Tensor] = None,
+            workspace: Optional[torch.Tensor] = None) -> Tuple[Layout, torch.Tensor]:
+    """Layout + normal-mode scatter in one call (two kernels).  `out` holds
+    `rows` rows (default T*k, an upper bound on R); the first R rows receive
+    the dispatched rows.  Returns (layout, out)."""
+    _need(x, "x", torch.bfloat16)
+    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace)
+    T, k, L = lay.T, lay.k, lay.num_local_experts
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T = %d" % T)
+    H = x.shape[1]
+    if out is None:
+        out = torch.empty(T * k if rows is None else int(rows), H, dtype=torch.bfloat16,
+                          device=x.device)
+    _need(out, "out", torch.bfloat16)
+    if out.dim() != 2 or out.shape[1] != H:
+        raise ValueError("out must be [rows, H]")
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_permute(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
+                               _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
+                               _ptr(lay.reorder_buf), _ptr(out), out.shape[0], _ptr(status),
+                               _ptr(ws), ws.numel() * ws.element_size(), _stream(x.device))
+    _check(rc, "cdl_permute")
+    return lay, out
+
+
+def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
+                num_local_experts: int, rows: Optional[int] = None,
+                out_q: Optional[torch.Tensor] = None, out_scales: Optional[torch.Tensor] = None,
+                status: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """Layout + fp8 (e4m3fn, groups of 128) scatter in one call.  Returns
+    (layout, q [rows, H] uint8, scales [rows, H/128] fp32)."""
+    _need(x, "x", torch.bfloat16)
+    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace)
+    T, k, L = lay.T, lay.k, lay.num_local_experts
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T = %d" % T)
+    H = x.shape[1]
+    if H % FP8_GROUP:
+        raise CdlError(-3, "permute_fp8 (H must be a multiple of 128)")
+    n = T * k if rows is None else int(rows)
+    if out_q is None:
+        out_q = torch.empty(n, H, dtype=torch.uint8, device=x.device)
+    if out_scales is None:
+        out_scales = torch.empty(out_q.shape[0], H // FP8_GROUP, dtype=torch.float32,
+                                 device=x.device)
+    _need(out_q, "out_q", torch.uint8)
+    _need(out_scales, "out_scales", torch.float32, (out_q.shape[0], H // FP8_GROUP))
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_permute_fp8(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
+                                   _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
+                                   _ptr(lay.reorder_buf), _ptr(out_q), _ptr(out_scales),
+                                   out_q.shape[0], _ptr(status), _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(x.device))
+    _check(rc, "cdl_permute_fp8")
+    return lay, out_q, out_scales
 
 
 def dispatch(x: torch.Tensor, layout: Layout, out: Optional[torch.Tensor] = None,

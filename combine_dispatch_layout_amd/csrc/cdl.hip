@@ -9,15 +9,23 @@
 // The work is data movement plus a few ALU operations per element, so every
 // kernel is bound by HBM bandwidth or by latency; there is no dense
 // contraction and no MFMA.  Design points for CDNA4:
-//   * 64-lane wavefronts: the layout ranks slots with wave ballots
-//     (__ballot / popcount / readlane) instead of atomics, so src2dst is
-//     deterministic and stable by flat slot index.
-//   * Row kernels move 16 bytes per lane per access (global_load_dwordx4 /
-//     global_store_dwordx4) and keep all of a lane's chunks of a row in
-//     registers, so each source row is read once whatever its fan-out.
-//   * Routing indices are block-uniform and land in scalar registers.
-//   * No kernel keeps state across calls; nothing needs zeroing except the
-//     caller's status word.
+//   * Layout in two launches with no atomics across workgroups and no state
+//     kept between calls: (A) per-superblock expert histograms; (B) every
+//     workgroup of 8 tokens (one wave per token) derives its own expert
+//     offsets from the superblock counts plus a recount of the slots of its
+//     superblock that precede it, then ranks its slots with wave ballots
+//     (__ballot / popcount / readlane), so src2dst is deterministic and stable
+//     by flat slot index.
+//   * The permute fuses (B) with the row scatter: each wave issues the loads
+//     of its token's row before the layout arithmetic starts, so HBM reads
+//     are in flight while the offsets are computed.
+//   * Rows move as 16-byte lane accesses (buffer_load/store_dwordx4 through a
+//     per-row buffer resource); a wave holds up to 16 chunks (256 bytes) of a
+//     row per lane, so a source row is read once whatever its fan-out.
+//   * Dispatched rows are stored with the temporal policy so the combine
+//     finds them in the Infinity Cache; the combine loads and stores
+//     non-temporally (measured fastest of the policy combinations).
+//   * Routing indices are wave-uniform and are kept in scalar registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,6 +34,58 @@
 namespace {
 
 constexpr int kWave = 64;
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Rows are addressed through buffer resources: the row base and its length
+// live in scalar registers, each lane adds a 32-bit offset, and the hardware
+// range check returns zeros for loads past the row end and drops stores
+// there, so no per-chunk bounds test or 64-bit lane address is needed.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (gfx9 family)
+constexpr int kPolicyNT = 2;             // cache policy: non-temporal (streaming)
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, kRsrcWord3);
+}
+// Cache policy per access.  Measured on MI355X in the dispatch -> combine
+// step: the dispatched rows are stored with the default (temporal) policy so
+// that the next kernel finds them in the caches (the 256 MB Infinity Cache
+// holds a 60 MB permuted buffer), while the combine, the last reader of those
+// rows and the writer of rows nobody reads back soon, loads and stores
+// non-temporally.
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ u32x4 buf_ld16_stream(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kPolicyNT);
+}
+__device__ __forceinline__ void buf_st16(rsrc_t r, u32x4 v, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st16_stream(rsrc_t r, u32x4 v, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, kPolicyNT);
+}
+__device__ __forceinline__ void buf_st8(rsrc_t r, u32x2 v, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+}
+__device__ __forceinline__ void buf_st4(rsrc_t r, float v, uint32_t voff, uint32_t soff)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+}
+__device__ __forceinline__ int32_t buf_ld4(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // ---------------------------------------------------------------------------
 // number formats
@@ -45,6 +105,13 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b)
     return (uint32_t)ha | ((uint32_t)hb << 16);
 }
 
+// Two fp32 values (already clamped to [-448, 448]) to OCP E4M3FN bytes, round
+// to nearest even: v_cvt_pk_fp8_f32, which on gfx950 produces the OCP format.
+__device__ __forceinline__ uint32_t pack2_e4m3(float a, float b)
+{
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+}
+
 __device__ __forceinline__ int32_t local_expert(int32_t id, int32_t expert_begin, int32_t L)
 {
     // id - expert_begin in 64 bits: no overflow for any int32 pair
@@ -58,40 +125,132 @@ __device__ __forceinline__ void set_status(int32_t *status, int32_t bit)
 }
 
 // ---------------------------------------------------------------------------
-// layout: per-tile histogram, then scan + stable rank
+// fp8 group quantisation of one 16-byte chunk (8 bf16) held by a lane; the
+// 16 lanes of a 16-lane segment hold one group of 128 elements.
 // ---------------------------------------------------------------------------
 
-constexpr int kLayoutThreads = 256;
-constexpr int kLayoutWaves = kLayoutThreads / kWave;          // 4
-constexpr int kTile = 1024;                                   // slots per tile
-constexpr int kSlotsPerWave = kTile / kLayoutWaves;            // 256
-constexpr int kGroupsPerWave = kSlotsPerWave / kWave;          // 4
-
-inline int64_t layout_tiles(int64_t n) { return (n + kTile - 1) / kTile; }
-
-// Kernel 1: tile_counts[tile][e] = number of valid slots of expert e in the
-// tile (an LDS histogram; the count is order independent).
-__global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
-    const int32_t *__restrict__ ids, int64_t n, int32_t expert_begin, int32_t L,
-    int32_t *__restrict__ tile_counts)
+__device__ __forceinline__ float quant_in(float v, float a, float s)
 {
-    extern __shared__ int32_t hist[];
-    for (int e = threadIdx.x; e < L; e += kLayoutThreads) hist[e] = 0;
-    __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kTile;
-    for (int s = threadIdx.x; s < kTile; s += kLayoutThreads) {
-        const int64_t i = base + s;
-        if (i < n) {
-            const int32_t e = local_expert(ids[i], expert_begin, L);
-            if (e >= 0) atomicAdd(&hist[e], 1);
-        }
+    if (a > 0.0f) {
+        v = v / s;                      // correctly rounded binary32 division
+        v = fminf(fmaxf(v, -448.0f), 448.0f);
     }
-    __syncthreads();
-    int32_t *row = tile_counts + (int64_t)blockIdx.x * L;
-    for (int e = threadIdx.x; e < L; e += kLayoutThreads) row[e] = hist[e];
+    return v;
 }
 
-// Block-wide exclusive scan of one int32 per thread (256 threads).
+// Returns the 8 e4m3fn bytes of the chunk; *scale receives the group scale.
+__device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float *scale)
+{
+    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
+    const float s = a / 448.0f;
+    const uint32_t lo = pack2_e4m3(quant_in(f[0], a, s), quant_in(f[1], a, s)) |
+                        (pack2_e4m3(quant_in(f[2], a, s), quant_in(f[3], a, s)) << 16);
+    const uint32_t hi = pack2_e4m3(quant_in(f[4], a, s), quant_in(f[5], a, s)) |
+                        (pack2_e4m3(quant_in(f[6], a, s), quant_in(f[7], a, s)) << 16);
+    *scale = s;
+    return u32x2{lo, hi};
+}
+
+// ---------------------------------------------------------------------------
+// layout plan
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxChunks = 16;          // 16-byte chunks a lane holds per pass
+constexpr int kCountThreads = 256;
+
+struct Plan {
+    int64_t n;            // slots, T * k
+    int tpb;              // tokens per permute workgroup (one wave each)
+    int64_t nblocks;      // permute workgroups, ceil(T / tpb)
+    int64_t sbb;          // permute workgroups per superblock
+    int64_t S;            // superblocks
+    int64_t sb_slots;     // slots per superblock
+};
+
+// Tokens per workgroup: enough workgroups to fill the chip (about 512) for
+// small batches, 8 tokens (512 threads) for large ones.  Superblock size: the
+// power of two that balances the superblock counts every workgroup reads
+// (S * L) against the slots it may recount (sbb * tpb * k).
+inline Plan make_plan(int64_t T, int32_t k, int32_t L)
+{
+    Plan p;
+    p.n = T * k;
+    int tpb = 1;
+    while (tpb < 8 && (T + tpb - 1) / tpb > 512) tpb *= 2;
+    p.tpb = tpb;
+    p.nblocks = (T + tpb - 1) / tpb;
+    const int64_t bs = (int64_t)tpb * k;
+    int64_t best_sbb = 1, best_cost = INT64_MAX;
+    for (int64_t sbb = 1; sbb <= (p.nblocks > 0 ? p.nblocks : 1); sbb *= 2) {
+        const int64_t S = (p.nblocks + sbb - 1) / sbb;
+        const int64_t cost = S * (int64_t)L + (sbb - 1) * bs;
+        if (cost < best_cost) {
+            best_cost = cost;
+            best_sbb = sbb;
+        }
+    }
+    p.sbb = best_sbb;
+    p.S = (p.nblocks + best_sbb - 1) / best_sbb;
+    p.sb_slots = best_sbb * bs;
+    return p;
+}
+
+// ---------------------------------------------------------------------------
+// layout kernel A: superblock histograms
+// ---------------------------------------------------------------------------
+
+// sb_counts[s][e] = number of valid slots of local expert e in superblock s
+// (an LDS histogram; counts are order independent).  Each thread loads a batch
+// of kCountBatch ids before touching the histogram, so one superblock costs
+// one memory latency per batch rather than one per id.
+constexpr int kCountBatch = 8;
+
+__global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
+    const int32_t *__restrict__ ids, int64_t n, int64_t sb_slots, int32_t expert_begin, int32_t L,
+    int32_t *__restrict__ sb_counts)
+{
+    extern __shared__ int32_t hist[];
+    for (int e = threadIdx.x; e < L; e += kCountThreads) hist[e] = 0;
+    const int64_t begin = (int64_t)blockIdx.x * sb_slots;
+    const int64_t end = begin + sb_slots < n ? begin + sb_slots : n;
+    // ids of the superblock through a buffer resource: loads past its end
+    // return 0 without a branch (their slots are masked below)
+    const rsrc_t r = make_rsrc(ids + begin, (uint32_t)((end > begin ? end - begin : 0) * 4));
+    for (int64_t b0 = begin; b0 < end; b0 += (int64_t)kCountThreads * kCountBatch) {
+        int32_t raw[kCountBatch], le[kCountBatch];
+#pragma unroll
+        for (int q = 0; q < kCountBatch; ++q)
+            raw[q] = buf_ld4(r, (uint32_t)(q * kCountThreads + threadIdx.x) * 4u, (uint32_t)((b0 - begin) * 4));
+#pragma unroll
+        for (int q = 0; q < kCountBatch; ++q) {
+            const int64_t i = b0 + q * kCountThreads + threadIdx.x;
+            le[q] = i < end ? local_expert(raw[q], expert_begin, L) : -1;
+        }
+        if (b0 == begin) __syncthreads();            // histogram zeroed
+#pragma unroll
+        for (int q = 0; q < kCountBatch; ++q)
+            if (le[q] >= 0) atomicAdd(&hist[le[q]], 1);
+    }
+    if (end <= begin) __syncthreads();
+    __syncthreads();
+    int32_t *row = sb_counts + (int64_t)blockIdx.x * L;
+    for (int e = threadIdx.x; e < L; e += kCountThreads) row[e] = hist[e];
+}
+
+// ---------------------------------------------------------------------------
+// layout kernel B (+ fused row scatter): the permute
+// ---------------------------------------------------------------------------
+
+enum PermuteMode { kLayoutOnly = 0, kRowsBf16 = 1, kRowsFp8 = 2 };
+
+// Block-wide exclusive scan of one int32 per thread (NW waves).
+template <int NW>
 __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *lds_waves, int32_t *total)
 {
     const int lane = threadIdx.x & (kWave - 1);
@@ -106,7 +265,7 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *lds_
     __syncthreads();
     int32_t before = 0, all = 0;
 #pragma unroll
-    for (int i = 0; i < kLayoutWaves; ++i) {
+    for (int i = 0; i < NW; ++i) {
         const int32_t s = lds_waves[i];
         if (i < w) before += s;
         all += s;
@@ -116,164 +275,287 @@ __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *lds_
     return before + incl - v;
 }
 
-// Kernel 2 (grid = max(1, tiles)): every block derives the per-expert totals
-// and its tile's prefix from tile_counts, block 0 publishes counts and
-// seg_indptr, and each block ranks its own slots:
-//   dst(i) = seg_indptr[e] + sum over earlier tiles of tile_counts[.][e]
-//          + slots of e in earlier waves of this tile
-//          + slots of e earlier in this wave (ballot / popcount).
-// Slot order inside the tile is wave-major, group-major, lane-minor, which is
-// the flat slot order, so the ranks are stable.
-__global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
-    const int32_t *__restrict__ ids, int64_t n, int32_t expert_begin, int32_t L,
-    const int32_t *__restrict__ tile_counts, int64_t tiles, int32_t *__restrict__ counts,
-    int64_t *__restrict__ seg_indptr, int32_t *__restrict__ src2dst,
-    int32_t *__restrict__ reorder)
-{
-    extern __shared__ int32_t smem[];
-    int32_t *base = smem;                 // [L] first row of expert e in this tile
-    int32_t *wcnt = smem + L;             // [kLayoutWaves][L]
-    __shared__ int32_t scan_tmp[kLayoutWaves];
+struct PermuteArgs {
+    const int32_t *ids;
+    int64_t T;
+    int32_t k;
+    int32_t expert_begin;
+    int32_t L;
+    const int32_t *sb_counts;
+    int64_t S;
+    int64_t sbb;
+    int64_t sb_slots;
+    int32_t *counts;
+    int64_t *seg_indptr;
+    int32_t *src2dst;
+    int32_t *reorder;
+    // rows
+    const u32x4 *x;
+    int64_t chunks;       // H / 8
+    u32x4 *out;           // bf16 rows
+    u32x2 *out_q;         // fp8 rows (8 bytes per chunk)
+    float *out_s;         // fp8 scales, chunks / 16 per row
+    int64_t cap_rows;
+    int32_t *status;
+};
 
-    const int64_t tile = blockIdx.x;
+// One workgroup per TPB tokens, one wave per token.
+//  0. the wave of token t loads its row (first kMaxChunks chunks per lane)
+//     if the token has a valid slot;
+//  1. tot[e] = all valid slots of e; cur[e] = valid slots of e before this
+//     workgroup's first slot (superblock counts of earlier superblocks plus a
+//     recount of this superblock's earlier slots);
+//  2. exclusive scan of tot over e gives seg_indptr (workgroup 0 publishes
+//     counts and seg_indptr) and cur[e] += seg_indptr[e];
+//  3. the workgroup's TPB*k slots are ranked 64 at a time, wave by wave in
+//     slot order, with ballots; the leader of each expert match advances
+//     cur[e]; dst = cur[e] + rank in the match;
+//  4. each wave stores its row to its token's destinations.
+template <int TPB, int MODE>
+__global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
+{
+    constexpr int NT = TPB * kWave;
+    extern __shared__ int32_t lds[];
+    const int L = a.L;
+    int32_t *tot = lds;
+    int32_t *cur = lds + L;
+    int32_t *dsts = lds + 2 * L;          // [TPB * k]
+    __shared__ int32_t scan_tmp[TPB];
+
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int w = tid / kWave;
+    const int wave = tid / kWave;
+    const int k = a.k;
+    const int64_t blk = blockIdx.x;
+    const int64_t t_begin = blk * TPB;
+    const int64_t t_end = t_begin + TPB < a.T ? t_begin + TPB : a.T;
+    const int64_t slot_begin = t_begin * k;
+    const int nslots = (int)((t_end > t_begin ? t_end - t_begin : 0) * k);
 
-    // 1. totals and tile prefixes; each thread owns a run of experts
-    const int per = (L + kLayoutThreads - 1) / kLayoutThreads;
-    const int e0 = tid * per;
-    int32_t run_total = 0;
-    for (int q = 0; q < per; ++q) {
-        const int e = e0 + q;
-        if (e >= L) break;
-        int32_t tot = 0, pre = 0;
-        for (int64_t t = 0; t < tiles; ++t) {
-            const int32_t c = tile_counts[t * L + e];
-            tot += c;
-            pre += (t < tile) ? c : 0;
-        }
-        base[e] = pre;
-        wcnt[e] = tot;                     // scratch: totals, overwritten below
-        run_total += tot;
+    // 0. row prefetch
+    const int64_t t = t_begin + wave;
+    bool tok_valid = false;
+    if (MODE != kLayoutOnly && t < a.T) {
+        for (int j = 0; j < k; ++j) tok_valid |= local_expert(a.ids[t * k + j], a.expert_begin, L) >= 0;
     }
-    int32_t R = 0;
-    int32_t excl = block_exclusive_scan(run_total, scan_tmp, &R);
-    for (int q = 0; q < per; ++q) {
-        const int e = e0 + q;
-        if (e >= L) break;
-        const int32_t tot = wcnt[e];
-        if (tile == 0) {
-            counts[e] = tot;
-            seg_indptr[e] = excl;
-        }
-        base[e] += excl;
-        excl += tot;
+    u32x4 v[kMaxChunks];
+    const uint32_t row_bytes = (uint32_t)(a.chunks * 16);
+    const uint32_t voff = (uint32_t)lane * 16u;
+    const rsrc_t xr = make_rsrc(a.x + (tok_valid ? t * a.chunks : 0), row_bytes);
+    if (MODE != kLayoutOnly && tok_valid) {
+#pragma unroll
+        for (int u = 0; u < kMaxChunks; ++u) v[u] = buf_ld16(xr, voff, u * kWave * 16);
     }
-    if (tile == 0 && tid == 0) seg_indptr[L] = R;
+
+    // 1. totals and offsets before this workgroup
+    for (int e = tid; e < L; e += NT) {
+        tot[e] = 0;
+        cur[e] = 0;
+    }
     __syncthreads();
-    for (int idx = tid; idx < kLayoutWaves * L; idx += kLayoutThreads) wcnt[idx] = 0;
+    const int64_t s_me = blk / a.sbb;
+    const int64_t nsc = a.S * L;
+    {
+        // superblock counts, kBatch per thread per round, loads first
+        constexpr int kBatch = 8;
+        const rsrc_t r = make_rsrc(a.sb_counts, (uint32_t)(nsc * 4));
+        for (int64_t b0 = 0; b0 < nsc; b0 += (int64_t)NT * kBatch) {
+            int32_t c[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                c[q] = buf_ld4(r, (uint32_t)(q * NT + tid) * 4u, (uint32_t)(b0 * 4));
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int64_t idx = b0 + q * NT + tid;
+                if (idx < nsc && c[q]) {
+                    const int e = (int)(idx % L);
+                    atomicAdd(&tot[e], c[q]);
+                    if (idx / L < s_me) atomicAdd(&cur[e], c[q]);
+                }
+            }
+        }
+        // recount of this superblock's slots before the workgroup
+        const int64_t rc_begin = s_me * a.sb_slots;
+        const int64_t nrc = slot_begin - rc_begin;
+        const rsrc_t ri = make_rsrc(a.ids + rc_begin, (uint32_t)(nrc * 4));
+        for (int64_t b0 = 0; b0 < nrc; b0 += (int64_t)NT * kBatch) {
+            int32_t id[kBatch];
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q)
+                id[q] = buf_ld4(ri, (uint32_t)(q * NT + tid) * 4u, (uint32_t)(b0 * 4));
+#pragma unroll
+            for (int q = 0; q < kBatch; ++q) {
+                const int32_t e = b0 + q * NT + tid < nrc ? local_expert(id[q], a.expert_begin, L) : -1;
+                if (e >= 0) atomicAdd(&cur[e], 1);
+            }
+        }
+    }
     __syncthreads();
 
-    // 2. ranks inside each wave's 256 consecutive slots, 64 at a time
-    int32_t *my_cnt = wcnt + w * L;
+    // 2. scan over experts; each thread owns a run of consecutive experts
+    {
+        const int per = (L + NT - 1) / NT;
+        const int e0 = tid * per;
+        int32_t run = 0;
+        for (int q = 0; q < per && e0 + q < L; ++q) run += tot[e0 + q];
+        int32_t R = 0;
+        int32_t excl = block_exclusive_scan<TPB>(run, scan_tmp, &R);
+        for (int q = 0; q < per && e0 + q < L; ++q) {
+            const int e = e0 + q;
+            const int32_t c = tot[e];
+            if (blk == 0) {
+                a.counts[e] = c;
+                a.seg_indptr[e] = excl;
+            }
+            cur[e] += excl;
+            excl += c;
+        }
+        if (blk == 0 && tid == 0) a.seg_indptr[L] = R;
+    }
+    __syncthreads();
+
+    // 3. stable ranks, 64 slots per round in slot order
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
-    int32_t ge[kGroupsPerWave], gr[kGroupsPerWave];
-    const int64_t wave_base = tile * kTile + (int64_t)w * kSlotsPerWave;
-#pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) {
-        const int64_t i = wave_base + g * kWave + lane;
-        const int32_t e = (i < n) ? local_expert(ids[i], expert_begin, L) : -1;
-        uint64_t pending = __ballot(e >= 0);
-        int32_t r = 0;
-        while (pending) {
-            const int leader = __builtin_ctzll(pending);
-            const int32_t el = __builtin_amdgcn_readlane(e, leader);
-            const uint64_t m = __ballot(e == el);
-            const int32_t before = my_cnt[el];
-            if (e == el) r = before + __popcll(m & lt_mask);
-            if (lane == leader) my_cnt[el] = before + __popcll(m);
-            pending &= ~m;
+    for (int r0 = 0, rw = 0; r0 < nslots; r0 += kWave, ++rw) {
+        if (wave == rw) {
+            const int rel = r0 + lane;
+            const int64_t i = slot_begin + rel;
+            const int32_t e = rel < nslots ? local_expert(a.ids[i], a.expert_begin, L) : -1;
+            uint64_t pending = __ballot(e >= 0);
+            int32_t dst = -1;
+            while (pending) {
+                const int leader = __builtin_ctzll(pending);
+                const int32_t el = __builtin_amdgcn_readlane(e, leader);
+                const uint64_t m = __ballot(e == el);
+                const int32_t before = cur[el];
+                if (e == el) dst = before + __popcll(m & lt_mask);
+                if (lane == leader) cur[el] = before + __popcll(m);
+                pending &= ~m;
+            }
+            if (rel < nslots) {
+                a.src2dst[i] = dst;
+                if (dst >= 0) a.reorder[dst] = e;
+                if (MODE != kLayoutOnly) dsts[rel] = dst;
+            }
         }
-        ge[g] = e;
-        gr[g] = r;
+        __syncthreads();
     }
-    __syncthreads();
 
-    // 3. wave counts -> wave offsets (in place), seeded with the tile base
-    for (int e = tid; e < L; e += kLayoutThreads) {
-        int32_t run = base[e];
+    // 4. rows
+    if (MODE == kLayoutOnly || !tok_valid) return;
+    const int32_t *my = dsts + wave * k;
+    for (int64_t c0 = 0; c0 < a.chunks; c0 += (int64_t)kMaxChunks * kWave) {
+        const uint32_t pass = (uint32_t)(c0 * 16);
+        if (c0 > 0) {
 #pragma unroll
-        for (int v = 0; v < kLayoutWaves; ++v) {
-            const int32_t c = wcnt[v * L + e];
-            wcnt[v * L + e] = run;
-            run += c;
+            for (int u = 0; u < kMaxChunks; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         }
-    }
-    __syncthreads();
-
-    // 4. publish
+        if (MODE == kRowsBf16) {
+            for (int j = 0; j < k; ++j) {
+                const int32_t dst = uniform(my[j]);
+                if (dst < 0) continue;
+                if ((int64_t)dst >= a.cap_rows) {
+                    if (c0 == 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
+                    continue;
+                }
+                const rsrc_t o = make_rsrc(a.out + (int64_t)dst * a.chunks, row_bytes);
 #pragma unroll
-    for (int g = 0; g < kGroupsPerWave; ++g) {
-        const int64_t i = wave_base + g * kWave + lane;
-        if (i >= n) continue;
-        const int32_t e = ge[g];
-        if (e < 0) {
-            src2dst[i] = -1;
+                for (int u = 0; u < kMaxChunks; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
+            }
         } else {
-            const int32_t dst = my_cnt[e] + gr[g];
-            src2dst[i] = dst;
-            reorder[dst] = e;
+            // fp8 row: 8 bytes per chunk, one fp32 scale per 16 chunks (written
+            // by the first lane of each 16-lane group)
+            u32x2 q[kMaxChunks];
+            float sc[kMaxChunks];
+#pragma unroll
+            for (int u = 0; u < kMaxChunks; ++u) q[u] = quant_chunk(v[u], &sc[u]);
+            const uint32_t q_bytes = (uint32_t)(a.chunks * 8);
+            const uint32_t s_bytes = (uint32_t)(a.chunks / 16 * 4);
+            const bool group_head = (lane & 15) == 0;
+            for (int j = 0; j < k; ++j) {
+                const int32_t dst = uniform(my[j]);
+                if (dst < 0) continue;
+                if ((int64_t)dst >= a.cap_rows) {
+                    if (c0 == 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
+                    continue;
+                }
+                const rsrc_t oq = make_rsrc(a.out_q + (int64_t)dst * a.chunks, q_bytes);
+                const rsrc_t os = make_rsrc(a.out_s + (int64_t)dst * (a.chunks / 16), s_bytes);
+#pragma unroll
+                for (int u = 0; u < kMaxChunks; ++u) {
+                    buf_st8(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + u * kWave * 8);
+                    if (group_head)
+                        buf_st4(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + u * 16);
+                }
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// normal dispatch: row scatter
+// normal dispatch from a given layout: row scatter
 // ---------------------------------------------------------------------------
 
-constexpr int kRowThreads = 128;
-constexpr int kRowUnroll = 8;        // 16-byte chunks per lane per pass
+constexpr int kRowTok = 4;                       // tokens (waves) per workgroup
+constexpr int kRowThreads = kRowTok * kWave;
 
-// One block per token.  Each lane loads up to kRowUnroll 16-byte chunks of
-// the row once, then stores them to every valid destination.
-__global__ __launch_bounds__(kRowThreads) void scatter_rows_v16(
-    const uint4 *__restrict__ x, int64_t chunks, int32_t k,
-    const int32_t *__restrict__ src2dst, uint4 *__restrict__ out, int64_t cap_rows,
-    int32_t *__restrict__ status)
+// One wave per token: the wave loads up to kMaxChunks 16-byte chunks per
+// lane of the row once, then stores them to every valid destination.
+template <bool FP8>
+__global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
+    const u32x4 *__restrict__ x, int64_t T, int64_t chunks, int32_t k,
+    const int32_t *__restrict__ src2dst, u32x4 *__restrict__ out, u32x2 *__restrict__ out_q,
+    float *__restrict__ out_s, int64_t cap_rows, int32_t *__restrict__ status)
 {
-    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = (int64_t)blockIdx.x * kRowTok + threadIdx.x / kWave;
+    if (t >= T) return;
     const int32_t *d = src2dst + t * k;
     bool any = false;
     for (int j = 0; j < k; ++j) any |= d[j] >= 0;
     if (!any) return;
-    const uint4 *src = x + t * chunks;
-    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kRowThreads * kRowUnroll) {
-        uint4 v[kRowUnroll];
+    const uint32_t row_bytes = (uint32_t)(chunks * 16);
+    const uint32_t voff = (uint32_t)lane * 16u;
+    const rsrc_t xr = make_rsrc(x + t * chunks, row_bytes);
+    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kMaxChunks * kWave) {
+        const uint32_t pass = (uint32_t)(c0 * 16);
+        u32x4 v[kMaxChunks];
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-            const int64_t c = c0 + u * kRowThreads + threadIdx.x;
-            v[u] = (c < chunks) ? src[c] : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < kMaxChunks; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+        u32x2 q[kMaxChunks];
+        float sc[kMaxChunks];
+        if (FP8) {
+#pragma unroll
+            for (int u = 0; u < kMaxChunks; ++u) q[u] = quant_chunk(v[u], &sc[u]);
         }
         for (int j = 0; j < k; ++j) {
             const int32_t dst = d[j];
             if (dst < 0) continue;
             if (dst >= cap_rows) {
-                if (c0 == 0 && threadIdx.x == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
+                if (c0 == 0 && lane == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
                 continue;
             }
-            uint4 *o = out + (int64_t)dst * chunks;
+            if (FP8) {
+                const rsrc_t oq = make_rsrc(out_q + (int64_t)dst * chunks, (uint32_t)(chunks * 8));
+                const rsrc_t os = make_rsrc(out_s + (int64_t)dst * (chunks / 16), (uint32_t)(chunks / 16 * 4));
+                const bool group_head = (lane & 15) == 0;
 #pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const int64_t c = c0 + u * kRowThreads + threadIdx.x;
-                if (c < chunks) o[c] = v[u];
+                for (int u = 0; u < kMaxChunks; ++u) {
+                    buf_st8(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + u * kWave * 8);
+                    if (group_head)
+                        buf_st4(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + u * 16);
+                }
+            } else {
+                const rsrc_t o = make_rsrc(out + (int64_t)dst * chunks, row_bytes);
+#pragma unroll
+                for (int u = 0; u < kMaxChunks; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
             }
         }
     }
 }
 
 // Any H, any 2-byte alignment: element-wise copy.
-__global__ __launch_bounds__(kRowThreads) void scatter_rows_u16(
+__global__ __launch_bounds__(128) void scatter_rows_u16(
     const uint16_t *__restrict__ x, int64_t H, int32_t k, const int32_t *__restrict__ src2dst,
     uint16_t *__restrict__ out, int64_t cap_rows, int32_t *__restrict__ status)
 {
@@ -286,84 +568,7 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_u16(
             if (threadIdx.x == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
             continue;
         }
-        for (int64_t h = threadIdx.x; h < H; h += kRowThreads) out[(int64_t)dst * H + h] = x[t * H + h];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// fp8 dispatch: per-token group quantisation on the scatter
-// ---------------------------------------------------------------------------
-
-// Two fp32 values (already clamped to [-448, 448]) to OCP E4M3FN bytes, round
-// to nearest even: v_cvt_pk_fp8_f32, which on gfx950 produces the OCP format.
-__device__ __forceinline__ uint32_t pack2_e4m3(float a, float b)
-{
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
-}
-
-__device__ __forceinline__ float quant_in(float v, float a, float s)
-{
-    if (a > 0.0f) {
-        v = v / s;                      // correctly rounded binary32 division
-        v = fminf(fmaxf(v, -448.0f), 448.0f);
-    }
-    return v;
-}
-
-// One block per token.  A group of 128 elements is 16 chunks of 8, held by 16
-// consecutive lanes; their amax is reduced with xor shuffles inside the 16.
-__global__ __launch_bounds__(kRowThreads) void scatter_rows_fp8(
-    const uint4 *__restrict__ x, int64_t chunks, int32_t k, const int32_t *__restrict__ src2dst,
-    uint2 *__restrict__ out_q, float *__restrict__ out_s, int64_t groups, int64_t cap_rows,
-    int32_t *__restrict__ status)
-{
-    const int64_t t = blockIdx.x;
-    const int32_t *d = src2dst + t * k;
-    bool any = false;
-    for (int j = 0; j < k; ++j) any |= d[j] >= 0;
-    if (!any) return;
-    const uint4 *src = x + t * chunks;
-    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kRowThreads * kRowUnroll) {
-        uint2 q[kRowUnroll];
-        float sc[kRowUnroll];
-#pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-            const int64_t c = c0 + u * kRowThreads + threadIdx.x;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (c < chunks) v = src[c];
-            float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                          bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-            float a = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
-#pragma unroll
-            for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
-            const float s = a / 448.0f;
-            uint32_t lo = pack2_e4m3(quant_in(f[0], a, s), quant_in(f[1], a, s)) |
-                          (pack2_e4m3(quant_in(f[2], a, s), quant_in(f[3], a, s)) << 16);
-            uint32_t hi = pack2_e4m3(quant_in(f[4], a, s), quant_in(f[5], a, s)) |
-                          (pack2_e4m3(quant_in(f[6], a, s), quant_in(f[7], a, s)) << 16);
-            q[u] = make_uint2(lo, hi);
-            sc[u] = s;
-        }
-        for (int j = 0; j < k; ++j) {
-            const int32_t dst = d[j];
-            if (dst < 0) continue;
-            if (dst >= cap_rows) {
-                if (c0 == 0 && threadIdx.x == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
-                continue;
-            }
-            uint2 *oq = out_q + (int64_t)dst * chunks;
-            float *os = out_s + (int64_t)dst * groups;
-#pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const int64_t c = c0 + u * kRowThreads + threadIdx.x;
-                if (c < chunks) {
-                    oq[c] = q[u];
-                    if ((c & 15) == 0) os[c >> 4] = sc[u];
-                }
-            }
-        }
+        for (int64_t h = threadIdx.x; h < H; h += 128) out[(int64_t)dst * H + h] = x[t * H + h];
     }
 }
 
@@ -371,9 +576,8 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_fp8(
 // low-latency dispatch
 // ---------------------------------------------------------------------------
 
-// One block per token: the destination of valid slot i in the padded buffer is
-// row e*cap + (src2dst[i] - seg_indptr[e]).  Blocks whose index is below
-// ceil(L / threads) also write masked_m; blocks at or beyond T stop there.
+// The destination of valid slot i in the padded buffer is row
+// e*cap + (src2dst[i] - seg_indptr[e]).
 __device__ __forceinline__ int64_t ll_row(const int32_t *__restrict__ ids, int32_t expert_begin,
                                           int32_t L, const int32_t *__restrict__ src2dst,
                                           const int64_t *__restrict__ seg_indptr, int64_t cap,
@@ -393,11 +597,13 @@ __device__ __forceinline__ int64_t ll_row(const int32_t *__restrict__ ids, int32
     return (int64_t)e * cap + slot;
 }
 
+// One wave per token (kRowTok per workgroup); workgroups whose index is below
+// ceil(L / threads) also write masked_m; waves at or beyond T stop there.
 __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
-    const uint4 *__restrict__ x, int64_t T, int64_t chunks, int32_t k,
+    const u32x4 *__restrict__ x, int64_t T, int64_t chunks, int32_t k,
     const int32_t *__restrict__ ids, int32_t expert_begin, int32_t L,
     const int32_t *__restrict__ src2dst, const int64_t *__restrict__ seg_indptr,
-    const int32_t *__restrict__ counts, int64_t cap, uint4 *__restrict__ out,
+    const int32_t *__restrict__ counts, int64_t cap, u32x4 *__restrict__ out,
     int32_t *__restrict__ masked_m, int32_t *__restrict__ ll_src2dst,
     int32_t *__restrict__ status)
 {
@@ -405,38 +611,36 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
         const int64_t e = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
         if (e < L) masked_m[e] = (int32_t)((int64_t)counts[e] < cap ? counts[e] : cap);
     }
-    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t t = (int64_t)blockIdx.x * kRowTok + threadIdx.x / kWave;
     if (t >= T) return;
     bool any = false;
     for (int j = 0; j < k; ++j) {
         const int64_t i = t * k + j;
         bool ovf;
         const int64_t row = ll_row(ids, expert_begin, L, src2dst, seg_indptr, cap, i, &ovf);
-        if (threadIdx.x == 0) {
+        if (lane == 0) {
             ll_src2dst[i] = (int32_t)row;
             if (ovf) set_status(status, CDL_STATUS_LL_OVERFLOW);
         }
         any |= row >= 0;
     }
     if (!any) return;
-    const uint4 *src = x + t * chunks;
-    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kRowThreads * kRowUnroll) {
-        uint4 v[kRowUnroll];
+    const uint32_t row_bytes = (uint32_t)(chunks * 16);
+    const uint32_t voff = (uint32_t)lane * 16u;
+    const rsrc_t xr = make_rsrc(x + t * chunks, row_bytes);
+    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kMaxChunks * kWave) {
+        const uint32_t pass = (uint32_t)(c0 * 16);
+        u32x4 v[kMaxChunks];
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-            const int64_t c = c0 + u * kRowThreads + threadIdx.x;
-            v[u] = (c < chunks) ? src[c] : make_uint4(0, 0, 0, 0);
-        }
+        for (int u = 0; u < kMaxChunks; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         for (int j = 0; j < k; ++j) {
             bool ovf;
             const int64_t row = ll_row(ids, expert_begin, L, src2dst, seg_indptr, cap, t * k + j, &ovf);
             if (row < 0) continue;
-            uint4 *o = out + row * chunks;
+            const rsrc_t o = make_rsrc(out + row * chunks, row_bytes);
 #pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const int64_t c = c0 + u * kRowThreads + threadIdx.x;
-                if (c < chunks) o[c] = v[u];
-            }
+            for (int u = 0; u < kMaxChunks; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
         }
     }
 }
@@ -445,20 +649,27 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
 // combine: gather + weighted fp32 reduce
 // ---------------------------------------------------------------------------
 
-// One block per token.  acc = fma(w_j, y_j, acc) over the valid slots j in
+constexpr int kCombThreads = 128;
+constexpr int kCombUnroll = 8;       // chunks per lane per pass
+
+// One workgroup per token.  acc = fma(w_j, y_j, acc) over the valid slots j in
 // ascending order from +0 (v_fma_f32 is correctly rounded), one bf16 rounding.
-__global__ __launch_bounds__(kRowThreads) void combine_rows_v16(
-    const uint4 *__restrict__ y, int64_t y_rows, int64_t chunks, const int32_t *__restrict__ map,
-    const float *__restrict__ wts, int32_t k, uint4 *__restrict__ out,
+__global__ __launch_bounds__(kCombThreads) void combine_rows_v16(
+    const u32x4 *__restrict__ y, int64_t y_rows, int64_t chunks, const int32_t *__restrict__ map,
+    const float *__restrict__ wts, int32_t k, u32x4 *__restrict__ out,
     int32_t *__restrict__ status)
 {
     const int64_t t = blockIdx.x;
     const int32_t *m = map + t * k;
     const float *w = wts + t * k;
-    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kRowThreads * kRowUnroll) {
-        float acc[kRowUnroll][8];
+    const uint32_t row_bytes = (uint32_t)(chunks * 16);
+    const uint32_t voff = threadIdx.x * 16u;
+    const rsrc_t orow = make_rsrc(out + t * chunks, row_bytes);
+    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kCombThreads * kCombUnroll) {
+        const uint32_t pass = (uint32_t)(c0 * 16);
+        float acc[kCombUnroll][8];
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u)
+        for (int u = 0; u < kCombUnroll; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
         for (int j = 0; j < k; ++j) {
@@ -469,15 +680,12 @@ __global__ __launch_bounds__(kRowThreads) void combine_rows_v16(
                 continue;
             }
             const float wj = w[j];
-            const uint4 *yr = y + (int64_t)r * chunks;
-            uint4 v[kRowUnroll];
+            const rsrc_t yr = make_rsrc(y + (int64_t)r * chunks, row_bytes);
+            u32x4 v[kCombUnroll];
 #pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const int64_t c = c0 + u * kRowThreads + threadIdx.x;
-                v[u] = (c < chunks) ? yr[c] : make_uint4(0, 0, 0, 0);
-            }
+            for (int u = 0; u < kCombUnroll; ++u) v[u] = buf_ld16_stream(yr, voff, pass + u * kCombThreads * 16);
 #pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
+            for (int u = 0; u < kCombUnroll; ++u) {
                 acc[u][0] = fmaf(wj, bf16_lo(v[u].x), acc[u][0]);
                 acc[u][1] = fmaf(wj, bf16_hi(v[u].x), acc[u][1]);
                 acc[u][2] = fmaf(wj, bf16_lo(v[u].y), acc[u][2]);
@@ -488,19 +696,17 @@ __global__ __launch_bounds__(kRowThreads) void combine_rows_v16(
                 acc[u][7] = fmaf(wj, bf16_hi(v[u].w), acc[u][7]);
             }
         }
-        uint4 *o = out + t * chunks;
 #pragma unroll
-        for (int u = 0; u < kRowUnroll; ++u) {
-            const int64_t c = c0 + u * kRowThreads + threadIdx.x;
-            if (c < chunks)
-                o[c] = make_uint4(pack_bf16_rne(acc[u][0], acc[u][1]), pack_bf16_rne(acc[u][2], acc[u][3]),
-                                  pack_bf16_rne(acc[u][4], acc[u][5]), pack_bf16_rne(acc[u][6], acc[u][7]));
-        }
+        for (int u = 0; u < kCombUnroll; ++u)
+            buf_st16_stream(orow,
+                        u32x4{pack_bf16_rne(acc[u][0], acc[u][1]), pack_bf16_rne(acc[u][2], acc[u][3]),
+                              pack_bf16_rne(acc[u][4], acc[u][5]), pack_bf16_rne(acc[u][6], acc[u][7])},
+                        voff, pass + u * kCombThreads * 16);
     }
 }
 
 // Any H, any 2-byte alignment.
-__global__ __launch_bounds__(kRowThreads) void combine_rows_u16(
+__global__ __launch_bounds__(128) void combine_rows_u16(
     const uint16_t *__restrict__ y, int64_t y_rows, int64_t H, const int32_t *__restrict__ map,
     const float *__restrict__ wts, int32_t k, uint16_t *__restrict__ out,
     int32_t *__restrict__ status)
@@ -508,7 +714,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_rows_u16(
     const int64_t t = blockIdx.x;
     const int32_t *m = map + t * k;
     const float *w = wts + t * k;
-    for (int64_t h = threadIdx.x; h < H; h += kRowThreads) {
+    for (int64_t h = threadIdx.x; h < H; h += 128) {
         float acc = 0.0f;
         for (int j = 0; j < k; ++j) {
             const int32_t r = m[j];
@@ -527,7 +733,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_rows_u16(
 // host helpers
 // ---------------------------------------------------------------------------
 
-inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 inline int launch_status()
 {
@@ -543,9 +749,73 @@ inline int check_tk(int64_t T, int32_t k)
 
 inline size_t layout_ws_bytes(int64_t T, int32_t k, int32_t L)
 {
-    const int64_t tiles = layout_tiles(T * k);
-    const size_t bytes = (size_t)tiles * (size_t)L * sizeof(int32_t);
+    const Plan p = make_plan(T, k, L);
+    const size_t bytes = (size_t)p.S * (size_t)L * sizeof(int32_t);
     return ((bytes + 255) & ~(size_t)255) + 256;
+}
+
+inline int check_layout_args(const int32_t *topk_ids, int64_t T, int32_t k, int32_t L,
+                             const int32_t *counts, const int64_t *seg_indptr,
+                             const int32_t *src2dst, const int32_t *reorder, const void *ws,
+                             size_t ws_bytes)
+{
+    int rc = check_tk(T, k);
+    if (rc != CDL_OK) return rc;
+    if (L < 1 || L > CDL_MAX_LOCAL_EXPERTS) return CDL_ERR_BAD_SIZE;
+    if (!counts || !seg_indptr) return CDL_ERR_NULL_POINTER;
+    if (T > 0 && (!topk_ids || !src2dst || !reorder)) return CDL_ERR_NULL_POINTER;
+    if (!ws) return CDL_ERR_NULL_POINTER;
+    if (ws_bytes < layout_ws_bytes(T, k, L)) return CDL_ERR_WORKSPACE;
+    return CDL_OK;
+}
+
+template <int MODE>
+int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
+{
+    const size_t lds = (size_t)(2 * a.L + p.tpb * a.k) * sizeof(int32_t);
+    const dim3 grid((unsigned)(p.nblocks > 0 ? p.nblocks : 1));
+    switch (p.tpb) {
+    case 1: permute_kernel<1, MODE><<<grid, dim3(1 * kWave), lds, s>>>(a); break;
+    case 2: permute_kernel<2, MODE><<<grid, dim3(2 * kWave), lds, s>>>(a); break;
+    case 4: permute_kernel<4, MODE><<<grid, dim3(4 * kWave), lds, s>>>(a); break;
+    default: permute_kernel<8, MODE><<<grid, dim3(8 * kWave), lds, s>>>(a); break;
+    }
+    return launch_status();
+}
+
+// Kernel A then kernel B in the given mode.
+template <int MODE>
+int run_layout(PermuteArgs a, void *ws, hipStream_t s)
+{
+    const Plan p = make_plan(a.T, a.k, a.L);
+    a.sb_counts = (const int32_t *)ws;
+    a.S = p.S;
+    a.sbb = p.sbb;
+    a.sb_slots = p.sb_slots;
+    if (p.S > 0) {
+        layout_count_kernel<<<dim3((unsigned)p.S), dim3(kCountThreads), a.L * sizeof(int32_t), s>>>(
+            a.ids, p.n, p.sb_slots, a.expert_begin, a.L, (int32_t *)ws);
+        int rc = launch_status();
+        if (rc != CDL_OK) return rc;
+    }
+    return launch_permute<MODE>(a, p, s);
+}
+
+PermuteArgs layout_args(const int32_t *topk_ids, int64_t T, int32_t k, int32_t expert_begin,
+                        int32_t L, int32_t *counts, int64_t *seg_indptr, int32_t *src2dst,
+                        int32_t *reorder)
+{
+    PermuteArgs a = {};
+    a.ids = topk_ids;
+    a.T = T;
+    a.k = k;
+    a.expert_begin = expert_begin;
+    a.L = L;
+    a.counts = counts;
+    a.seg_indptr = seg_indptr;
+    a.src2dst = src2dst;
+    a.reorder = reorder;
+    return a;
 }
 
 }  // namespace
@@ -566,29 +836,61 @@ int cdl_dispatch_layout(const int32_t *topk_ids, int64_t T, int32_t k, int32_t e
                         int32_t L, int32_t *counts, int64_t *seg_indptr, int32_t *src2dst,
                         int32_t *reorder_topk_ids, void *ws, size_t ws_bytes, void *stream)
 {
-    int rc = check_tk(T, k);
+    int rc = check_layout_args(topk_ids, T, k, L, counts, seg_indptr, src2dst, reorder_topk_ids,
+                               ws, ws_bytes);
     if (rc != CDL_OK) return rc;
-    if (L < 1 || L > CDL_MAX_LOCAL_EXPERTS) return CDL_ERR_BAD_SIZE;
-    if (!counts || !seg_indptr) return CDL_ERR_NULL_POINTER;
-    if (T > 0 && (!topk_ids || !src2dst || !reorder_topk_ids)) return CDL_ERR_NULL_POINTER;
-    const size_t need = layout_ws_bytes(T, k, L);
-    if (!ws) return CDL_ERR_NULL_POINTER;
-    if (ws_bytes < need) return CDL_ERR_WORKSPACE;
+    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, counts, seg_indptr, src2dst,
+                                reorder_topk_ids);
+    return run_layout<kLayoutOnly>(a, ws, (hipStream_t)stream);
+}
 
-    hipStream_t s = (hipStream_t)stream;
-    const int64_t n = T * k;
-    const int64_t tiles = layout_tiles(n);
-    int32_t *tile_counts = (int32_t *)ws;
-    if (tiles > 0) {
-        layout_count_kernel<<<dim3((unsigned)tiles), dim3(kLayoutThreads), L * sizeof(int32_t), s>>>(
-            topk_ids, n, expert_begin, L, tile_counts);
-        if ((rc = launch_status()) != CDL_OK) return rc;
-    }
-    const size_t lds = (size_t)(1 + kLayoutWaves) * L * sizeof(int32_t);
-    layout_rank_kernel<<<dim3((unsigned)(tiles > 0 ? tiles : 1)), dim3(kLayoutThreads), lds, s>>>(
-        topk_ids, n, expert_begin, L, tile_counts, tiles, counts, seg_indptr, src2dst,
-        reorder_topk_ids);
-    return launch_status();
+int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
+                int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
+                int32_t *src2dst, int32_t *reorder_topk_ids, uint16_t *out, int64_t cap_rows,
+                int32_t *status, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_layout_args(topk_ids, T, k, L, counts, seg_indptr, src2dst, reorder_topk_ids,
+                               ws, ws_bytes);
+    if (rc != CDL_OK) return rc;
+    if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
+    if (cap_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
+    if (T > 0 && !x) return CDL_ERR_NULL_POINTER;
+    if (cap_rows > 0 && !out) return CDL_ERR_NULL_POINTER;
+    if (H % 8 != 0 || !aligned(x, 16) || !aligned(out, 16)) return CDL_ERR_UNSUPPORTED;
+    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, counts, seg_indptr, src2dst,
+                                reorder_topk_ids);
+    a.x = (const u32x4 *)x;
+    a.chunks = H / 8;
+    a.out = (u32x4 *)out;
+    a.cap_rows = cap_rows;
+    a.status = status;
+    return run_layout<kRowsBf16>(a, ws, (hipStream_t)stream);
+}
+
+int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
+                    int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
+                    int32_t *src2dst, int32_t *reorder_topk_ids, uint8_t *out_q,
+                    float *out_scales, int64_t cap_rows, int32_t *status, void *ws,
+                    size_t ws_bytes, void *stream)
+{
+    int rc = check_layout_args(topk_ids, T, k, L, counts, seg_indptr, src2dst, reorder_topk_ids,
+                               ws, ws_bytes);
+    if (rc != CDL_OK) return rc;
+    if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
+    if (H % CDL_FP8_GROUP != 0) return CDL_ERR_UNSUPPORTED;
+    if (cap_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
+    if (T > 0 && !x) return CDL_ERR_NULL_POINTER;
+    if (cap_rows > 0 && (!out_q || !out_scales)) return CDL_ERR_NULL_POINTER;
+    if (!aligned(x, 16) || !aligned(out_q, 8) || !aligned(out_scales, 4)) return CDL_ERR_UNSUPPORTED;
+    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, counts, seg_indptr, src2dst,
+                                reorder_topk_ids);
+    a.x = (const u32x4 *)x;
+    a.chunks = H / 8;
+    a.out_q = (u32x2 *)out_q;
+    a.out_s = out_scales;
+    a.cap_rows = cap_rows;
+    a.status = status;
+    return run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
 }
 
 int cdl_dispatch(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *src2dst,
@@ -602,12 +904,12 @@ int cdl_dispatch(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32
     if (cap_rows > 0 && !out) return CDL_ERR_NULL_POINTER;
     if (cap_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
     hipStream_t s = (hipStream_t)stream;
-    if (H % 8 == 0 && aligned16(x) && aligned16(out)) {
-        scatter_rows_v16<<<dim3((unsigned)T), dim3(kRowThreads), 0, s>>>(
-            (const uint4 *)x, H / 8, k, src2dst, (uint4 *)out, cap_rows, status);
+    if (H % 8 == 0 && aligned(x, 16) && aligned(out, 16)) {
+        scatter_rows_kernel<false><<<dim3((unsigned)((T + kRowTok - 1) / kRowTok)), dim3(kRowThreads), 0, s>>>(
+            (const u32x4 *)x, T, H / 8, k, src2dst, (u32x4 *)out, nullptr, nullptr, cap_rows, status);
     } else {
-        scatter_rows_u16<<<dim3((unsigned)T), dim3(kRowThreads), 0, s>>>(x, H, k, src2dst, out,
-                                                                            cap_rows, status);
+        scatter_rows_u16<<<dim3((unsigned)T), dim3(128), 0, s>>>(x, H, k, src2dst, out, cap_rows,
+                                                                  status);
     }
     return launch_status();
 }
@@ -624,13 +926,13 @@ int cdl_dispatch_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const i
     if (!x || !src2dst) return CDL_ERR_NULL_POINTER;
     if (cap_rows > 0 && (!out_q || !out_scales)) return CDL_ERR_NULL_POINTER;
     if (cap_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
-    if (!aligned16(x) || (cap_rows > 0 && ((uintptr_t)out_q & 7u) != 0) ||
-        (cap_rows > 0 && ((uintptr_t)out_scales & 3u) != 0))
+    if (!aligned(x, 16) || (cap_rows > 0 && !aligned(out_q, 8)) ||
+        (cap_rows > 0 && !aligned(out_scales, 4)))
         return CDL_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    scatter_rows_fp8<<<dim3((unsigned)T), dim3(kRowThreads), 0, s>>>(
-        (const uint4 *)x, H / 8, k, src2dst, (uint2 *)out_q, out_scales, H / CDL_FP8_GROUP,
-        cap_rows, status);
+    scatter_rows_kernel<true><<<dim3((unsigned)((T + kRowTok - 1) / kRowTok)), dim3(kRowThreads), 0, s>>>(
+        (const u32x4 *)x, T, H / 8, k, src2dst, nullptr, (u32x2 *)out_q, out_scales, cap_rows,
+        status);
     return launch_status();
 }
 
@@ -647,14 +949,15 @@ int cdl_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
     if (!counts || !seg_indptr || !masked_m) return CDL_ERR_NULL_POINTER;
     if (T > 0 && (!x || !topk_ids || !src2dst || !ll_src2dst)) return CDL_ERR_NULL_POINTER;
     if (cap > 0 && !out) return CDL_ERR_NULL_POINTER;
-    if ((T > 0 && !aligned16(x)) || (cap > 0 && !aligned16(out))) return CDL_ERR_UNSUPPORTED;
+    if ((T > 0 && !aligned(x, 16)) || (cap > 0 && !aligned(out, 16))) return CDL_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
-    // one block per token; at least enough blocks to write masked_m
+    // one wave per token; at least enough workgroups to write masked_m
     const int64_t mm_blocks = (L + kRowThreads - 1) / kRowThreads;
-    const int64_t grid = T > mm_blocks ? T : mm_blocks;
+    const int64_t tok_blocks = (T + kRowTok - 1) / kRowTok;
+    const int64_t grid = tok_blocks > mm_blocks ? tok_blocks : mm_blocks;
     scatter_rows_ll<<<dim3((unsigned)grid), dim3(kRowThreads), 0, s>>>(
-        (const uint4 *)x, T, H / 8, k, topk_ids, expert_begin, L, src2dst, seg_indptr, counts,
-        cap, (uint4 *)out, masked_m, ll_src2dst, status);
+        (const u32x4 *)x, T, H / 8, k, topk_ids, expert_begin, L, src2dst, seg_indptr, counts,
+        cap, (u32x4 *)out, masked_m, ll_src2dst, status);
     return launch_status();
 }
 
@@ -670,12 +973,12 @@ int cdl_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32_t *map
     if (y_rows > 0 && !y) return CDL_ERR_NULL_POINTER;
     if (y_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
     hipStream_t s = (hipStream_t)stream;
-    if (H % 8 == 0 && aligned16(y) && aligned16(out)) {
-        combine_rows_v16<<<dim3((unsigned)T), dim3(kRowThreads), 0, s>>>(
-            (const uint4 *)y, y_rows, H / 8, map, topk_weights, k, (uint4 *)out, status);
+    if (H % 8 == 0 && aligned(y, 16) && aligned(out, 16)) {
+        combine_rows_v16<<<dim3((unsigned)T), dim3(kCombThreads), 0, s>>>(
+            (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k, (u32x4 *)out, status);
     } else {
-        combine_rows_u16<<<dim3((unsigned)T), dim3(kRowThreads), 0, s>>>(
-            y, y_rows, H, map, topk_weights, k, out, status);
+        combine_rows_u16<<<dim3((unsigned)T), dim3(128), 0, s>>>(y, y_rows, H, map, topk_weights,
+                                                                  k, out, status);
     }
     return launch_status();
 }

@@ -114,6 +114,40 @@ int cdl_dispatch_layout(const int32_t *topk_ids, int64_t T, int32_t k,
                         void *stream);
 
 /*
+ * cdl_permute -- layout and normal-mode scatter in one call, the older
+ * dispatcher's permute step ([0.4.4 diff],
+ * _DeepEPDispatcherImplNormal._deepep_permute: preprocess the received top-k
+ * ids into reorder_topk_ids / src2dst / seg_indptr, then copy every token row
+ * to its destination rows).  Two kernel launches; the row loads are issued
+ * before the layout arithmetic, inside the second.
+ *
+ * Layout arguments and outputs are exactly those of cdl_dispatch_layout
+ * (same workspace size); x, out, cap_rows and status as for cdl_dispatch.
+ * R is not known before the call: `out` must hold cap_rows rows with
+ * cap_rows an upper bound (T*k always suffices) or a known R; a destination at
+ * or beyond cap_rows is dropped and sets CDL_STATUS_ROWS_OVERFLOW.
+ * Requires H % 8 == 0 and 16-byte aligned x and out (CDL_ERR_UNSUPPORTED
+ * otherwise).
+ */
+int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
+                int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
+                int32_t *src2dst, int32_t *reorder_topk_ids, uint16_t *out, int64_t cap_rows,
+                int32_t *status, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * cdl_permute_fp8 -- cdl_permute with the per-token, per-128-group fp8
+ * quantisation of cdl_dispatch_fp8 on the scatter ([deepep.py],
+ * _DeepEPDispatcherImplNormal.dispatch_a).  out_q [cap_rows, H] E4M3FN bytes,
+ * out_scales [cap_rows, H/128] fp32.  Requires H % 128 == 0, 16-byte aligned
+ * x, 8-byte aligned out_q and 4-byte aligned out_scales.
+ */
+int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
+                    int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
+                    int32_t *src2dst, int32_t *reorder_topk_ids, uint8_t *out_q,
+                    float *out_scales, int64_t cap_rows, int32_t *status, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/*
  * cdl_dispatch -- normal-mode bf16 row scatter ([0.4.4 diff],
  * _deepep_permute: the PreReorder permute copies every token row to the
  * destination rows src2dst names; it takes no weights).

@@ -147,3 +147,48 @@ def test_binding_refuses_cpu_tensors():
     import torch
     with pytest.raises(ValueError):
         cdl.dispatch_layout(torch.zeros(4, 2, dtype=torch.int32), 0, 4)
+
+
+def test_permute_rejects():
+    lib = cdl.library()
+    names = ["x", "T", "H", "k", "ids", "b", "L", "counts", "seg", "s2d", "reorder", "out", "cap",
+             "status", "ws", "wsb", "stream"]
+    base = [FAKE, 4, 256, 2, FAKE, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 16, NULL, FAKE, 1 << 20, NULL]
+
+    def call(**over):
+        a = list(base)
+        for n, v in over.items():
+            a[names.index(n)] = v
+        return lib.cdl_permute(*a)
+
+    assert call(k=0) == ESIZE
+    assert call(L=0) == ESIZE
+    assert call(H=0) == ESIZE
+    assert call(cap=-1) == ESIZE
+    assert call(H=100) == EUNSUP
+    assert call(x=ctypes.c_void_p(0x1004)) == EUNSUP
+    assert call(out=NULL) == ENULL
+    assert call(x=NULL) == ENULL
+    assert call(ws=NULL) == ENULL
+    assert call(wsb=8) == EWS
+    assert call(cap=1 << 31) == EBIG
+
+
+def test_permute_fp8_rejects():
+    lib = cdl.library()
+    names = ["x", "T", "H", "k", "ids", "b", "L", "counts", "seg", "s2d", "reorder", "q", "s",
+             "cap", "status", "ws", "wsb", "stream"]
+    base = [FAKE, 4, 256, 2, FAKE, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, NULL, FAKE,
+            1 << 20, NULL]
+
+    def call(**over):
+        a = list(base)
+        for n, v in over.items():
+            a[names.index(n)] = v
+        return lib.cdl_permute_fp8(*a)
+
+    assert call(H=200) == EUNSUP
+    assert call(q=NULL) == ENULL
+    assert call(s=NULL) == ENULL
+    assert call(q=ctypes.c_void_p(0x1004)) == EUNSUP
+    assert call(counts=NULL) == ENULL

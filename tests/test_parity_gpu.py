@@ -345,3 +345,128 @@ def test_deterministic_repeats():
     assert np.array_equal(npy(a[0].src2dst), npy(b[0].src2dst))
     assert np.array_equal(bits16(a[2]), bits16(b[2]))
     assert np.array_equal(bits16(a[3]), bits16(b[3]))
+
+
+# --------------------------------------------------------------------------
+# fused permute (layout + scatter in one call)
+# --------------------------------------------------------------------------
+
+PERMUTE = PARITY + [W.WORKLOADS["dsv3_prefill"], W.WORKLOADS["ll_decode"].scaled(mode="normal"),
+                    W.WORKLOADS["zipf_prefill"].scaled(T=5000, H=256)]
+
+
+@pytest.mark.parametrize("w", PERMUTE, ids=lambda w: "%s_T%d_H%d_b%d" % (w.name, w.T, w.H, w.expert_begin))
+def test_permute_parity(w):
+    announce("permute %s T=%d H=%d b=%d" % (w.name, w.T, w.H, w.expert_begin))
+    x, ids, wts = W.make_inputs(w)
+    c, s, d, r = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s[-1])
+    cap = R + 1                                  # one spare row, then canaries
+    buf = bf16_filled(cap + 3, w.H, 0x7F7F)
+    st = status_word()
+    lay, _ = cdl.permute(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out=buf[:cap], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    check_layout(lay, ids, w.expert_begin, w.L)
+    P = oracle.dispatch(W.bf16_bits(x), d, w.k, R)
+    got = bits16(buf)
+    assert np.array_equal(got[:R], P)
+    assert np.all(got[R:] == 0x7F7F)
+
+
+def test_permute_default_capacity_and_repeat():
+    """rows defaults to T*k (no host sync); two calls give identical bits."""
+    w = W.WORKLOADS["zipf_prefill"].scaled(T=3000, H=512)
+    announce("permute default cap T=%d" % w.T)
+    x, ids, wts = W.make_inputs(w)
+    lay1, out1 = cdl.permute(x.to(DEV), ids.to(DEV), 0, w.L)
+    lay2, out2 = cdl.permute(x.to(DEV), ids.to(DEV), 0, w.L)
+    torch.cuda.synchronize()
+    assert out1.shape[0] == w.T * w.k
+    R = lay1.num_rows()
+    assert torch.equal(lay1.src2dst, lay2.src2dst)
+    assert torch.equal(out1[:R].view(torch.int16), out2[:R].view(torch.int16))
+    _, s, d, _ = check_layout(lay1, ids, 0, w.L)
+    assert np.array_equal(bits16(out1[:R]), oracle.dispatch(W.bf16_bits(x), d, w.k, R))
+
+
+def test_permute_rows_overflow_flag():
+    w = W.WORKLOADS["tiny"]
+    announce("permute cap < R")
+    x, ids, wts = W.make_inputs(w)
+    _, s, d, _ = oracle.layout(ids.numpy(), 0, w.L)
+    R = int(s[-1])
+    cap = R - 5
+    buf = bf16_filled(R, w.H, 0x7F7F)
+    st = status_word()
+    lay, _ = cdl.permute(x.to(DEV), ids.to(DEV), 0, w.L, out=buf[:cap], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == cdl.CDL_STATUS_ROWS_OVERFLOW
+    P = oracle.dispatch(W.bf16_bits(x), d, w.k, R)
+    got = bits16(buf)
+    assert np.array_equal(got[:cap], P[:cap]) and np.all(got[cap:] == 0x7F7F)
+
+
+@pytest.mark.parametrize("case", ["T0", "T1", "all_invalid", "max_k", "max_L", "H8"])
+def test_permute_edge_cases(case):
+    announce("permute edge " + case)
+    g = torch.Generator().manual_seed(zlib.crc32(case.encode()))
+    T, k, L, E, H, b = 200, 4, 16, 64, 64, 0
+    if case == "T0":
+        T = 0
+    elif case == "T1":
+        T, k = 1, 3
+    elif case == "max_k":
+        T, k, L, E = 150, 64, 128, 128
+    elif case == "max_L":
+        T, k, L, E = 900, 8, 2048, 2048
+    elif case == "H8":
+        H = 8
+    if case in ("max_k", "max_L"):
+        ids = torch.multinomial(torch.ones(max(T, 1), E), k, generator=g).to(torch.int32)[:T]
+    else:
+        ids = torch.randint(-1, E + 1, (T, k), generator=g, dtype=torch.int32)
+    if case == "all_invalid":
+        ids = torch.randint(L, E, (T, k), generator=g, dtype=torch.int32)
+    x = torch.randn(T, H, generator=g).to(torch.bfloat16)
+    c, s, d, r = oracle.layout(ids.numpy(), b, L)
+    R = int(s[-1])
+    buf = bf16_filled(R + 2, H, 0x7F7F)
+    lay, _ = cdl.permute(x.to(DEV), ids.to(DEV), b, L, out=buf[:R])
+    torch.cuda.synchronize()
+    check_layout(lay, ids, b, L)
+    got = bits16(buf)
+    assert np.array_equal(got[:R], oracle.dispatch(W.bf16_bits(x), d, k, R))
+    assert np.all(got[R:] == 0x7F7F)
+
+
+@pytest.mark.parametrize("w", [W.WORKLOADS["fp8_dispatch"],
+                               W.WORKLOADS["fp8_dispatch"].scaled(T=333, H=1152, expert_begin=96)],
+                         ids=lambda w: "T%d_H%d" % (w.T, w.H))
+def test_permute_fp8_parity(w):
+    announce("permute fp8 T=%d H=%d" % (w.T, w.H))
+    x, ids, wts = W.make_inputs(w)
+    _, s, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s[-1])
+    G = w.H // 128
+    q = torch.full((R + 2, w.H), 0xA5, dtype=torch.uint8, device=DEV)
+    sc = torch.full((R + 2, G), -7.0, dtype=torch.float32, device=DEV)
+    st = status_word()
+    lay, _, _ = cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q[:R],
+                                out_scales=sc[:R], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    check_layout(lay, ids, w.expert_begin, w.L)
+    Q, S = oracle.dispatch_fp8(W.bf16_bits(x), d, w.k, R)
+    gq, gs = u8(q), npy(sc)
+    assert np.array_equal(gq[:R], Q)
+    assert np.array_equal(gs[:R].view(np.uint32), S.view(np.uint32))
+    assert np.all(gq[R:] == 0xA5) and np.all(gs[R:] == -7.0)
+
+
+def test_permute_rejects_unsupported_shapes():
+    ids = torch.zeros(2, 1, dtype=torch.int32, device=DEV)
+    with pytest.raises(cdl.CdlError):
+        cdl.permute(torch.zeros(2, 100, dtype=torch.bfloat16, device=DEV), ids, 0, 1)
+    with pytest.raises(cdl.CdlError):
+        cdl.permute_fp8(torch.zeros(2, 200, dtype=torch.bfloat16, device=DEV), ids, 0, 1)
