@@ -87,6 +87,12 @@ __device__ __forceinline__ int32_t buf_ld4(rsrc_t r, uint32_t voff, uint32_t sof
 
 __device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar)
+// value: the compiler does not infer that threadIdx.x / 64 is uniform, and a
+// buffer resource derived from a non-uniform value costs a readfirstlane
+// loop around every access.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / 64); }
+
 // ---------------------------------------------------------------------------
 // number formats
 // ---------------------------------------------------------------------------
@@ -126,17 +132,37 @@ __device__ __forceinline__ void set_status(int32_t *status, int32_t bit)
 
 // ---------------------------------------------------------------------------
 // fp8 group quantisation of one 16-byte chunk (8 bf16) held by a lane; the
-// 16 lanes of a 16-lane segment hold one group of 128 elements.
+// 16 lanes of a DPP row hold one group of 128 elements.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float quant_in(float v, float a, float s)
+// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), which hold one
+// 128-element group: quad_perm swaps at distance 1 and 2 give each quad its
+// maximum, row_half_mirror pairs the two quads of each half row, row_mirror
+// the two halves.  Four VALU ops, no LDS traffic.
+template <int CTRL>
+__device__ __forceinline__ float dpp_max_step(float a)
 {
-    if (a > 0.0f) {
-        v = v / s;                      // correctly rounded binary32 division
-        v = fminf(fmaxf(v, -448.0f), 448.0f);
-    }
-    return v;
+    const int b = __builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xF, 0xF, false);
+    return fmaxf(a, __int_as_float(b));
 }
+__device__ __forceinline__ float row16_max(float a)
+{
+    a = dpp_max_step<0xB1>(a);    // quad_perm [1,0,3,2]
+    a = dpp_max_step<0x4E>(a);    // quad_perm [2,3,0,1]
+    a = dpp_max_step<0x141>(a);   // row_half_mirror
+    a = dpp_max_step<0x140>(a);   // row_mirror
+    return a;
+}
+
+// Groups with amax >= kFastQuotientMinAmax divide by the scale with one
+// correctly rounded reciprocal y = 1/s per group and Markstein's correction
+// step per element: q0 = x*y, r = fma(-q0, s, x) (exact), q = fma(r, y, q0).
+// An exhaustive check over every bf16 amax and every bf16 x with |x| <= amax
+// (about 1.06e9 pairs) finds the e4m3fn code of this quotient equal to that of
+// the correctly rounded x / s whenever amax >= 3.3e-32; below 2^-96 the
+// element-wise division is kept.  x = +-0 keeps its sign explicitly (the
+// correction step would return +0).
+constexpr float kFastQuotientMinAmax = 0x1p-96f;
 
 // Returns the 8 e4m3fn bytes of the chunk; *scale receives the group scale.
 __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float *scale)
@@ -146,22 +172,47 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float *scale)
     float a = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
+    a = row16_max(a);
+    const float s = a / 448.0f;                 // correctly rounded binary32 division
+    float q[8];
+    if (a >= kFastQuotientMinAmax) {
+        const float y = 1.0f / s;               // correctly rounded reciprocal
 #pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) a = fmaxf(a, __shfl_xor(a, m, 16));
-    const float s = a / 448.0f;
-    const uint32_t lo = pack2_e4m3(quant_in(f[0], a, s), quant_in(f[1], a, s)) |
-                        (pack2_e4m3(quant_in(f[2], a, s), quant_in(f[3], a, s)) << 16);
-    const uint32_t hi = pack2_e4m3(quant_in(f[4], a, s), quant_in(f[5], a, s)) |
-                        (pack2_e4m3(quant_in(f[6], a, s), quant_in(f[7], a, s)) << 16);
+        for (int e = 0; e < 8; ++e) {
+            const float q0 = f[e] * y;
+            const float q1 = fmaf(fmaf(-q0, s, f[e]), y, q0);
+            q[e] = f[e] == 0.0f ? f[e] : q1;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = a > 0.0f ? f[e] / s : f[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = fminf(fmaxf(q[e], -448.0f), 448.0f);
+    const uint32_t lo = pack2_e4m3(q[0], q[1]) | (pack2_e4m3(q[2], q[3]) << 16);
+    const uint32_t hi = pack2_e4m3(q[4], q[5]) | (pack2_e4m3(q[6], q[7]) << 16);
     *scale = s;
     return u32x2{lo, hi};
 }
+
+// Quantises chunks [U0, U0 + NQ) of a lane's pass (chunk u of the pass is row
+// chunk c0 + u*64 + lane) and stores the e4m3fn bytes and the group scales to
+// every valid destination in dlist[0..k).  A row pass is quantised in parts so
+// that only NQ chunks of quantisation temporaries are live at a time while all
+// of the pass's loads were issued together.
+template <int U0, int NQ, int NCH>
+__device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], const int32_t *dlist, int k,
+                                               int lane, int64_t c0, int64_t chunks,
+                                               u32x2 *out_q, float *out_s, int64_t cap_rows,
+                                               int32_t *status);
 
 // ---------------------------------------------------------------------------
 // layout plan
 // ---------------------------------------------------------------------------
 
-constexpr int kMaxChunks = 16;          // 16-byte chunks a lane holds per pass
+constexpr int kMaxChunks = 16;          // 16-byte chunks a lane holds per pass (bf16 rows)
+constexpr int kMaxChunksFp8 = 8;        // the same for rows quantised on the way: fewer live
+                                        // registers for the quantisation temporaries
 constexpr int kCountThreads = 256;
 
 struct Plan {
@@ -243,6 +294,37 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     for (int e = threadIdx.x; e < L; e += kCountThreads) row[e] = hist[e];
 }
 
+template <int U0, int NQ, int NCH>
+__device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], const int32_t *dlist, int k,
+                                               int lane, int64_t c0, int64_t chunks,
+                                               u32x2 *out_q, float *out_s, int64_t cap_rows,
+                                               int32_t *status)
+{
+    u32x2 q[NQ];
+    float sc[NQ];
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) q[u] = quant_chunk(v[U0 + u], &sc[u]);
+    const uint32_t q_bytes = (uint32_t)(chunks * 8);
+    const uint32_t s_bytes = (uint32_t)(chunks / 16 * 4);
+    const bool group_head = (lane & 15) == 0;       // one scale per 16-lane group
+    for (int j = 0; j < k; ++j) {
+        const int32_t dst = uniform(dlist[j]);
+        if (dst < 0) continue;
+        if ((int64_t)dst >= cap_rows) {
+            if (c0 == 0 && U0 == 0 && lane == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
+            continue;
+        }
+        const rsrc_t oq = make_rsrc(out_q + (int64_t)dst * chunks, q_bytes);
+        const rsrc_t os = make_rsrc(out_s + (int64_t)dst * (chunks / 16), s_bytes);
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            buf_st8(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + (U0 + u) * kWave * 8);
+            if (group_head)
+                buf_st4(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + (U0 + u) * 16);
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // layout kernel B (+ fused row scatter): the permute
 // ---------------------------------------------------------------------------
@@ -254,7 +336,7 @@ template <int NW>
 __device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t *lds_waves, int32_t *total)
 {
     const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
+    const int w = wave_id();
     int32_t incl = v;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -300,7 +382,7 @@ struct PermuteArgs {
 };
 
 // One workgroup per TPB tokens, one wave per token.
-//  0. the wave of token t loads its row (first kMaxChunks chunks per lane)
+//  0. the wave of token t loads its row (first NC chunks per lane)
 //     if the token has a valid slot;
 //  1. tot[e] = all valid slots of e; cur[e] = valid slots of e before this
 //     workgroup's first slot (superblock counts of earlier superblocks plus a
@@ -315,6 +397,7 @@ template <int TPB, int MODE>
 __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 {
     constexpr int NT = TPB * kWave;
+    constexpr int NC = MODE == kRowsFp8 ? kMaxChunksFp8 : kMaxChunks;
     extern __shared__ int32_t lds[];
     const int L = a.L;
     int32_t *tot = lds;
@@ -324,7 +407,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int wave = wave_id();
     const int k = a.k;
     const int64_t blk = blockIdx.x;
     const int64_t t_begin = blk * TPB;
@@ -338,13 +421,13 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     if (MODE != kLayoutOnly && t < a.T) {
         for (int j = 0; j < k; ++j) tok_valid |= local_expert(a.ids[t * k + j], a.expert_begin, L) >= 0;
     }
-    u32x4 v[kMaxChunks];
+    u32x4 v[NC];
     const uint32_t row_bytes = (uint32_t)(a.chunks * 16);
     const uint32_t voff = (uint32_t)lane * 16u;
     const rsrc_t xr = make_rsrc(a.x + (tok_valid ? t * a.chunks : 0), row_bytes);
     if (MODE != kLayoutOnly && tok_valid) {
 #pragma unroll
-        for (int u = 0; u < kMaxChunks; ++u) v[u] = buf_ld16(xr, voff, u * kWave * 16);
+        for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, u * kWave * 16);
     }
 
     // 1. totals and offsets before this workgroup
@@ -444,11 +527,11 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     // 4. rows
     if (MODE == kLayoutOnly || !tok_valid) return;
     const int32_t *my = dsts + wave * k;
-    for (int64_t c0 = 0; c0 < a.chunks; c0 += (int64_t)kMaxChunks * kWave) {
+    for (int64_t c0 = 0; c0 < a.chunks; c0 += (int64_t)NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
         if (c0 > 0) {
 #pragma unroll
-            for (int u = 0; u < kMaxChunks; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+            for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         }
         if (MODE == kRowsBf16) {
             for (int j = 0; j < k; ++j) {
@@ -460,34 +543,12 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
                 }
                 const rsrc_t o = make_rsrc(a.out + (int64_t)dst * a.chunks, row_bytes);
 #pragma unroll
-                for (int u = 0; u < kMaxChunks; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
+                for (int u = 0; u < NC; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
             }
         } else {
-            // fp8 row: 8 bytes per chunk, one fp32 scale per 16 chunks (written
-            // by the first lane of each 16-lane group)
-            u32x2 q[kMaxChunks];
-            float sc[kMaxChunks];
-#pragma unroll
-            for (int u = 0; u < kMaxChunks; ++u) q[u] = quant_chunk(v[u], &sc[u]);
-            const uint32_t q_bytes = (uint32_t)(a.chunks * 8);
-            const uint32_t s_bytes = (uint32_t)(a.chunks / 16 * 4);
-            const bool group_head = (lane & 15) == 0;
-            for (int j = 0; j < k; ++j) {
-                const int32_t dst = uniform(my[j]);
-                if (dst < 0) continue;
-                if ((int64_t)dst >= a.cap_rows) {
-                    if (c0 == 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
-                    continue;
-                }
-                const rsrc_t oq = make_rsrc(a.out_q + (int64_t)dst * a.chunks, q_bytes);
-                const rsrc_t os = make_rsrc(a.out_s + (int64_t)dst * (a.chunks / 16), s_bytes);
-#pragma unroll
-                for (int u = 0; u < kMaxChunks; ++u) {
-                    buf_st8(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + u * kWave * 8);
-                    if (group_head)
-                        buf_st4(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + u * 16);
-                }
-            }
+            store_fp8_part<0, NC / 2>(v, my, k, lane, c0, a.chunks, a.out_q, a.out_s, a.cap_rows, a.status);
+            store_fp8_part<NC / 2, NC / 2>(v, my, k, lane, c0, a.chunks, a.out_q, a.out_s, a.cap_rows,
+                                          a.status);
         }
     }
 }
@@ -499,7 +560,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 constexpr int kRowTok = 4;                       // tokens (waves) per workgroup
 constexpr int kRowThreads = kRowTok * kWave;
 
-// One wave per token: the wave loads up to kMaxChunks 16-byte chunks per
+// One wave per token: the wave loads up to NC 16-byte chunks per
 // lane of the row once, then stores them to every valid destination.
 template <bool FP8>
 __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
@@ -507,8 +568,9 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
     const int32_t *__restrict__ src2dst, u32x4 *__restrict__ out, u32x2 *__restrict__ out_q,
     float *__restrict__ out_s, int64_t cap_rows, int32_t *__restrict__ status)
 {
+    constexpr int NC = FP8 ? kMaxChunksFp8 : kMaxChunks;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kRowTok + threadIdx.x / kWave;
+    const int64_t t = (int64_t)blockIdx.x * kRowTok + wave_id();
     if (t >= T) return;
     const int32_t *d = src2dst + t * k;
     bool any = false;
@@ -517,16 +579,15 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
     const uint32_t row_bytes = (uint32_t)(chunks * 16);
     const uint32_t voff = (uint32_t)lane * 16u;
     const rsrc_t xr = make_rsrc(x + t * chunks, row_bytes);
-    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kMaxChunks * kWave) {
+    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
-        u32x4 v[kMaxChunks];
+        u32x4 v[NC];
 #pragma unroll
-        for (int u = 0; u < kMaxChunks; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
-        u32x2 q[kMaxChunks];
-        float sc[kMaxChunks];
+        for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         if (FP8) {
-#pragma unroll
-            for (int u = 0; u < kMaxChunks; ++u) q[u] = quant_chunk(v[u], &sc[u]);
+            store_fp8_part<0, NC / 2>(v, d, k, lane, c0, chunks, out_q, out_s, cap_rows, status);
+            store_fp8_part<NC / 2, NC / 2>(v, d, k, lane, c0, chunks, out_q, out_s, cap_rows, status);
+            continue;
         }
         for (int j = 0; j < k; ++j) {
             const int32_t dst = d[j];
@@ -535,21 +596,9 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
                 if (c0 == 0 && lane == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
                 continue;
             }
-            if (FP8) {
-                const rsrc_t oq = make_rsrc(out_q + (int64_t)dst * chunks, (uint32_t)(chunks * 8));
-                const rsrc_t os = make_rsrc(out_s + (int64_t)dst * (chunks / 16), (uint32_t)(chunks / 16 * 4));
-                const bool group_head = (lane & 15) == 0;
+            const rsrc_t o = make_rsrc(out + (int64_t)dst * chunks, row_bytes);
 #pragma unroll
-                for (int u = 0; u < kMaxChunks; ++u) {
-                    buf_st8(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + u * kWave * 8);
-                    if (group_head)
-                        buf_st4(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + u * 16);
-                }
-            } else {
-                const rsrc_t o = make_rsrc(out + (int64_t)dst * chunks, row_bytes);
-#pragma unroll
-                for (int u = 0; u < kMaxChunks; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
-            }
+            for (int u = 0; u < NC; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
         }
     }
 }
@@ -612,7 +661,7 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
         if (e < L) masked_m[e] = (int32_t)((int64_t)counts[e] < cap ? counts[e] : cap);
     }
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kRowTok + threadIdx.x / kWave;
+    const int64_t t = (int64_t)blockIdx.x * kRowTok + wave_id();
     if (t >= T) return;
     bool any = false;
     for (int j = 0; j < k; ++j) {

@@ -470,3 +470,36 @@ def test_permute_rejects_unsupported_shapes():
         cdl.permute(torch.zeros(2, 100, dtype=torch.bfloat16, device=DEV), ids, 0, 1)
     with pytest.raises(cdl.CdlError):
         cdl.permute_fp8(torch.zeros(2, 200, dtype=torch.bfloat16, device=DEV), ids, 0, 1)
+
+
+def test_fp8_group_magnitudes():
+    """Groups at every binary magnitude from bf16 subnormals to the largest
+    bf16 values: both sides of the fast-quotient threshold (amax 2^-96), groups
+    made of subnormals, signed zeros, and all-zero groups."""
+    announce("fp8 group magnitudes")
+    g = torch.Generator().manual_seed(4242)
+    exps = list(range(-133, 128))
+    G = len(exps) * 2
+    base = torch.randn(G, 128, generator=g)
+    scale = torch.tensor([2.0 ** e for e in exps for _ in range(2)], dtype=torch.float64)
+    # finite inputs only (NaN / Inf are outside the contract): clip at the
+    # largest bf16 magnitude below the overflow threshold
+    vals = (base.double() * scale[:, None]).clamp(-3.3e38, 3.3e38).float().to(torch.bfloat16)
+    assert torch.isfinite(vals.float()).all()
+    xb = W.bf16_bits(vals).copy()
+    xb[1, :] = 0x0000                      # an all-zero group
+    xb[3, ::3] = 0x8000                    # signed zeros inside a group
+    rows = -(-G // 8)
+    xfull = np.zeros((rows * 8, 128), np.uint16)
+    xfull[:G] = xb
+    xfull = xfull.reshape(rows, 1024)
+    ids = torch.arange(rows, dtype=torch.int32).reshape(rows, 1)
+    lay = cdl.dispatch_layout(ids.to(DEV), 0, rows)
+    q, s = cdl.dispatch_fp8(W.bits_to_bf16(xfull).to(DEV), lay)
+    lay2, q2, s2 = cdl.permute_fp8(W.bits_to_bf16(xfull).to(DEV), ids.to(DEV), 0, rows, rows=rows)
+    torch.cuda.synchronize()
+    _, _, d, _ = oracle.layout(ids.numpy(), 0, rows)
+    Q, S = oracle.dispatch_fp8(xfull, d, 1, rows)
+    assert np.array_equal(u8(q), Q) and np.array_equal(u8(q2), Q)
+    assert np.array_equal(npy(s).view(np.uint32), S.view(np.uint32))
+    assert np.array_equal(npy(s2).view(np.uint32), S.view(np.uint32))
