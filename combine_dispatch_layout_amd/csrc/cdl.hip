@@ -158,9 +158,9 @@ __device__ __forceinline__ float row16_max(float a)
 // correctly rounded reciprocal y = 1/s per group and Markstein's correction
 // step per element: q0 = x*y, r = fma(-q0, s, x) (exact), q = fma(r, y, q0).
 // An exhaustive check over every bf16 amax and every bf16 x with |x| <= amax
-// (about 1.06e9 pairs) finds the e4m3fn code of this quotient equal to that of
-// the correctly rounded x / s whenever amax >= 3.3e-32; below 2^-96 the
-// element-wise division is kept.  x = +-0 keeps its sign explicitly (the
+// (about 1.06e9 pairs, tests/fast_quotient_check.c) finds the e4m3fn code of
+// this quotient equal to that of the correctly rounded x / s whenever
+// amax >= 3.3e-32; below 2^-96 the element-wise division is kept.  x = +-0 keeps its sign explicitly (the
 // correction step would return +0).
 constexpr float kFastQuotientMinAmax = 0x1p-96f;
 
