@@ -66,6 +66,9 @@ def lib():
         L.oracle_layout.argtypes = [_i32p, _i64, _i32, _i32, _i32, _i32p, _i64p,
                                     _i32p, _i32p]
         L.oracle_layout.restype = _i64
+        L.oracle_layout_aligned.argtypes = [_i32p, _i64, _i32, _i32, _i32, _i32, _i32p,
+                                            _i64p, _i32p, _i32p]
+        L.oracle_layout_aligned.restype = _i64
         L.oracle_dispatch.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _u16p]
         L.oracle_dispatch.restype = None
         L.oracle_dispatch_ll.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _i32,
@@ -166,6 +169,23 @@ def layout(topk_ids: np.ndarray, expert_begin: int, L: int):
                             src2dst, reorder)
     if R < 0:
         raise MemoryError("oracle_layout failed")
+    return counts, seg, src2dst, reorder[:R].copy()
+
+
+def layout_aligned(topk_ids: np.ndarray, expert_begin: int, L: int, alignment: int):
+    """Layout with segments padded to multiples of `alignment`; padding rows
+    have reorder id -1.  Returns counts, seg_indptr, src2dst, reorder[R_pad]."""
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    counts = np.zeros(L, np.int32)
+    seg = np.zeros(L + 1, np.int64)
+    src2dst = np.zeros(T * k, np.int32)
+    cap = T * k + L * max(alignment - 1, 0)
+    reorder = np.zeros(max(cap, 1), np.int32)
+    R = lib().oracle_layout_aligned(ids.reshape(-1), T, k, expert_begin, L, alignment,
+                                    counts, seg, src2dst, reorder)
+    if R < 0:
+        raise ValueError("oracle_layout_aligned failed")
     return counts, seg, src2dst, reorder[:R].copy()
 
 

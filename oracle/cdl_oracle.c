@@ -216,6 +216,50 @@ int64_t oracle_layout(const int32_t *topk_ids, int64_t T, int32_t k,
     return seg_indptr[L];
 }
 
+/* Layout with every expert segment padded to a multiple of `alignment` rows
+ * ([deepep.py], _DeepEPDispatcherImplNormal._dispatch_core: the normal
+ * dispatch aligns the rows each local expert receives to 128 when the
+ * grouped GEMM is DeepGEMM, else to 1).  Reading: counts stay the true
+ * counts; seg_indptr[e+1] = seg_indptr[e] + alignment * ceil(counts[e] /
+ * alignment); real rows keep the stable order at the start of their segment;
+ * padding rows belong to no slot and their reorder_topk_ids entry is -1.
+ * reorder_topk_ids must hold seg_indptr[L] entries.  Returns seg_indptr[L]. */
+int64_t oracle_layout_aligned(const int32_t *topk_ids, int64_t T, int32_t k,
+                              int32_t expert_begin, int32_t L, int32_t alignment,
+                              int32_t *counts, int64_t *seg_indptr, int32_t *src2dst,
+                              int32_t *reorder_topk_ids)
+{
+    if (alignment < 1)
+        return -1;
+    int64_t n = T * (int64_t)k;
+    for (int32_t e = 0; e < L; ++e)
+        counts[e] = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t e = local_expert(topk_ids[i], expert_begin, L);
+        if (e >= 0)
+            counts[e] += 1;
+    }
+    seg_indptr[0] = 0;
+    for (int32_t e = 0; e < L; ++e) {
+        int64_t padded = ((int64_t)counts[e] + alignment - 1) / alignment * alignment;
+        seg_indptr[e + 1] = seg_indptr[e] + padded;
+    }
+    for (int32_t e = 0; e < L; ++e)
+        for (int64_t r = seg_indptr[e]; r < seg_indptr[e + 1]; ++r)
+            reorder_topk_ids[r] = (r < seg_indptr[e] + counts[e]) ? e : -1;
+    int64_t *cursor = (int64_t *)malloc(sizeof(int64_t) * (size_t)(L > 0 ? L : 1));
+    if (!cursor)
+        return -1;
+    for (int32_t e = 0; e < L; ++e)
+        cursor[e] = seg_indptr[e];
+    for (int64_t i = 0; i < n; ++i) {
+        int32_t e = local_expert(topk_ids[i], expert_begin, L);
+        src2dst[i] = e < 0 ? -1 : (int32_t)cursor[e]++;
+    }
+    free(cursor);
+    return seg_indptr[L];
+}
+
 /* ------------------------------------------------------------------------ */
 /* Dispatch.                                                                 */
 /* ------------------------------------------------------------------------ */

@@ -155,3 +155,76 @@ def test_layout_all_invalid_and_one_hot():
 def test_expected_m_golden(golden):
     for T, n, k, E, want in golden("expected_m.txt"):
         assert oracle.expected_m(int(T), int(n), int(k), int(E)) == int(want)
+
+
+# --------------------------------------------------------------------------
+# expert alignment
+# --------------------------------------------------------------------------
+
+def brute_layout_aligned(ids, b, L, A):
+    counts, _, src_plain, _ = brute_layout(ids, b, L)
+    seg = [0]
+    for c in counts:
+        seg.append(seg[-1] + -(-c // A) * A)
+    plain_seg = [0]
+    for c in counts:
+        plain_seg.append(plain_seg[-1] + c)
+    flat = [int(v) for v in np.asarray(ids).reshape(-1)]
+    loc = [(v - b) if b <= v < b + L else -1 for v in flat]
+    src2dst = [-1 if e < 0 else seg[e] + (src_plain[i] - plain_seg[e]) for i, e in enumerate(loc)]
+    reorder = []
+    for e in range(L):
+        reorder += [e] * counts[e] + [-1] * (seg[e + 1] - seg[e] - counts[e])
+    return counts, seg, src2dst, reorder
+
+
+def test_layout_aligned_golden_example(golden):
+    g = {row[0]: row[1:] for row in golden("layout_worked.txt")}
+    T, k, b, L = (int(g[n][0]) for n in ("T", "k", "expert_begin", "L"))
+    ids = np.array([int(v) for v in g["topk_ids"]], np.int32).reshape(T, k)
+    c, s, d, r = oracle.layout_aligned(ids, b, L, int(g["align"][0]))
+    assert c.tolist() == [int(v) for v in g["counts"]]
+    assert s.tolist() == [int(v) for v in g["aligned_seg_indptr"]]
+    assert d.tolist() == [int(v) for v in g["aligned_src2dst"]]
+    assert r.tolist() == [int(v) for v in g["aligned_reorder_topk_ids"]]
+
+
+@pytest.mark.parametrize("A", [1, 2, 3, 8, 128])
+def test_layout_aligned_bruteforce(A):
+    rng = np.random.default_rng(A)
+    for _ in range(150):
+        T = int(rng.integers(0, 13))
+        k = int(rng.integers(1, 4))
+        E = int(rng.integers(1, 7))
+        L = int(rng.integers(1, E + 1))
+        b = int(rng.integers(0, E - L + 1))
+        ids = rng.integers(-1, E + 1, size=(T, k)).astype(np.int32)
+        c, s, d, r = oracle.layout_aligned(ids, b, L, A)
+        bc, bs, bd, br = brute_layout_aligned(ids, b, L, A)
+        assert c.tolist() == bc and s.tolist() == bs and d.tolist() == bd and r.tolist() == br
+
+
+def test_layout_aligned_one_is_plain_layout():
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=700)
+    ids = W.make_topk_ids(w).numpy()
+    for a, b_ in zip(oracle.layout_aligned(ids, 0, w.L, 1), oracle.layout(ids, 0, w.L)):
+        assert np.array_equal(a, b_)
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill", "zipf_prefill"])
+def test_layout_aligned_invariants(name):
+    w = W.WORKLOADS[name]
+    ids = W.make_topk_ids(w).numpy()
+    A = 128
+    c, s, d, r = oracle.layout_aligned(ids, 0, w.L, A)
+    c0, s0, d0, r0 = oracle.layout(ids, 0, w.L)
+    assert np.array_equal(c, c0)
+    assert np.all(s % A == 0)
+    seg_len = np.diff(s)
+    assert np.all((seg_len >= c) & (seg_len < c + A))
+    valid = d0 >= 0
+    e = r0[d0[valid]]
+    # each real row moves by the padding accumulated before its expert
+    assert np.array_equal(d[valid] - s[e], d0[valid] - s0[e])
+    assert np.all(d[~valid] == -1)
+    assert r.size == s[-1] and np.sum(r == -1) == s[-1] - c.sum()
