@@ -140,8 +140,8 @@ class NormalSet:
         self.a_dispatch = (P(self.x.data_ptr()), T, H, k, P(self.src2dst.data_ptr()),
                            P(self.P.data_ptr()), self.R, P(self.status.data_ptr()), self.stream)
         self.a_permute = (P(self.x.data_ptr()), T, H, k, P(self.ids.data_ptr()), w.expert_begin, L,
-                          P(self.counts.data_ptr()), P(self.seg.data_ptr()),
-                          P(self.src2dst.data_ptr()), P(self.reorder.data_ptr()),
+                          1, P(self.counts.data_ptr()), P(self.seg.data_ptr()),
+                          P(self.src2dst.data_ptr()), P(self.reorder.data_ptr()), T * k,
                           P(self.P.data_ptr()), self.R, P(self.status.data_ptr()),
                           P(self.ws.data_ptr()), wsb, self.stream)
         self.a_combine = (P(self.P.data_ptr()), self.R, H, P(self.src2dst.data_ptr()),
@@ -252,9 +252,9 @@ def measure_fp8(torch, cdl, sets, steps):
         sc = torch.empty(max(s.R, 1), s.H // 128, dtype=torch.float32, device=s.x.device)
         a_scatter = (P(s.x.data_ptr()), s.T, s.H, s.k, P(s.src2dst.data_ptr()), P(q.data_ptr()),
                      P(sc.data_ptr()), s.R, P(s.status.data_ptr()), s.stream)
-        a_perm = (P(s.x.data_ptr()), s.T, s.H, s.k, P(s.ids.data_ptr()), 0, s.L,
+        a_perm = (P(s.x.data_ptr()), s.T, s.H, s.k, P(s.ids.data_ptr()), 0, s.L, 1,
                   P(s.counts.data_ptr()), P(s.seg.data_ptr()), P(s.src2dst.data_ptr()),
-                  P(s.reorder.data_ptr()), P(q.data_ptr()), P(sc.data_ptr()), s.R,
+                  P(s.reorder.data_ptr()), s.T * s.k, P(q.data_ptr()), P(sc.data_ptr()), s.R,
                   P(s.status.data_ptr()), P(s.ws.data_ptr()), s.ws.numel(), s.stream)
         bufs.append((s, a_scatter, a_perm, q, sc))
 

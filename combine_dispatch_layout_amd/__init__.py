@@ -7,6 +7,7 @@ seeded synthetic inputs.
 from .api import (  # noqa: F401
     CDL_STATUS_LL_OVERFLOW,
     CDL_STATUS_MAP_RANGE,
+    CDL_STATUS_REORDER_OVERFLOW,
     CDL_STATUS_ROWS_OVERFLOW,
     FP8_GROUP,
     LIB_PATH,

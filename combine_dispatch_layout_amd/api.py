@@ -34,6 +34,7 @@ CDL_OK = 0
 CDL_STATUS_ROWS_OVERFLOW = 1
 CDL_STATUS_LL_OVERFLOW = 2
 CDL_STATUS_MAP_RANGE = 4
+CDL_STATUS_REORDER_OVERFLOW = 8
 FP8_GROUP = 128
 
 _lib = None
@@ -61,11 +62,14 @@ def library():
         L.cdl_dispatch_layout_workspace_size.restype = sz
         L.cdl_dispatch_layout.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.cdl_dispatch_layout.restype = ctypes.c_int
-        L.cdl_permute.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, vp, vp, i64, vp,
-                                  vp, sz, vp]
+        L.cdl_dispatch_layout_aligned.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp,
+                                                  i64, vp, vp, sz, vp]
+        L.cdl_dispatch_layout_aligned.restype = ctypes.c_int
+        L.cdl_permute.argtypes = [vp, i64, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, i64, vp,
+                                  i64, vp, vp, sz, vp]
         L.cdl_permute.restype = ctypes.c_int
-        L.cdl_permute_fp8.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp,
-                                      i64, vp, vp, sz, vp]
+        L.cdl_permute_fp8.argtypes = [vp, i64, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, i64,
+                                      vp, vp, i64, vp, vp, sz, vp]
         L.cdl_permute_fp8.restype = ctypes.c_int
         L.cdl_dispatch.argtypes = [vp, i64, i64, i32, vp, vp, i64, vp, vp]
         L.cdl_dispatch.restype = ctypes.c_int
@@ -125,10 +129,11 @@ class Layout:
     expert_begin: int
     num_local_experts: int
     topk_ids: torch.Tensor          # [T, k] int32 (global ids)
-    counts: torch.Tensor            # [L] int32
-    seg_indptr: torch.Tensor        # [L+1] int64
+    counts: torch.Tensor            # [L] int32 (true counts)
+    seg_indptr: torch.Tensor        # [L+1] int64 (segments padded to `alignment`)
     src2dst: torch.Tensor           # [T*k] int32
-    reorder_buf: torch.Tensor       # [T*k] int32 (first R entries valid)
+    reorder_buf: torch.Tensor       # [T*k + L*(alignment-1)] int32 (first R entries valid)
+    alignment: int = 1
 
     def num_rows(self) -> int:
         """R, the number of dispatched rows (synchronises with the device)."""
@@ -148,23 +153,24 @@ def layout_workspace_size(T: int, k: int, L: int) -> int:
 
 
 def dispatch_layout(topk_ids: torch.Tensor, expert_begin: int, num_local_experts: int,
-                    workspace: Optional[torch.Tensor] = None) -> Layout:
+                    workspace: Optional[torch.Tensor] = None, alignment: int = 1) -> Layout:
     """Per-expert counts, seg_indptr, src2dst and reorder_topk_ids of the
     rank's slots (global ids outside [expert_begin, expert_begin+L) are
-    invalid).  int64 ids are narrowed to int32 here."""
-    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace)
-    rc = library().cdl_dispatch_layout(_ptr(lay.topk_ids), lay.T, lay.k, lay.expert_begin,
-                                       lay.num_local_experts, _ptr(lay.counts),
-                                       _ptr(lay.seg_indptr), _ptr(lay.src2dst),
-                                       _ptr(lay.reorder_buf), _ptr(ws),
-                                       ws.numel() * ws.element_size(),
-                                       _stream(lay.topk_ids.device))
-    _check(rc, "cdl_dispatch_layout")
+    invalid).  With alignment > 1 every expert segment is padded to a
+    multiple of `alignment` rows (padding rows have reorder id -1).  int64
+    ids are narrowed to int32 here."""
+    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace, alignment)
+    rc = library().cdl_dispatch_layout_aligned(
+        _ptr(lay.topk_ids), lay.T, lay.k, lay.expert_begin, lay.num_local_experts,
+        lay.alignment, _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
+        _ptr(lay.reorder_buf), lay.reorder_buf.numel(), None, _ptr(ws),
+        ws.numel() * ws.element_size(), _stream(lay.topk_ids.device))
+    _check(rc, "cdl_dispatch_layout_aligned")
     return lay
 
 
 def _new_layout(topk_ids: torch.Tensor, expert_begin: int, num_local_experts: int,
-                workspace: Optional[torch.Tensor]):
+                workspace: Optional[torch.Tensor], alignment: int = 1):
     _need_gpu(topk_ids, "topk_ids")
     if topk_ids.dim() != 2:
         raise ValueError("topk_ids must be [T, k]")
@@ -179,39 +185,45 @@ def _new_layout(topk_ids: torch.Tensor, expert_begin: int, num_local_experts: in
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     elif workspace.numel() * workspace.element_size() < ws_bytes:
         raise ValueError("workspace too small: need %d bytes" % ws_bytes)
+    A = int(alignment)
+    if A < 1:
+        raise ValueError("alignment must be >= 1")
     lay = Layout(T, k, int(expert_begin), L, topk_ids,
                  torch.empty(L, dtype=torch.int32, device=dev),
                  torch.empty(L + 1, dtype=torch.int64, device=dev),
                  torch.empty(T * k, dtype=torch.int32, device=dev),
-                 torch.empty(max(T * k, 1), dtype=torch.int32, device=dev))
+                 torch.empty(max(T * k + L * (A - 1), 1), dtype=torch.int32, device=dev), A)
     return lay, workspace
 
 
 def permute(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int, num_local_experts: int,
             out: Optional[torch.Tensor] = None, rows: Optional[int] = None,
             status: Optional[torch.Tensor] = None,
-            workspace: Optional[torch.Tensor] = None) -> Tuple[Layout, torch.Tensor]:
+            workspace: Optional[torch.Tensor] = None,
+            alignment: int = 1) -> Tuple[Layout, torch.Tensor]:
     """Layout + normal-mode scatter in one call (two kernels).  `out` holds
-    `rows` rows (default T*k, an upper bound on R); the first R rows receive
-    the dispatched rows.  Returns (layout, out)."""
+    `rows` rows (default T*k + L*(alignment-1), an upper bound on R); the
+    first R rows receive the dispatched rows (padding rows are not written).
+    Returns (layout, out)."""
     _need(x, "x", torch.bfloat16)
-    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace)
+    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace, alignment)
     T, k, L = lay.T, lay.k, lay.num_local_experts
     if x.dim() != 2 or x.shape[0] != T:
         raise ValueError("x must be [T, H] with T = %d" % T)
     H = x.shape[1]
     if out is None:
-        out = torch.empty(T * k if rows is None else int(rows), H, dtype=torch.bfloat16,
-                          device=x.device)
+        out = torch.empty(lay.reorder_buf.numel() if rows is None else int(rows), H,
+                          dtype=torch.bfloat16, device=x.device)
     _need(out, "out", torch.bfloat16)
     if out.dim() != 2 or out.shape[1] != H:
         raise ValueError("out must be [rows, H]")
     if status is not None:
         _need(status, "status", torch.int32)
     rc = library().cdl_permute(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
-                               _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
-                               _ptr(lay.reorder_buf), _ptr(out), out.shape[0], _ptr(status),
-                               _ptr(ws), ws.numel() * ws.element_size(), _stream(x.device))
+                               lay.alignment, _ptr(lay.counts), _ptr(lay.seg_indptr),
+                               _ptr(lay.src2dst), _ptr(lay.reorder_buf), lay.reorder_buf.numel(),
+                               _ptr(out), out.shape[0], _ptr(status), _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream(x.device))
     _check(rc, "cdl_permute")
     return lay, out
 
@@ -219,18 +231,19 @@ def permute(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int, num_loca
 def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
                 num_local_experts: int, rows: Optional[int] = None,
                 out_q: Optional[torch.Tensor] = None, out_scales: Optional[torch.Tensor] = None,
-                status: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+                status: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                alignment: int = 1):
     """Layout + fp8 (e4m3fn, groups of 128) scatter in one call.  Returns
     (layout, q [rows, H] uint8, scales [rows, H/128] fp32)."""
     _need(x, "x", torch.bfloat16)
-    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace)
+    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace, alignment)
     T, k, L = lay.T, lay.k, lay.num_local_experts
     if x.dim() != 2 or x.shape[0] != T:
         raise ValueError("x must be [T, H] with T = %d" % T)
     H = x.shape[1]
     if H % FP8_GROUP:
         raise CdlError(-3, "permute_fp8 (H must be a multiple of 128)")
-    n = T * k if rows is None else int(rows)
+    n = lay.reorder_buf.numel() if rows is None else int(rows)
     if out_q is None:
         out_q = torch.empty(n, H, dtype=torch.uint8, device=x.device)
     if out_scales is None:
@@ -241,8 +254,9 @@ def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
     if status is not None:
         _need(status, "status", torch.int32)
     rc = library().cdl_permute_fp8(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
-                                   _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
-                                   _ptr(lay.reorder_buf), _ptr(out_q), _ptr(out_scales),
+                                   lay.alignment, _ptr(lay.counts), _ptr(lay.seg_indptr),
+                                   _ptr(lay.src2dst), _ptr(lay.reorder_buf),
+                                   lay.reorder_buf.numel(), _ptr(out_q), _ptr(out_scales),
                                    out_q.shape[0], _ptr(status), _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(x.device))
     _check(rc, "cdl_permute_fp8")

@@ -367,10 +367,12 @@ struct PermuteArgs {
     int64_t S;
     int64_t sbb;
     int64_t sb_slots;
+    int32_t alignment;    // expert segments padded to multiples of this
     int32_t *counts;
     int64_t *seg_indptr;
     int32_t *src2dst;
     int32_t *reorder;
+    int64_t reorder_cap;  // entries of reorder
     // rows
     const u32x4 *x;
     int64_t chunks;       // H / 8
@@ -387,8 +389,10 @@ struct PermuteArgs {
 //  1. tot[e] = all valid slots of e; cur[e] = valid slots of e before this
 //     workgroup's first slot (superblock counts of earlier superblocks plus a
 //     recount of this superblock's earlier slots);
-//  2. exclusive scan of tot over e gives seg_indptr (workgroup 0 publishes
-//     counts and seg_indptr) and cur[e] += seg_indptr[e];
+//  2. exclusive scan over e of tot rounded up to the alignment gives
+//     seg_indptr (workgroup 0 publishes counts and seg_indptr) and
+//     cur[e] += seg_indptr[e]; the padding rows of expert e get reorder id -1
+//     from workgroup e mod gridDim;
 //  3. the workgroup's TPB*k slots are ranked 64 at a time, wave by wave in
 //     slot order, with ballots; the leader of each expert match advances
 //     cur[e]; dst = cur[e] + rank in the match;
@@ -477,23 +481,31 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 
     // 2. scan over experts; each thread owns a run of consecutive experts
     {
+        const int A = a.alignment;
         const int per = (L + NT - 1) / NT;
         const int e0 = tid * per;
         int32_t run = 0;
-        for (int q = 0; q < per && e0 + q < L; ++q) run += tot[e0 + q];
+        for (int q = 0; q < per && e0 + q < L; ++q) run += (tot[e0 + q] + A - 1) / A * A;
         int32_t R = 0;
         int32_t excl = block_exclusive_scan<TPB>(run, scan_tmp, &R);
         for (int q = 0; q < per && e0 + q < L; ++q) {
             const int e = e0 + q;
             const int32_t c = tot[e];
+            const int32_t padded = (c + A - 1) / A * A;
             if (blk == 0) {
                 a.counts[e] = c;
                 a.seg_indptr[e] = excl;
             }
             cur[e] += excl;
-            excl += c;
+            if (padded > c && (int64_t)(e % gridDim.x) == blk) {
+                for (int64_t r = excl + c; r < excl + padded && r < a.reorder_cap; ++r) a.reorder[r] = -1;
+            }
+            excl += padded;
         }
-        if (blk == 0 && tid == 0) a.seg_indptr[L] = R;
+        if (blk == 0 && tid == 0) {
+            a.seg_indptr[L] = R;
+            if ((int64_t)R > a.reorder_cap) set_status(a.status, CDL_STATUS_REORDER_OVERFLOW);
+        }
     }
     __syncthreads();
 
@@ -517,7 +529,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
             }
             if (rel < nslots) {
                 a.src2dst[i] = dst;
-                if (dst >= 0) a.reorder[dst] = e;
+                if (dst >= 0 && (int64_t)dst < a.reorder_cap) a.reorder[dst] = e;
                 if (MODE != kLayoutOnly) dsts[rel] = dst;
             }
         }
@@ -804,15 +816,19 @@ inline size_t layout_ws_bytes(int64_t T, int32_t k, int32_t L)
 }
 
 inline int check_layout_args(const int32_t *topk_ids, int64_t T, int32_t k, int32_t L,
-                             const int32_t *counts, const int64_t *seg_indptr,
-                             const int32_t *src2dst, const int32_t *reorder, const void *ws,
-                             size_t ws_bytes)
+                             int32_t alignment, const int32_t *counts, const int64_t *seg_indptr,
+                             const int32_t *src2dst, const int32_t *reorder, int64_t reorder_cap,
+                             const void *ws, size_t ws_bytes)
 {
     int rc = check_tk(T, k);
     if (rc != CDL_OK) return rc;
     if (L < 1 || L > CDL_MAX_LOCAL_EXPERTS) return CDL_ERR_BAD_SIZE;
+    if (alignment < 1 || alignment > CDL_MAX_ALIGNMENT || reorder_cap < 0) return CDL_ERR_BAD_SIZE;
+    // the largest padded row index must stay below 2^31
+    if (T * k + (int64_t)L * (alignment - 1) > (int64_t)INT32_MAX) return CDL_ERR_TOO_LARGE;
     if (!counts || !seg_indptr) return CDL_ERR_NULL_POINTER;
-    if (T > 0 && (!topk_ids || !src2dst || !reorder)) return CDL_ERR_NULL_POINTER;
+    if (T > 0 && (!topk_ids || !src2dst)) return CDL_ERR_NULL_POINTER;
+    if (reorder_cap > 0 && !reorder) return CDL_ERR_NULL_POINTER;
     if (!ws) return CDL_ERR_NULL_POINTER;
     if (ws_bytes < layout_ws_bytes(T, k, L)) return CDL_ERR_WORKSPACE;
     return CDL_OK;
@@ -851,8 +867,8 @@ int run_layout(PermuteArgs a, void *ws, hipStream_t s)
 }
 
 PermuteArgs layout_args(const int32_t *topk_ids, int64_t T, int32_t k, int32_t expert_begin,
-                        int32_t L, int32_t *counts, int64_t *seg_indptr, int32_t *src2dst,
-                        int32_t *reorder)
+                        int32_t L, int32_t alignment, int32_t *counts, int64_t *seg_indptr,
+                        int32_t *src2dst, int32_t *reorder, int64_t reorder_cap, int32_t *status)
 {
     PermuteArgs a = {};
     a.ids = topk_ids;
@@ -860,10 +876,13 @@ PermuteArgs layout_args(const int32_t *topk_ids, int64_t T, int32_t k, int32_t e
     a.k = k;
     a.expert_begin = expert_begin;
     a.L = L;
+    a.alignment = alignment;
     a.counts = counts;
     a.seg_indptr = seg_indptr;
     a.src2dst = src2dst;
     a.reorder = reorder;
+    a.reorder_cap = reorder_cap;
+    a.status = status;
     return a;
 }
 
@@ -885,45 +904,56 @@ int cdl_dispatch_layout(const int32_t *topk_ids, int64_t T, int32_t k, int32_t e
                         int32_t L, int32_t *counts, int64_t *seg_indptr, int32_t *src2dst,
                         int32_t *reorder_topk_ids, void *ws, size_t ws_bytes, void *stream)
 {
-    int rc = check_layout_args(topk_ids, T, k, L, counts, seg_indptr, src2dst, reorder_topk_ids,
-                               ws, ws_bytes);
+    return cdl_dispatch_layout_aligned(topk_ids, T, k, expert_begin, L, 1, counts, seg_indptr,
+                                       src2dst, reorder_topk_ids, T * k, nullptr, ws, ws_bytes,
+                                       stream);
+}
+
+int cdl_dispatch_layout_aligned(const int32_t *topk_ids, int64_t T, int32_t k,
+                                int32_t expert_begin, int32_t L, int32_t alignment,
+                                int32_t *counts, int64_t *seg_indptr, int32_t *src2dst,
+                                int32_t *reorder_topk_ids, int64_t reorder_cap, int32_t *status,
+                                void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_layout_args(topk_ids, T, k, L, alignment, counts, seg_indptr, src2dst,
+                               reorder_topk_ids, reorder_cap, ws, ws_bytes);
     if (rc != CDL_OK) return rc;
-    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, counts, seg_indptr, src2dst,
-                                reorder_topk_ids);
+    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, alignment, counts, seg_indptr,
+                                src2dst, reorder_topk_ids, reorder_cap, status);
     return run_layout<kLayoutOnly>(a, ws, (hipStream_t)stream);
 }
 
 int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
-                int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
-                int32_t *src2dst, int32_t *reorder_topk_ids, uint16_t *out, int64_t cap_rows,
-                int32_t *status, void *ws, size_t ws_bytes, void *stream)
+                int32_t expert_begin, int32_t L, int32_t alignment, int32_t *counts,
+                int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
+                int64_t reorder_cap, uint16_t *out, int64_t cap_rows, int32_t *status, void *ws,
+                size_t ws_bytes, void *stream)
 {
-    int rc = check_layout_args(topk_ids, T, k, L, counts, seg_indptr, src2dst, reorder_topk_ids,
-                               ws, ws_bytes);
+    int rc = check_layout_args(topk_ids, T, k, L, alignment, counts, seg_indptr, src2dst,
+                               reorder_topk_ids, reorder_cap, ws, ws_bytes);
     if (rc != CDL_OK) return rc;
     if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
     if (cap_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
     if (T > 0 && !x) return CDL_ERR_NULL_POINTER;
     if (cap_rows > 0 && !out) return CDL_ERR_NULL_POINTER;
     if (H % 8 != 0 || !aligned(x, 16) || !aligned(out, 16)) return CDL_ERR_UNSUPPORTED;
-    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, counts, seg_indptr, src2dst,
-                                reorder_topk_ids);
+    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, alignment, counts, seg_indptr,
+                                src2dst, reorder_topk_ids, reorder_cap, status);
     a.x = (const u32x4 *)x;
     a.chunks = H / 8;
     a.out = (u32x4 *)out;
     a.cap_rows = cap_rows;
-    a.status = status;
     return run_layout<kRowsBf16>(a, ws, (hipStream_t)stream);
 }
 
 int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
-                    int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
-                    int32_t *src2dst, int32_t *reorder_topk_ids, uint8_t *out_q,
-                    float *out_scales, int64_t cap_rows, int32_t *status, void *ws,
-                    size_t ws_bytes, void *stream)
+                    int32_t expert_begin, int32_t L, int32_t alignment, int32_t *counts,
+                    int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
+                    int64_t reorder_cap, uint8_t *out_q, float *out_scales, int64_t cap_rows,
+                    int32_t *status, void *ws, size_t ws_bytes, void *stream)
 {
-    int rc = check_layout_args(topk_ids, T, k, L, counts, seg_indptr, src2dst, reorder_topk_ids,
-                               ws, ws_bytes);
+    int rc = check_layout_args(topk_ids, T, k, L, alignment, counts, seg_indptr, src2dst,
+                               reorder_topk_ids, reorder_cap, ws, ws_bytes);
     if (rc != CDL_OK) return rc;
     if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
     if (H % CDL_FP8_GROUP != 0) return CDL_ERR_UNSUPPORTED;
@@ -931,14 +961,13 @@ int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
     if (T > 0 && !x) return CDL_ERR_NULL_POINTER;
     if (cap_rows > 0 && (!out_q || !out_scales)) return CDL_ERR_NULL_POINTER;
     if (!aligned(x, 16) || !aligned(out_q, 8) || !aligned(out_scales, 4)) return CDL_ERR_UNSUPPORTED;
-    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, counts, seg_indptr, src2dst,
-                                reorder_topk_ids);
+    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, alignment, counts, seg_indptr,
+                                src2dst, reorder_topk_ids, reorder_cap, status);
     a.x = (const u32x4 *)x;
     a.chunks = H / 8;
     a.out_q = (u32x2 *)out_q;
     a.out_s = out_scales;
     a.cap_rows = cap_rows;
-    a.status = status;
     return run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
 }
 

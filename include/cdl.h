@@ -67,10 +67,12 @@ extern "C" {
 #define CDL_STATUS_ROWS_OVERFLOW 1  /* a destination row >= cap_rows */
 #define CDL_STATUS_LL_OVERFLOW 2    /* an expert received more than cap rows */
 #define CDL_STATUS_MAP_RANGE 4      /* a combine map entry >= y_rows */
+#define CDL_STATUS_REORDER_OVERFLOW 8 /* padded rows exceed the reorder_topk_ids capacity */
 
 #define CDL_MAX_TOPK 64
 #define CDL_MAX_LOCAL_EXPERTS 2048
 #define CDL_FP8_GROUP 128
+#define CDL_MAX_ALIGNMENT 1024
 
 /*
  * cdl_dispatch_layout_workspace_size -- bytes of device workspace that
@@ -114,6 +116,30 @@ int cdl_dispatch_layout(const int32_t *topk_ids, int64_t T, int32_t k,
                         void *stream);
 
 /*
+ * cdl_dispatch_layout_aligned -- cdl_dispatch_layout with every expert
+ * segment padded to a multiple of `alignment` rows ([deepep.py],
+ * _DeepEPDispatcherImplNormal._dispatch_core: the normal dispatch aligns the
+ * rows each local expert receives to 128 for DeepGEMM, else to 1).
+ *
+ *   alignment         1..CDL_MAX_ALIGNMENT
+ *   counts            true (unpadded) counts
+ *   seg_indptr        seg_indptr[e+1] = seg_indptr[e] + alignment*ceil(counts[e]/alignment)
+ *   src2dst           seg_indptr[e_i] + rank of slot i among e_i's slots
+ *   reorder_topk_ids  [reorder_cap] int32: e for the first counts[e] rows of
+ *                     segment e, -1 for its padding rows; entries at or beyond
+ *                     reorder_cap are not written and set
+ *                     CDL_STATUS_REORDER_OVERFLOW in *status (may be NULL).
+ *                     T*k + L*(alignment-1) entries always suffice.
+ * Padding rows of the dispatched buffer are never written by any dispatch.
+ * Rejects T*k + L*(alignment-1) >= 2^31 with CDL_ERR_TOO_LARGE.
+ */
+int cdl_dispatch_layout_aligned(const int32_t *topk_ids, int64_t T, int32_t k,
+                                int32_t expert_begin, int32_t L, int32_t alignment,
+                                int32_t *counts, int64_t *seg_indptr, int32_t *src2dst,
+                                int32_t *reorder_topk_ids, int64_t reorder_cap, int32_t *status,
+                                void *ws, size_t ws_bytes, void *stream);
+
+/*
  * cdl_permute -- layout and normal-mode scatter in one call, the older
  * dispatcher's permute step ([0.4.4 diff],
  * _DeepEPDispatcherImplNormal._deepep_permute: preprocess the received top-k
@@ -121,18 +147,21 @@ int cdl_dispatch_layout(const int32_t *topk_ids, int64_t T, int32_t k,
  * to its destination rows).  Two kernel launches; the row loads are issued
  * before the layout arithmetic, inside the second.
  *
- * Layout arguments and outputs are exactly those of cdl_dispatch_layout
- * (same workspace size); x, out, cap_rows and status as for cdl_dispatch.
- * R is not known before the call: `out` must hold cap_rows rows with
- * cap_rows an upper bound (T*k always suffices) or a known R; a destination at
- * or beyond cap_rows is dropped and sets CDL_STATUS_ROWS_OVERFLOW.
+ * Layout arguments and outputs are exactly those of
+ * cdl_dispatch_layout_aligned (alignment 1 gives cdl_dispatch_layout's; same
+ * workspace size); x, out, cap_rows and status as for cdl_dispatch.
+ * R (the padded row count seg_indptr[L]) is not known before the call: `out`
+ * must hold cap_rows rows with cap_rows an upper bound (T*k + L*(alignment-1)
+ * always suffices) or a known R; a destination at or beyond cap_rows is
+ * dropped and sets CDL_STATUS_ROWS_OVERFLOW.  Padding rows are not written.
  * Requires H % 8 == 0 and 16-byte aligned x and out (CDL_ERR_UNSUPPORTED
  * otherwise).
  */
 int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
-                int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
-                int32_t *src2dst, int32_t *reorder_topk_ids, uint16_t *out, int64_t cap_rows,
-                int32_t *status, void *ws, size_t ws_bytes, void *stream);
+                int32_t expert_begin, int32_t L, int32_t alignment, int32_t *counts,
+                int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
+                int64_t reorder_cap, uint16_t *out, int64_t cap_rows, int32_t *status, void *ws,
+                size_t ws_bytes, void *stream);
 
 /*
  * cdl_permute_fp8 -- cdl_permute with the per-token, per-128-group fp8
@@ -142,10 +171,10 @@ int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_
  * x, 8-byte aligned out_q and 4-byte aligned out_scales.
  */
 int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
-                    int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
-                    int32_t *src2dst, int32_t *reorder_topk_ids, uint8_t *out_q,
-                    float *out_scales, int64_t cap_rows, int32_t *status, void *ws,
-                    size_t ws_bytes, void *stream);
+                    int32_t expert_begin, int32_t L, int32_t alignment, int32_t *counts,
+                    int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
+                    int64_t reorder_cap, uint8_t *out_q, float *out_scales, int64_t cap_rows,
+                    int32_t *status, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * cdl_dispatch -- normal-mode bf16 row scatter ([0.4.4 diff],

@@ -83,6 +83,27 @@ def test_layout_rejects(kw, code):
     assert layout_call(**kw) == code
 
 
+def test_dispatch_layout_aligned_rejects():
+    f = cdl.library().cdl_dispatch_layout_aligned
+    # ids, T, k, b, L, A, counts, seg, s2d, reorder, rcap, status, ws, wsb, stream
+    base = [FAKE, 16, 2, 0, 4, 8, FAKE, FAKE, FAKE, FAKE, 64, NULL, FAKE, 1 << 20, NULL]
+    names = ["ids", "T", "k", "b", "L", "A", "counts", "seg", "s2d", "reorder", "rcap", "status",
+             "ws", "wsb", "stream"]
+
+    def call(**over):
+        a = list(base)
+        for n, v in over.items():
+            a[names.index(n)] = v
+        return f(*a)
+
+    assert call(A=0) == ESIZE
+    assert call(A=4096) == ESIZE
+    assert call(rcap=-5) == ESIZE
+    assert call(counts=NULL) == ENULL
+    assert call(reorder=NULL) == ENULL
+    assert call(wsb=4) == EWS
+
+
 def test_dispatch_rejects():
     lib = cdl.library()
     # x, T, H, k, src2dst, out, cap_rows, status, stream
@@ -151,9 +172,10 @@ def test_binding_refuses_cpu_tensors():
 
 def test_permute_rejects():
     lib = cdl.library()
-    names = ["x", "T", "H", "k", "ids", "b", "L", "counts", "seg", "s2d", "reorder", "out", "cap",
-             "status", "ws", "wsb", "stream"]
-    base = [FAKE, 4, 256, 2, FAKE, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, 16, NULL, FAKE, 1 << 20, NULL]
+    names = ["x", "T", "H", "k", "ids", "b", "L", "A", "counts", "seg", "s2d", "reorder", "rcap",
+             "out", "cap", "status", "ws", "wsb", "stream"]
+    base = [FAKE, 4, 256, 2, FAKE, 0, 8, 1, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 16, NULL, FAKE,
+            1 << 20, NULL]
 
     def call(**over):
         a = list(base)
@@ -172,13 +194,19 @@ def test_permute_rejects():
     assert call(ws=NULL) == ENULL
     assert call(wsb=8) == EWS
     assert call(cap=1 << 31) == EBIG
+    assert call(A=0) == ESIZE
+    assert call(A=1025) == ESIZE
+    assert call(rcap=-1) == ESIZE
+    assert call(reorder=NULL) == ENULL
+    assert call(reorder=NULL, rcap=0) != ENULL      # no reorder output requested
+    assert call(T=(1 << 28) - 1, k=8, A=1024, L=2048) == EBIG   # padded rows reach 2^31
 
 
 def test_permute_fp8_rejects():
     lib = cdl.library()
-    names = ["x", "T", "H", "k", "ids", "b", "L", "counts", "seg", "s2d", "reorder", "q", "s",
-             "cap", "status", "ws", "wsb", "stream"]
-    base = [FAKE, 4, 256, 2, FAKE, 0, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, NULL, FAKE,
+    names = ["x", "T", "H", "k", "ids", "b", "L", "A", "counts", "seg", "s2d", "reorder", "rcap",
+             "q", "s", "cap", "status", "ws", "wsb", "stream"]
+    base = [FAKE, 4, 256, 2, FAKE, 0, 8, 1, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 16, NULL, FAKE,
             1 << 20, NULL]
 
     def call(**over):

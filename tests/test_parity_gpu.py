@@ -503,3 +503,95 @@ def test_fp8_group_magnitudes():
     assert np.array_equal(u8(q), Q) and np.array_equal(u8(q2), Q)
     assert np.array_equal(npy(s).view(np.uint32), S.view(np.uint32))
     assert np.array_equal(npy(s2).view(np.uint32), S.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# expert alignment
+# --------------------------------------------------------------------------
+
+ALIGNED = [W.WORKLOADS["tiny"], W.WORKLOADS["dsv3_prefill"].scaled(T=1000, H=512),
+           W.WORKLOADS["zipf_prefill"].scaled(T=2000, H=256)]
+
+
+@pytest.mark.parametrize("A", [2, 16, 128])
+@pytest.mark.parametrize("w", ALIGNED, ids=lambda w: "%s_T%d" % (w.name, w.T))
+def test_permute_aligned_parity(w, A):
+    announce("aligned %s T=%d A=%d" % (w.name, w.T, A))
+    x, ids, wts = W.make_inputs(w)
+    c, s, d, r = oracle.layout_aligned(ids.numpy(), w.expert_begin, w.L, A)
+    R = int(s[-1])
+    # layout alone
+    lay = cdl.dispatch_layout(ids.to(DEV), w.expert_begin, w.L, alignment=A)
+    torch.cuda.synchronize()
+    assert np.array_equal(npy(lay.counts), c) and np.array_equal(npy(lay.seg_indptr), s)
+    assert np.array_equal(npy(lay.src2dst), d)
+    assert np.array_equal(npy(lay.reorder_topk_ids), r)
+    # fused permute into a canaried buffer: real rows bit-exact, padding untouched
+    buf = bf16_filled(R + 2, w.H, 0x7F7F)
+    st = status_word()
+    lay2, _ = cdl.permute(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out=buf[:R], status=st,
+                          alignment=A)
+    out = cdl.combine(buf[:R], lay2.src2dst, wts.to(DEV), status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(npy(lay2.src2dst), d)
+    assert np.array_equal(npy(lay2.reorder_topk_ids), r)
+    P = oracle.dispatch(W.bf16_bits(x), d, w.k, R, fill=0x7F7F)
+    assert np.array_equal(bits16(buf[:R]), P)                 # padding rows keep 0x7F7F
+    assert np.all(bits16(buf[R:]) == 0x7F7F)
+    # the combine reads only real rows: same result as the unaligned path
+    c0, s0, d0, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    want = oracle.combine(oracle.dispatch(W.bf16_bits(x), d0, w.k, int(s0[-1])), d0,
+                          wts.numpy(), w.T, w.k)
+    assert np.array_equal(bits16(out), want)
+
+
+def test_permute_fp8_aligned_parity():
+    w = W.WORKLOADS["fp8_dispatch"].scaled(T=600, H=1024)
+    A = 128
+    announce("aligned fp8 T=%d" % w.T)
+    x, ids, wts = W.make_inputs(w)
+    c, s, d, r = oracle.layout_aligned(ids.numpy(), w.expert_begin, w.L, A)
+    R = int(s[-1])
+    q = torch.full((R, w.H), 0xA5, dtype=torch.uint8, device=DEV)
+    sc = torch.full((R, w.H // 128), -7.0, dtype=torch.float32, device=DEV)
+    lay, _, _ = cdl.permute_fp8(x.to(DEV), ids.to(DEV), 0, w.L, out_q=q, out_scales=sc, alignment=A)
+    torch.cuda.synchronize()
+    assert np.array_equal(npy(lay.src2dst), d)
+    Q, S = oracle.dispatch_fp8(W.bf16_bits(x), d, w.k, R)
+    real = np.zeros(R, bool)
+    real[d[d >= 0]] = True
+    assert np.array_equal(u8(q)[real], Q[real])
+    assert np.array_equal(npy(sc)[real].view(np.uint32), S[real].view(np.uint32))
+    assert np.all(u8(q)[~real] == 0xA5) and np.all(npy(sc)[~real] == -7.0)
+
+
+def test_layout_aligned_reorder_capacity_flag():
+    """A reorder_topk_ids capacity below the padded row count: entries past
+    it are not written and the status bit is set."""
+    import ctypes
+    w = W.WORKLOADS["tiny"]
+    announce("aligned reorder capacity")
+    ids = W.make_topk_ids(w)
+    A = 64
+    c, s, d, r = oracle.layout_aligned(ids.numpy(), 0, w.L, A)
+    R = int(s[-1])
+    cap = R - 100
+    idd = ids.to(DEV)
+    counts = torch.empty(w.L, dtype=torch.int32, device=DEV)
+    seg = torch.empty(w.L + 1, dtype=torch.int64, device=DEV)
+    s2d = torch.empty(w.T * w.k, dtype=torch.int32, device=DEV)
+    reorder = torch.full((R,), 12345, dtype=torch.int32, device=DEV)
+    ws = torch.empty(cdl.layout_workspace_size(w.T, w.k, w.L), dtype=torch.uint8, device=DEV)
+    st = status_word()
+    P = ctypes.c_void_p
+    rc = cdl.library().cdl_dispatch_layout_aligned(
+        P(idd.data_ptr()), w.T, w.k, 0, w.L, A, P(counts.data_ptr()), P(seg.data_ptr()),
+        P(s2d.data_ptr()), P(reorder.data_ptr()), cap, P(st.data_ptr()), P(ws.data_ptr()),
+        ws.numel(), P(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert int(st.item()) == cdl.CDL_STATUS_REORDER_OVERFLOW
+    assert np.array_equal(npy(s2d), d) and np.array_equal(npy(seg), s)
+    got = npy(reorder)
+    assert np.array_equal(got[:cap], r[:cap]) and np.all(got[cap:] == 12345)
