@@ -23,5 +23,7 @@ from .api import (  # noqa: F401
     ll_expected_m,
     permute,
     permute_fp8,
+    rank_layout,
+    RankLayout,
     status_string,
 )

@@ -71,6 +71,10 @@ def library():
         L.cdl_permute_fp8.argtypes = [vp, i64, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, i64,
                                       vp, vp, i64, vp, vp, sz, vp]
         L.cdl_permute_fp8.restype = ctypes.c_int
+        L.cdl_rank_layout_workspace_size.argtypes = [i64, i32, i32, i32, i32]
+        L.cdl_rank_layout_workspace_size.restype = sz
+        L.cdl_rank_layout.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.cdl_rank_layout.restype = ctypes.c_int
         L.cdl_dispatch.argtypes = [vp, i64, i64, i32, vp, vp, i64, vp, vp]
         L.cdl_dispatch.restype = ctypes.c_int
         L.cdl_dispatch_fp8.argtypes = [vp, i64, i64, i32, vp, vp, vp, i64, vp, vp]
@@ -261,6 +265,43 @@ def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
                                    ws.numel() * ws.element_size(), _stream(x.device))
     _check(rc, "cdl_permute_fp8")
     return lay, out_q, out_scales
+
+
+@dataclasses.dataclass
+class RankLayout:
+    """Where a token batch goes before the exchange (device tensors)."""
+    num_tokens_per_rank: torch.Tensor       # [R] int32
+    num_tokens_per_rdma_rank: torch.Tensor  # [R / ranks_per_node] int32
+    num_tokens_per_expert: torch.Tensor     # [E] int32 (global experts)
+    is_token_in_rank: torch.Tensor          # [T, R] bool
+
+
+def rank_layout(topk_ids: torch.Tensor, num_experts: int, num_ranks: int,
+                ranks_per_node: int = 1) -> RankLayout:
+    """Per-rank / per-node token counts, per-expert slot counts and the
+    token-in-rank table of global top-k ids (ids outside [0, E) are
+    unrouted)."""
+    _need_gpu(topk_ids, "topk_ids")
+    if topk_ids.dim() != 2:
+        raise ValueError("topk_ids must be [T, k]")
+    ids = topk_ids.to(torch.int32).contiguous()
+    T, k = ids.shape
+    E, R, rpn = int(num_experts), int(num_ranks), int(ranks_per_node)
+    wsb = library().cdl_rank_layout_workspace_size(T, k, E, R, rpn)
+    if wsb == 0:
+        raise CdlError(-3, "cdl_rank_layout_workspace_size (sizes)")
+    dev = ids.device
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    out = RankLayout(torch.empty(R, dtype=torch.int32, device=dev),
+                     torch.empty(R // rpn, dtype=torch.int32, device=dev),
+                     torch.empty(E, dtype=torch.int32, device=dev),
+                     torch.empty(T, R, dtype=torch.bool, device=dev))
+    rc = library().cdl_rank_layout(_ptr(ids), T, k, E, R, rpn, _ptr(out.num_tokens_per_rank),
+                                   _ptr(out.num_tokens_per_rdma_rank),
+                                   _ptr(out.num_tokens_per_expert), _ptr(out.is_token_in_rank),
+                                   _ptr(ws), wsb, _stream(dev))
+    _check(rc, "cdl_rank_layout")
+    return out
 
 
 def dispatch(x: torch.Tensor, layout: Layout, out: Optional[torch.Tensor] = None,

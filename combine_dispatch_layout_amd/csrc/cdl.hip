@@ -634,6 +634,71 @@ __global__ __launch_bounds__(128) void scatter_rows_u16(
 }
 
 // ---------------------------------------------------------------------------
+// rank layout (before the exchange)
+// ---------------------------------------------------------------------------
+
+constexpr int kRankThreads = 256;        // tokens per workgroup, one per thread
+
+// Per-workgroup partial counts: partial[blk][0, E) slots per expert,
+// [E, E+R) tokens per rank, [E+R, E+R+N) tokens per node; each token also
+// writes its is_token_in_rank row.  A rank (node) counts a token once: only
+// the first of the token's valid slots on that rank (node) adds to it.
+__global__ __launch_bounds__(kRankThreads) void rank_layout_kernel(
+    const int32_t *__restrict__ ids, int64_t T, int32_t k, int32_t E, int32_t R, int32_t rpn,
+    uint8_t *__restrict__ in_rank, int32_t *__restrict__ partial)
+{
+    extern __shared__ int32_t h[];
+    const int N = R / rpn;
+    const int W = E + R + N;
+    for (int i = threadIdx.x; i < W; i += kRankThreads) h[i] = 0;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * kRankThreads + threadIdx.x;
+    if (t < T) {
+        const int32_t epr = E / R;
+        const int32_t *my = ids + t * k;
+        uint8_t *row = in_rank + t * R;
+        for (int r = 0; r < R; ++r) row[r] = 0;
+        for (int j = 0; j < k; ++j) {
+            const int32_t id = my[j];
+            if (id < 0 || id >= E) continue;
+            atomicAdd(&h[id], 1);
+            const int32_t r = id / epr;
+            const int32_t n = r / rpn;
+            bool first_r = true, first_n = true;
+            for (int j2 = 0; j2 < j; ++j2) {
+                const int32_t id2 = my[j2];
+                if (id2 < 0 || id2 >= E) continue;
+                const int32_t r2 = id2 / epr;
+                first_r &= r2 != r;
+                first_n &= r2 / rpn != n;
+            }
+            if (first_r) {
+                row[r] = 1;
+                atomicAdd(&h[E + r], 1);
+            }
+            if (first_n) atomicAdd(&h[E + R + n], 1);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < W; i += kRankThreads) partial[(int64_t)blockIdx.x * W + i] = h[i];
+}
+
+// Column sums of the partial counts into the three outputs.
+__global__ __launch_bounds__(256) void rank_layout_reduce_kernel(
+    const int32_t *__restrict__ partial, int64_t nblocks, int32_t E, int32_t R, int32_t N,
+    int32_t *__restrict__ per_expert, int32_t *__restrict__ per_rank, int32_t *__restrict__ per_node)
+{
+    const int W = E + R + N;
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= W) return;
+    int32_t sum = 0;
+    for (int64_t b = 0; b < nblocks; ++b) sum += partial[b * W + i];
+    if (i < E) per_expert[i] = sum;
+    else if (i < E + R) per_rank[i - E] = sum;
+    else if (per_node) per_node[i - E - R] = sum;
+}
+
+// ---------------------------------------------------------------------------
 // low-latency dispatch
 // ---------------------------------------------------------------------------
 
@@ -969,6 +1034,51 @@ int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
     a.out_s = out_scales;
     a.cap_rows = cap_rows;
     return run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
+}
+
+static int check_rank_layout_sizes(int64_t T, int32_t k, int32_t E, int32_t R, int32_t rpn)
+{
+    int rc = check_tk(T, k);
+    if (rc != CDL_OK) return rc;
+    if (E < 1 || E > CDL_MAX_EXPERTS || R < 1 || R > CDL_MAX_RANKS || rpn < 1) return CDL_ERR_BAD_SIZE;
+    if (E % R != 0 || R % rpn != 0) return CDL_ERR_UNSUPPORTED;
+    if (T * R > (int64_t)INT32_MAX) return CDL_ERR_TOO_LARGE;
+    return CDL_OK;
+}
+
+size_t cdl_rank_layout_workspace_size(int64_t T, int32_t k, int32_t E, int32_t num_ranks,
+                                      int32_t ranks_per_node)
+{
+    if (check_rank_layout_sizes(T, k, E, num_ranks, ranks_per_node) != CDL_OK) return 0;
+    const int64_t nblocks = (T + kRankThreads - 1) / kRankThreads;
+    const int64_t W = (int64_t)E + num_ranks + num_ranks / ranks_per_node;
+    return (size_t)(nblocks * W * 4 + 256);
+}
+
+int cdl_rank_layout(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E, int32_t num_ranks,
+                    int32_t ranks_per_node, int32_t *num_tokens_per_rank,
+                    int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
+                    uint8_t *is_token_in_rank, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_rank_layout_sizes(T, k, E, num_ranks, ranks_per_node);
+    if (rc != CDL_OK) return rc;
+    if (!num_tokens_per_rank || !num_tokens_per_expert || !ws) return CDL_ERR_NULL_POINTER;
+    if (T > 0 && (!topk_ids || !is_token_in_rank)) return CDL_ERR_NULL_POINTER;
+    if (ws_bytes < cdl_rank_layout_workspace_size(T, k, E, num_ranks, ranks_per_node))
+        return CDL_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t nblocks = (T + kRankThreads - 1) / kRankThreads;
+    const int32_t N = num_ranks / ranks_per_node;
+    const int32_t W = E + num_ranks + N;
+    if (nblocks > 0) {
+        rank_layout_kernel<<<dim3((unsigned)nblocks), dim3(kRankThreads), (size_t)W * 4, s>>>(
+            topk_ids, T, k, E, num_ranks, ranks_per_node, is_token_in_rank, (int32_t *)ws);
+        if ((rc = launch_status()) != CDL_OK) return rc;
+    }
+    rank_layout_reduce_kernel<<<dim3((unsigned)((W + 255) / 256)), dim3(256), 0, s>>>(
+        (const int32_t *)ws, nblocks, E, num_ranks, N, num_tokens_per_expert, num_tokens_per_rank,
+        num_tokens_per_rdma_rank);
+    return launch_status();
 }
 
 int cdl_dispatch(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *src2dst,

@@ -73,6 +73,8 @@ extern "C" {
 #define CDL_MAX_LOCAL_EXPERTS 2048
 #define CDL_FP8_GROUP 128
 #define CDL_MAX_ALIGNMENT 1024
+#define CDL_MAX_EXPERTS 8192        /* global experts for cdl_rank_layout */
+#define CDL_MAX_RANKS 1024
 
 /*
  * cdl_dispatch_layout_workspace_size -- bytes of device workspace that
@@ -175,6 +177,41 @@ int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
                     int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
                     int64_t reorder_cap, uint8_t *out_q, float *out_scales, int64_t cap_rows,
                     int32_t *status, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * cdl_rank_layout_workspace_size -- device workspace bytes for
+ * cdl_rank_layout (0 for rejected sizes).
+ */
+size_t cdl_rank_layout_workspace_size(int64_t T, int32_t k, int32_t E, int32_t num_ranks,
+                                      int32_t ranks_per_node);
+
+/*
+ * cdl_rank_layout -- where a token batch goes before the exchange
+ * ([deepep.py], _DeepEPDispatcherImplNormal._dispatch_core:
+ * get_dispatch_layout returns num_tokens_per_rank, num_tokens_per_rdma_rank,
+ * num_tokens_per_expert and is_token_in_rank).
+ *
+ *   topk_ids                  in  [T, k] int32 global ids; an id outside [0, E)
+ *                                 is an unrouted slot
+ *   E, num_ranks              E % num_ranks == 0; rank r owns experts
+ *                             [r*E/num_ranks, (r+1)*E/num_ranks)
+ *   ranks_per_node            num_ranks % ranks_per_node == 0 (node = RDMA rank)
+ *   num_tokens_per_rank       out [num_ranks] int32: tokens with >= 1 slot on r
+ *   num_tokens_per_rdma_rank  out [num_ranks/ranks_per_node] int32: tokens with
+ *                             >= 1 slot on the node's ranks (may be NULL)
+ *   num_tokens_per_expert     out [E] int32: slots per expert
+ *   is_token_in_rank          out [T, num_ranks] bytes, 1 if token t has a slot
+ *                             on rank r, else 0 (torch.bool compatible)
+ *   ws, ws_bytes              cdl_rank_layout_workspace_size bytes, no
+ *                             initialisation needed
+ * CDL_ERR_UNSUPPORTED for indivisible sizes; E <= CDL_MAX_EXPERTS and
+ * num_ranks <= CDL_MAX_RANKS.  Two kernel launches, no atomics outside
+ * workgroups (the counts are deterministic).
+ */
+int cdl_rank_layout(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E, int32_t num_ranks,
+                    int32_t ranks_per_node, int32_t *num_tokens_per_rank,
+                    int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
+                    uint8_t *is_token_in_rank, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * cdl_dispatch -- normal-mode bf16 row scatter ([0.4.4 diff],

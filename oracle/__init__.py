@@ -69,6 +69,9 @@ def lib():
         L.oracle_layout_aligned.argtypes = [_i32p, _i64, _i32, _i32, _i32, _i32, _i32p,
                                             _i64p, _i32p, _i32p]
         L.oracle_layout_aligned.restype = _i64
+        L.oracle_rank_layout.argtypes = [_i32p, _i64, _i32, _i32, _i32, _i32, _i32p, _i32p,
+                                         _i32p, _u8p]
+        L.oracle_rank_layout.restype = _i32
         L.oracle_dispatch.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _u16p]
         L.oracle_dispatch.restype = None
         L.oracle_dispatch_ll.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _i32,
@@ -187,6 +190,24 @@ def layout_aligned(topk_ids: np.ndarray, expert_begin: int, L: int, alignment: i
     if R < 0:
         raise ValueError("oracle_layout_aligned failed")
     return counts, seg, src2dst, reorder[:R].copy()
+
+
+def rank_layout(topk_ids: np.ndarray, E: int, num_ranks: int, ranks_per_node: int = 1):
+    """(num_tokens_per_rank [R], num_tokens_per_rdma_rank [R/rpn],
+    num_tokens_per_expert [E], is_token_in_rank [T, R] bool)."""
+    ids = _c(topk_ids, np.int32)
+    T, k = ids.shape
+    R = num_ranks
+    per_rank = np.zeros(R, np.int32)
+    per_node = np.zeros(max(R // max(ranks_per_node, 1), 1), np.int32)
+    per_expert = np.zeros(max(E, 1), np.int32)
+    in_rank = np.zeros(max(T * R, 1), np.uint8)
+    rc = lib().oracle_rank_layout(ids.reshape(-1), T, k, E, R, ranks_per_node, per_rank,
+                                  per_node, per_expert, in_rank)
+    if rc != 0:
+        raise ValueError("bad rank-layout sizes")
+    return (per_rank, per_node[:R // ranks_per_node], per_expert[:E],
+            in_rank[:T * R].reshape(T, R).astype(bool))
 
 
 def dispatch(x_bits: np.ndarray, src2dst: np.ndarray, k: int, rows: int,

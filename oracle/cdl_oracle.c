@@ -260,6 +260,54 @@ int64_t oracle_layout_aligned(const int32_t *topk_ids, int64_t T, int32_t k,
     return seg_indptr[L];
 }
 
+/* Rank layout of a token batch before the exchange ([deepep.py],
+ * _DeepEPDispatcherImplNormal._dispatch_core: get_dispatch_layout(topk_ids,
+ * num_experts) returns num_tokens_per_rank, num_tokens_per_rdma_rank,
+ * num_tokens_per_expert and is_token_in_rank).  Ids are global; an id outside
+ * [0, E) marks an unrouted slot.  Rank r owns experts [r*E/R, (r+1)*E/R);
+ * node n owns ranks [n*rpn, (n+1)*rpn).
+ *   per_expert[e]   = number of slots with id e
+ *   in_rank[t*R+r]  = 1 if token t has a slot on rank r, else 0
+ *   per_rank[r]     = number of tokens with in_rank[t][r] = 1
+ *   per_node[n]     = number of tokens with a slot on any rank of node n
+ * Returns -1 if E is not a multiple of R or R of rpn. */
+int32_t oracle_rank_layout(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E,
+                           int32_t R, int32_t rpn, int32_t *per_rank, int32_t *per_node,
+                           int32_t *per_expert, uint8_t *in_rank)
+{
+    if (E <= 0 || R <= 0 || rpn <= 0 || E % R != 0 || R % rpn != 0)
+        return -1;
+    int32_t epr = E / R;
+    int32_t N = R / rpn;
+    for (int32_t r = 0; r < R; ++r)
+        per_rank[r] = 0;
+    for (int32_t n = 0; n < N; ++n)
+        per_node[n] = 0;
+    for (int32_t e = 0; e < E; ++e)
+        per_expert[e] = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        uint8_t *row = in_rank + t * R;
+        for (int32_t r = 0; r < R; ++r)
+            row[r] = 0;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t id = topk_ids[t * k + j];
+            if (id < 0 || id >= E)
+                continue;
+            per_expert[id] += 1;
+            row[id / epr] = 1;
+        }
+        for (int32_t r = 0; r < R; ++r)
+            per_rank[r] += row[r];
+        for (int32_t n = 0; n < N; ++n) {
+            int any = 0;
+            for (int32_t r = n * rpn; r < (n + 1) * rpn; ++r)
+                any |= row[r];
+            per_node[n] += any;
+        }
+    }
+    return 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Dispatch.                                                                 */
 /* ------------------------------------------------------------------------ */

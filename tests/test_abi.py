@@ -220,3 +220,19 @@ def test_permute_fp8_rejects():
     assert call(s=NULL) == ENULL
     assert call(q=ctypes.c_void_p(0x1004)) == EUNSUP
     assert call(counts=NULL) == ENULL
+
+
+def test_rank_layout_rejects():
+    lib = cdl.library()
+    assert lib.cdl_rank_layout_workspace_size(16, 2, 256, 8, 4) > 0
+    assert lib.cdl_rank_layout_workspace_size(16, 2, 250, 8, 4) == 0        # E % R
+    assert lib.cdl_rank_layout_workspace_size(16, 2, 256, 8, 3) == 0        # R % rpn
+    assert lib.cdl_rank_layout_workspace_size(16, 2, 9000, 8, 1) == 0       # E too large
+    f = lib.cdl_rank_layout
+    # ids, T, k, E, R, rpn, per_rank, per_node, per_expert, in_rank, ws, wsb, stream
+    assert f(FAKE, 16, 2, 250, 8, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, NULL) == EUNSUP
+    assert f(FAKE, 16, 2, 256, 0, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, NULL) == ESIZE
+    assert f(FAKE, 16, 2, 256, 8, 1, NULL, FAKE, FAKE, FAKE, FAKE, 1 << 20, NULL) == ENULL
+    assert f(FAKE, 16, 2, 256, 8, 1, FAKE, FAKE, NULL, FAKE, FAKE, 1 << 20, NULL) == ENULL
+    assert f(FAKE, 16, 2, 256, 8, 1, FAKE, FAKE, FAKE, NULL, FAKE, 1 << 20, NULL) == ENULL
+    assert f(FAKE, 16, 2, 256, 8, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 8, NULL) == EWS

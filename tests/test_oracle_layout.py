@@ -228,3 +228,59 @@ def test_layout_aligned_invariants(name):
     assert np.array_equal(d[valid] - s[e], d0[valid] - s0[e])
     assert np.all(d[~valid] == -1)
     assert r.size == s[-1] and np.sum(r == -1) == s[-1] - c.sum()
+
+
+# --------------------------------------------------------------------------
+# rank layout (before the exchange)
+# --------------------------------------------------------------------------
+
+def brute_rank_layout(ids, E, R, rpn):
+    epr = E // R
+    T = ids.shape[0]
+    per_expert = [0] * E
+    in_rank = [[False] * R for _ in range(T)]
+    for t in range(T):
+        for v in ids[t]:
+            v = int(v)
+            if 0 <= v < E:
+                per_expert[v] += 1
+                in_rank[t][v // epr] = True
+    per_rank = [sum(in_rank[t][r] for t in range(T)) for r in range(R)]
+    per_node = [sum(any(in_rank[t][n * rpn:(n + 1) * rpn]) for t in range(T)) for n in range(R // rpn)]
+    return per_rank, per_node, per_expert, in_rank
+
+
+def test_rank_layout_bruteforce():
+    rng = np.random.default_rng(21)
+    for _ in range(200):
+        R = int(rng.choice([1, 2, 4, 8]))
+        rpn = int(rng.choice([d for d in (1, 2, 4, 8) if R % d == 0]))
+        E = R * int(rng.integers(1, 5))
+        T = int(rng.integers(0, 12))
+        k = int(rng.integers(1, 5))
+        ids = rng.integers(-1, E + 2, size=(T, k)).astype(np.int32)
+        got = oracle.rank_layout(ids, E, R, rpn)
+        want = brute_rank_layout(ids, E, R, rpn)
+        assert got[0].tolist() == want[0] and got[1].tolist() == want[1]
+        assert got[2].tolist() == want[2] and got[3].tolist() == want[3]
+
+
+@pytest.mark.parametrize("name", ["dsv3_prefill", "ll_decode", "zipf_prefill"])
+def test_rank_layout_against_library_and_local_layouts(name):
+    w = W.WORKLOADS[name]
+    ids = W.make_topk_ids(w).numpy()
+    R = 8 if w.E % 8 == 0 else 1
+    per_rank, per_node, per_expert, in_rank = oracle.rank_layout(ids, w.E, R, 4 if R % 4 == 0 else 1)
+    flat = ids.reshape(-1)
+    assert np.array_equal(per_expert, np.bincount(flat[(flat >= 0) & (flat < w.E)], minlength=w.E))
+    lib_in = np.zeros((w.T, R), bool)
+    tok = np.repeat(np.arange(w.T), w.k)
+    ok = (flat >= 0) & (flat < w.E)
+    lib_in[tok[ok], flat[ok] // (w.E // R)] = True
+    assert np.array_equal(in_rank, lib_in)
+    assert np.array_equal(per_rank, lib_in.sum(0))
+    # the tokens a rank receives are those with a valid slot in its local layout
+    epr = w.E // R
+    for r in range(R):
+        _, _, d, _ = oracle.layout(ids, r * epr, epr)
+        assert per_rank[r] == int((d.reshape(w.T, w.k) >= 0).any(1).sum())

@@ -595,3 +595,45 @@ def test_layout_aligned_reorder_capacity_flag():
     assert np.array_equal(npy(s2d), d) and np.array_equal(npy(seg), s)
     got = npy(reorder)
     assert np.array_equal(got[:cap], r[:cap]) and np.all(got[cap:] == 12345)
+
+
+# --------------------------------------------------------------------------
+# rank layout
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,R,rpn", [("dsv3_prefill", 8, 8), ("dsv3_prefill", 32, 8),
+                                        ("ll_decode", 8, 1), ("zipf_prefill", 16, 4),
+                                        ("tiny", 1, 1)])
+def test_rank_layout_parity(name, R, rpn):
+    w = W.WORKLOADS[name]
+    announce("rank layout %s R=%d rpn=%d" % (name, R, rpn))
+    ids = W.make_topk_ids(w).clone()
+    ids[::5, 0] = -1                                  # unrouted slots
+    ids[1::7, -1] = w.E                               # FlashInfer-style invalid id
+    rl = cdl.rank_layout(ids.to(DEV), w.E, R, rpn)
+    torch.cuda.synchronize()
+    pr, pn, pe, ir = oracle.rank_layout(ids.numpy(), w.E, R, rpn)
+    assert np.array_equal(npy(rl.num_tokens_per_rank), pr)
+    assert np.array_equal(npy(rl.num_tokens_per_rdma_rank), pn)
+    assert np.array_equal(npy(rl.num_tokens_per_expert), pe)
+    assert np.array_equal(npy(rl.is_token_in_rank), ir)
+
+
+def test_rank_layout_edge_cases():
+    announce("rank layout edges")
+    rl = cdl.rank_layout(torch.zeros(0, 8, dtype=torch.int32, device=DEV), 64, 8, 2)
+    torch.cuda.synchronize()
+    assert npy(rl.num_tokens_per_rank).tolist() == [0] * 8
+    assert npy(rl.num_tokens_per_expert).tolist() == [0] * 64
+    g = torch.Generator().manual_seed(9)
+    T, k, E, R = 1000, 64, 128, 64                    # k = 64, duplicate ranks per token
+    ids = torch.randint(-2, E + 3, (T, k), generator=g, dtype=torch.int32)
+    rl = cdl.rank_layout(ids.to(DEV), E, R, 8)
+    torch.cuda.synchronize()
+    pr, pn, pe, ir = oracle.rank_layout(ids.numpy(), E, R, 8)
+    assert np.array_equal(npy(rl.num_tokens_per_rank), pr)
+    assert np.array_equal(npy(rl.num_tokens_per_rdma_rank), pn)
+    assert np.array_equal(npy(rl.num_tokens_per_expert), pe)
+    assert np.array_equal(npy(rl.is_token_in_rank), ir)
+    with pytest.raises(cdl.CdlError):
+        cdl.rank_layout(ids.to(DEV), 100, 8, 1)
