@@ -72,6 +72,16 @@ def lib():
         L.oracle_rank_layout.argtypes = [_i32p, _i64, _i32, _i32, _i32, _i32, _i32p, _i32p,
                                          _i32p, _u8p]
         L.oracle_rank_layout.restype = _i32
+        L.oracle_quant_group_fp8_ue8m0.argtypes = [_u16p, _i64, _u8p,
+                                                   ctypes.POINTER(ctypes.c_float),
+                                                   ctypes.POINTER(ctypes.c_int32)]
+        L.oracle_quant_group_fp8_ue8m0.restype = None
+        L.oracle_dispatch_fp8_fmt.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _i64, _i32, _i64,
+                                              _u8p, _u8p]
+        L.oracle_dispatch_fp8_fmt.restype = _i32
+        L.oracle_dispatch_ll_fp8.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _i32, _i32, _i64,
+                                             _i64, _i32, _u8p, _u8p, _i32p, _i32p]
+        L.oracle_dispatch_ll_fp8.restype = _i32
         L.oracle_dispatch.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _u16p]
         L.oracle_dispatch.restype = None
         L.oracle_dispatch_ll.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _i32,
@@ -262,6 +272,62 @@ def dispatch_fp8(x_bits: np.ndarray, src2dst: np.ndarray, k: int, rows: int,
     if rc != 0:
         raise RuntimeError("oracle_dispatch_fp8 failed: %d" % rc)
     return Q, S
+
+
+SCALE_UE8M0, SCALE_COLMAJOR, SCALE_PACKED = 1, 2, 4
+
+
+def scale_buffer_bytes(rows: int, G: int, flags: int, rows_per_mat: int) -> int:
+    """Size in bytes of a scale buffer for `rows` destination rows."""
+    words = (G + 3) // 4 if flags & SCALE_PACKED else G
+    if flags & SCALE_COLMAJOR:
+        nmat = -(-rows // rows_per_mat) if rows else 0
+        ld = -(-rows_per_mat // 4) * 4
+        return nmat * words * ld * 4
+    return rows * words * 4
+
+
+def quant_group_fp8_ue8m0(x_bits: np.ndarray):
+    x = _c(x_bits, np.uint16).reshape(-1)
+    q = np.zeros(x.size, np.uint8)
+    p = ctypes.c_float(0.0)
+    e = ctypes.c_int32(0)
+    lib().oracle_quant_group_fp8_ue8m0(x, x.size, q, ctypes.byref(p), ctypes.byref(e))
+    return q, p.value, e.value
+
+
+def dispatch_fp8_fmt(x_bits: np.ndarray, src2dst: np.ndarray, k: int, rows: int, flags: int,
+                     rows_per_mat: int = 0, group: int = 128, fill: int = 0):
+    """fp8 dispatch with a scale format; returns (Q [rows, H] u8, S raw bytes
+    of scale_buffer_bytes(...), filled with `fill` where not written)."""
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    rpm = rows_per_mat or max(rows, 1)
+    Q = np.zeros((rows, H), np.uint8)
+    S = np.full(max(scale_buffer_bytes(rows, H // group, flags, rpm), 1), fill, np.uint8)
+    rc = lib().oracle_dispatch_fp8_fmt(x.reshape(-1), T, H, k, _c(src2dst, np.int32), group,
+                                       flags, rpm, Q.reshape(-1), S)
+    if rc != 0:
+        raise ValueError("oracle_dispatch_fp8_fmt failed: %d" % rc)
+    return Q, S
+
+
+def dispatch_ll_fp8(x_bits: np.ndarray, topk_ids: np.ndarray, expert_begin: int, L: int,
+                    cap: int, flags: int, group: int = 128, fill: int = 0):
+    """Returns (Q [L, cap, H] u8, S bytes, masked_m, ll_src2dst, overflow)."""
+    x = _c(x_bits, np.uint16)
+    ids = _c(topk_ids, np.int32)
+    T, H = x.shape
+    k = ids.shape[1]
+    Q = np.zeros((L, cap, H), np.uint8)
+    S = np.full(max(scale_buffer_bytes(L * cap, H // group, flags, cap), 1), fill, np.uint8)
+    mm = np.zeros(L, np.int32)
+    ll = np.zeros(T * k, np.int32)
+    ovf = lib().oracle_dispatch_ll_fp8(x.reshape(-1), T, H, k, ids.reshape(-1), expert_begin, L,
+                                       cap, group, flags, Q.reshape(-1), S, mm, ll)
+    if ovf < 0:
+        raise ValueError("oracle_dispatch_ll_fp8 failed")
+    return Q, S, mm, ll, int(ovf)
 
 
 def combine(y_bits: np.ndarray, map_: np.ndarray, weights: np.ndarray,

@@ -438,6 +438,160 @@ int32_t oracle_dispatch_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
     return 0;
 }
 
+/* fp8 scale variants ([deepep.py], _DeepEPDispatcherImplNormal.dispatch_a:
+ * the group quant takes column_major_scales, scale_tma_aligned and
+ * scale_ue8m0 switches for DeepGEMM; _DeepEPDispatcherImplLowLatency.
+ * _dispatch_core: round_scale / use_ue8m0 make DeepEP return int32-packed
+ * UE8M0 scales).  Readings, as flags:
+ *   UE8M0 (1):    the scale is the smallest power of two p >= 2^-127 with
+ *                 448 * p >= amax, so x / p is exact and needs no clamp;
+ *                 an all-zero group gets p = 2^-127
+ *   COLMAJOR (2): the scales of each matrix of rows_per_mat rows are stored
+ *                 group-major, [G][ld] with ld = rows_per_mat rounded up to
+ *                 a multiple of 4 (16-byte aligned columns, as a TMA load
+ *                 wants)
+ *   PACKED (4):   (with UE8M0) the scale is stored as its exponent byte
+ *                 log2(p) + 127, four consecutive groups per 32-bit word,
+ *                 group g in byte g % 4 (little endian)
+ * Without COLMAJOR the scales are row-major per destination row. */
+enum { ORACLE_SCALE_UE8M0 = 1, ORACLE_SCALE_COLMAJOR = 2, ORACLE_SCALE_PACKED = 4 };
+
+/* UE8M0 quantisation of one group: *p receives the power-of-two scale and
+ * *p_exp its exponent. */
+void oracle_quant_group_fp8_ue8m0(const uint16_t *x, int64_t n, uint8_t *q, float *p,
+                                  int32_t *p_exp)
+{
+    double a = 0.0;
+    for (int64_t c = 0; c < n; ++c) {
+        double v = fabs((double)oracle_bf16_to_f32(x[c]));
+        if (v > a)
+            a = v;
+    }
+    int e = -127;
+    while (ldexp(448.0, e) < a)
+        ++e;
+    float pf = (float)ldexp(1.0, e);
+    for (int64_t c = 0; c < n; ++c)
+        q[c] = oracle_e4m3fn_rne(oracle_bf16_to_f32(x[c]) / pf);
+    *p = pf;
+    *p_exp = e;
+}
+
+/* Byte offset of the scale of (destination row, group g) in a scale buffer
+ * of the given flags; G groups per row. */
+static int64_t scale_offset(int32_t flags, int64_t row, int64_t g, int64_t G,
+                            int64_t rows_per_mat)
+{
+    int packed = (flags & ORACLE_SCALE_PACKED) != 0;
+    int64_t words = packed ? (G + 3) / 4 : G;          /* 32-bit words per row */
+    if (flags & ORACLE_SCALE_COLMAJOR) {
+        int64_t ld = (rows_per_mat + 3) / 4 * 4;
+        int64_t mat = row / rows_per_mat, r = row % rows_per_mat;
+        int64_t word = mat * words * ld + (packed ? g / 4 : g) * ld + r;
+        return word * 4 + (packed ? g % 4 : 0);
+    }
+    return (row * words + (packed ? g / 4 : g)) * 4 + (packed ? g % 4 : 0);
+}
+
+/* Writes the scale of one group in the requested format. */
+static void put_scale(uint8_t *S, int32_t flags, int64_t row, int64_t g, int64_t G,
+                      int64_t rows_per_mat, float p, int32_t p_exp)
+{
+    int64_t off = scale_offset(flags, row, g, G, rows_per_mat);
+    if (flags & ORACLE_SCALE_PACKED)
+        S[off] = (uint8_t)(p_exp + 127);
+    else
+        memcpy(S + off, &p, sizeof p);
+}
+
+/* fp8 normal dispatch with a scale format: as oracle_dispatch_fp8 (group =
+ * 128 for the kernels), scales written at scale_offset() of S (bytes).
+ * rows_per_mat only matters for COLMAJOR.  Returns -1 for bad arguments. */
+int32_t oracle_dispatch_fp8_fmt(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                                const int32_t *src2dst, int64_t group, int32_t flags,
+                                int64_t rows_per_mat, uint8_t *Q, uint8_t *S)
+{
+    if (group <= 0 || H % group != 0 || rows_per_mat <= 0)
+        return -1;
+    if ((flags & ORACLE_SCALE_PACKED) && !(flags & ORACLE_SCALE_UE8M0))
+        return -1;
+    int64_t G = H / group;
+    uint8_t *qrow = (uint8_t *)malloc((size_t)(H > 0 ? H : 1));
+    float *prow = (float *)malloc(sizeof(float) * (size_t)(G > 0 ? G : 1));
+    int32_t *erow = (int32_t *)malloc(sizeof(int32_t) * (size_t)(G > 0 ? G : 1));
+    if (!qrow || !prow || !erow) {
+        free(qrow);
+        free(prow);
+        free(erow);
+        return -2;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        int any = 0;
+        for (int32_t j = 0; j < k; ++j)
+            any |= src2dst[t * k + j] >= 0;
+        if (!any)
+            continue;
+        for (int64_t g = 0; g < G; ++g) {
+            if (flags & ORACLE_SCALE_UE8M0) {
+                oracle_quant_group_fp8_ue8m0(x + t * H + g * group, group, qrow + g * group,
+                                             prow + g, erow + g);
+            } else {
+                oracle_quant_group_fp8(x + t * H + g * group, group, qrow + g * group, prow + g);
+                erow[g] = 0;
+            }
+        }
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t d = src2dst[t * k + j];
+            if (d < 0)
+                continue;
+            memcpy(Q + (int64_t)d * H, qrow, (size_t)H);
+            for (int64_t g = 0; g < G; ++g)
+                put_scale(S, flags, d, g, G, rows_per_mat, prow[g], erow[g]);
+        }
+    }
+    free(qrow);
+    free(prow);
+    free(erow);
+    return 0;
+}
+
+/* Low-latency dispatch with fp8 rows: oracle_dispatch_ll's slots with the
+ * rows quantised as oracle_dispatch_fp8_fmt (each expert's cap rows form one
+ * scale matrix for COLMAJOR).  Returns the overflow flag, or -1. */
+int32_t oracle_dispatch_ll_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                               const int32_t *topk_ids, int32_t expert_begin, int32_t L,
+                               int64_t cap, int64_t group, int32_t flags, uint8_t *Q,
+                               uint8_t *S, int32_t *masked_m, int32_t *ll_src2dst)
+{
+    if (group <= 0 || H % group != 0 || cap <= 0)
+        return -1;
+    int32_t overflow = 0;
+    int64_t *seen = (int64_t *)calloc((size_t)(L > 0 ? L : 1), sizeof(int64_t));
+    if (!seen)
+        return -1;
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t i = t * k + j;
+            int32_t e = local_expert(topk_ids[i], expert_begin, L);
+            if (e < 0) {
+                ll_src2dst[i] = -1;
+                continue;
+            }
+            int64_t slot = seen[e]++;
+            if (slot >= cap) {
+                ll_src2dst[i] = -1;
+                overflow = 1;
+                continue;
+            }
+            ll_src2dst[i] = (int32_t)((int64_t)e * cap + slot);
+        }
+    for (int32_t e = 0; e < L; ++e)
+        masked_m[e] = (int32_t)(seen[e] < cap ? seen[e] : cap);
+    free(seen);
+    int32_t rc = oracle_dispatch_fp8_fmt(x, T, H, k, ll_src2dst, group, flags, cap, Q, S);
+    return rc < 0 ? rc : overflow;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Combine.                                                                  */
 /* ------------------------------------------------------------------------ */
