@@ -254,7 +254,7 @@ def measure_fp8(torch, cdl, sets, steps):
                      P(sc.data_ptr()), s.R, P(s.status.data_ptr()), s.stream)
         a_perm = (P(s.x.data_ptr()), s.T, s.H, s.k, P(s.ids.data_ptr()), 0, s.L, 1,
                   P(s.counts.data_ptr()), P(s.seg.data_ptr()), P(s.src2dst.data_ptr()),
-                  P(s.reorder.data_ptr()), s.T * s.k, P(q.data_ptr()), P(sc.data_ptr()), s.R,
+                  P(s.reorder.data_ptr()), s.T * s.k, P(q.data_ptr()), P(sc.data_ptr()), 0, s.R,
                   P(s.status.data_ptr()), P(s.ws.data_ptr()), s.ws.numel(), s.stream)
         bufs.append((s, a_scatter, a_perm, q, sc))
 

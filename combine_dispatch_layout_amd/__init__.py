@@ -10,6 +10,9 @@ from .api import (  # noqa: F401
     CDL_STATUS_REORDER_OVERFLOW,
     CDL_STATUS_ROWS_OVERFLOW,
     FP8_GROUP,
+    FP8_SCALE_COLMAJOR,
+    FP8_SCALE_PACKED,
+    FP8_SCALE_UE8M0,
     LIB_PATH,
     CdlError,
     Layout,
@@ -18,6 +21,9 @@ from .api import (  # noqa: F401
     dispatch_fp8,
     dispatch_layout,
     dispatch_ll,
+    dispatch_ll_fp8,
+    fp8_scale_bytes,
+    new_scale_tensor,
     layout_workspace_size,
     library,
     ll_expected_m,

@@ -36,6 +36,9 @@ CDL_STATUS_LL_OVERFLOW = 2
 CDL_STATUS_MAP_RANGE = 4
 CDL_STATUS_REORDER_OVERFLOW = 8
 FP8_GROUP = 128
+FP8_SCALE_UE8M0 = 1
+FP8_SCALE_COLMAJOR = 2
+FP8_SCALE_PACKED = 4
 
 _lib = None
 
@@ -69,7 +72,14 @@ def library():
                                   i64, vp, vp, sz, vp]
         L.cdl_permute.restype = ctypes.c_int
         L.cdl_permute_fp8.argtypes = [vp, i64, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, i64,
-                                      vp, vp, i64, vp, vp, sz, vp]
+                                      vp, vp, i32, i64, vp, vp, sz, vp]
+        L.cdl_fp8_scale_bytes.argtypes = [i64, i64, i32, i64]
+        L.cdl_fp8_scale_bytes.restype = sz
+        L.cdl_dispatch_fp8_ex.argtypes = [vp, i64, i64, i32, vp, vp, vp, i32, i64, vp, vp]
+        L.cdl_dispatch_fp8_ex.restype = ctypes.c_int
+        L.cdl_dispatch_ll_fp8.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, i64, vp, vp,
+                                          i32, vp, vp, vp, vp]
+        L.cdl_dispatch_ll_fp8.restype = ctypes.c_int
         L.cdl_permute_fp8.restype = ctypes.c_int
         L.cdl_rank_layout_workspace_size.argtypes = [i64, i32, i32, i32, i32]
         L.cdl_rank_layout_workspace_size.restype = sz
@@ -236,7 +246,7 @@ def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
                 num_local_experts: int, rows: Optional[int] = None,
                 out_q: Optional[torch.Tensor] = None, out_scales: Optional[torch.Tensor] = None,
                 status: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                alignment: int = 1):
+                alignment: int = 1, scale_flags: int = 0):
     """Layout + fp8 (e4m3fn, groups of 128) scatter in one call.  Returns
     (layout, q [rows, H] uint8, scales [rows, H/128] fp32)."""
     _need(x, "x", torch.bfloat16)
@@ -251,17 +261,16 @@ def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
     if out_q is None:
         out_q = torch.empty(n, H, dtype=torch.uint8, device=x.device)
     if out_scales is None:
-        out_scales = torch.empty(out_q.shape[0], H // FP8_GROUP, dtype=torch.float32,
-                                 device=x.device)
+        out_scales = new_scale_tensor(out_q.shape[0], H, scale_flags, x.device)
     _need(out_q, "out_q", torch.uint8)
-    _need(out_scales, "out_scales", torch.float32, (out_q.shape[0], H // FP8_GROUP))
+    _check_scale_buffer(out_scales, out_q.shape[0], H, scale_flags, out_q.shape[0])
     if status is not None:
         _need(status, "status", torch.int32)
     rc = library().cdl_permute_fp8(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
                                    lay.alignment, _ptr(lay.counts), _ptr(lay.seg_indptr),
                                    _ptr(lay.src2dst), _ptr(lay.reorder_buf),
                                    lay.reorder_buf.numel(), _ptr(out_q), _ptr(out_scales),
-                                   out_q.shape[0], _ptr(status), _ptr(ws),
+                                   int(scale_flags), out_q.shape[0], _ptr(status), _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(x.device))
     _check(rc, "cdl_permute_fp8")
     return lay, out_q, out_scales
@@ -304,6 +313,32 @@ def rank_layout(topk_ids: torch.Tensor, num_experts: int, num_ranks: int,
     return out
 
 
+def fp8_scale_bytes(rows: int, H: int, scale_flags: int = 0, rows_per_mat: int = 0) -> int:
+    n = library().cdl_fp8_scale_bytes(rows, H, scale_flags, rows_per_mat or max(rows, 1))
+    if n == 0 and rows > 0:
+        raise CdlError(-3, "cdl_fp8_scale_bytes (format)")
+    return int(n)
+
+
+def new_scale_tensor(rows: int, H: int, scale_flags: int, device, rows_per_mat: int = 0):
+    """A scale buffer of the right size, typed and shaped for its format:
+    fp32 [rows, G] (row-major), fp32 [mats, G, ld] (column-major), int32
+    [rows, ceil(G/4)] or [mats, ceil(G/4), ld] (packed exponent bytes)."""
+    G = H // FP8_GROUP
+    rpm = rows_per_mat or max(rows, 1)
+    packed = bool(scale_flags & FP8_SCALE_PACKED)
+    dtype = torch.int32 if packed else torch.float32
+    words = -(-G // 4) if packed else G
+    if scale_flags & FP8_SCALE_COLMAJOR:
+        mats = -(-rows // rpm) if rows else 0
+        ld = -(-rpm // 4) * 4
+        t = torch.empty(mats, words, ld, dtype=dtype, device=device)
+    else:
+        t = torch.empty(rows, words, dtype=dtype, device=device)
+    assert t.numel() * 4 == fp8_scale_bytes(rows, H, scale_flags, rpm)
+    return t
+
+
 def dispatch(x: torch.Tensor, layout: Layout, out: Optional[torch.Tensor] = None,
              rows: Optional[int] = None, status: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Normal-mode scatter: out[src2dst[t*k+j]] = x[t].  Allocates [R, H]
@@ -329,10 +364,12 @@ def dispatch(x: torch.Tensor, layout: Layout, out: Optional[torch.Tensor] = None
 
 def dispatch_fp8(x: torch.Tensor, layout: Layout, out_q: Optional[torch.Tensor] = None,
                  out_scales: Optional[torch.Tensor] = None, rows: Optional[int] = None,
-                 status: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                 status: Optional[torch.Tensor] = None,
+                 scale_flags: int = 0) -> Tuple[torch.Tensor, torch.Tensor]:
     """Normal-mode scatter with per-token groups of 128 quantised to
-    e4m3fn.  Returns (q [rows, H] uint8 holding e4m3fn bytes, scales
-    [rows, H/128] fp32); ``q.view(torch.float8_e4m3fn)`` reinterprets."""
+    e4m3fn.  Returns (q [rows, H] uint8 holding e4m3fn bytes, scales in the
+    `scale_flags` format -- fp32 [rows, H/128] by default);
+    ``q.view(torch.float8_e4m3fn)`` reinterprets."""
     T, k = layout.T, layout.k
     _need(x, "x", torch.bfloat16)
     if x.dim() != 2 or x.shape[0] != T:
@@ -344,17 +381,26 @@ def dispatch_fp8(x: torch.Tensor, layout: Layout, out_q: Optional[torch.Tensor] 
         n = layout.num_rows() if rows is None else int(rows)
         out_q = torch.empty(n, H, dtype=torch.uint8, device=x.device)
     if out_scales is None:
-        out_scales = torch.empty(out_q.shape[0], H // FP8_GROUP, dtype=torch.float32,
-                                 device=x.device)
+        out_scales = new_scale_tensor(out_q.shape[0], H, scale_flags, x.device)
     _need(out_q, "out_q", torch.uint8)
-    _need(out_scales, "out_scales", torch.float32, (out_q.shape[0], H // FP8_GROUP))
+    _check_scale_buffer(out_scales, out_q.shape[0], H, scale_flags, out_q.shape[0])
     if status is not None:
         _need(status, "status", torch.int32)
-    rc = library().cdl_dispatch_fp8(_ptr(x), T, H, k, _ptr(layout.src2dst), _ptr(out_q),
-                                    _ptr(out_scales), out_q.shape[0], _ptr(status),
-                                    _stream(x.device))
-    _check(rc, "cdl_dispatch_fp8")
+    rc = library().cdl_dispatch_fp8_ex(_ptr(x), T, H, k, _ptr(layout.src2dst), _ptr(out_q),
+                                       _ptr(out_scales), int(scale_flags), out_q.shape[0],
+                                       _ptr(status), _stream(x.device))
+    _check(rc, "cdl_dispatch_fp8_ex")
     return out_q, out_scales
+
+
+def _check_scale_buffer(t: torch.Tensor, rows: int, H: int, scale_flags: int, rpm: int) -> None:
+    _need_gpu(t, "out_scales")
+    if not t.is_contiguous():
+        raise ValueError("out_scales must be contiguous")
+    need = fp8_scale_bytes(rows, H, scale_flags, rpm)
+    if t.numel() * t.element_size() < need:
+        raise ValueError("out_scales holds %d bytes, the format needs %d"
+                         % (t.numel() * t.element_size(), need))
 
 
 def dispatch_ll(x: torch.Tensor, layout: Layout, cap: int, out: Optional[torch.Tensor] = None,
@@ -380,6 +426,42 @@ def dispatch_ll(x: torch.Tensor, layout: Layout, cap: int, out: Optional[torch.T
                                    _ptr(ll_map), _ptr(status), _stream(x.device))
     _check(rc, "cdl_dispatch_ll")
     return out, masked_m, ll_map
+
+
+def dispatch_ll_fp8(x: torch.Tensor, layout: Layout, cap: int, scale_flags: int = 0,
+                    out_q: Optional[torch.Tensor] = None,
+                    out_scales: Optional[torch.Tensor] = None,
+                    status: Optional[torch.Tensor] = None):
+    """Low-latency dispatch with fp8 rows.  Returns (q [L, cap, H] uint8,
+    scales (every expert's cap rows are one matrix of the format), masked_m,
+    ll_src2dst)."""
+    T, k, L = layout.T, layout.k, layout.num_local_experts
+    _need(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T = %d" % T)
+    H = x.shape[1]
+    if H % FP8_GROUP:
+        raise CdlError(-3, "dispatch_ll_fp8 (H must be a multiple of 128)")
+    if out_q is None:
+        out_q = torch.empty(L, cap, H, dtype=torch.uint8, device=x.device)
+    _need(out_q, "out_q", torch.uint8, (L, cap, H))
+    if out_scales is None:
+        out_scales = new_scale_tensor(L * cap, H, scale_flags, x.device, rows_per_mat=cap)
+        if not scale_flags & FP8_SCALE_COLMAJOR:
+            out_scales = out_scales.view(L, cap, -1)
+    _check_scale_buffer(out_scales, L * cap, H, scale_flags, cap)
+    masked_m = torch.empty(L, dtype=torch.int32, device=x.device)
+    ll_map = torch.empty(T * k, dtype=torch.int32, device=x.device)
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_dispatch_ll_fp8(_ptr(x), T, H, k, _ptr(layout.topk_ids),
+                                       layout.expert_begin, L, _ptr(layout.src2dst),
+                                       _ptr(layout.seg_indptr), _ptr(layout.counts), int(cap),
+                                       _ptr(out_q), _ptr(out_scales), int(scale_flags),
+                                       _ptr(masked_m), _ptr(ll_map), _ptr(status),
+                                       _stream(x.device))
+    _check(rc, "cdl_dispatch_ll_fp8")
+    return out_q, out_scales, masked_m, ll_map
 
 
 def combine(y: torch.Tensor, map_: torch.Tensor, topk_weights: torch.Tensor,

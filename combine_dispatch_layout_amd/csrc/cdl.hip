@@ -164,8 +164,14 @@ __device__ __forceinline__ float row16_max(float a)
 // correction step would return +0).
 constexpr float kFastQuotientMinAmax = 0x1p-96f;
 
-// Returns the 8 e4m3fn bytes of the chunk; *scale receives the group scale.
-__device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float *scale)
+// Returns the 8 e4m3fn bytes of the chunk; *scale receives the group scale
+// and *scale_exp its exponent (power-of-two scales only).
+//
+// Power-of-two (UE8M0) scales: p is the smallest power of two >= 2^-127 with
+// 448 * p >= amax.  With amax = m * 2^ex, m in [0.5, 1) (frexp), that is
+// 2^(ex - 9) when m <= 0.875 (448 = 0.875 * 2^9) and 2^(ex - 8) otherwise;
+// x / p is then an exact power-of-two scaling and needs no clamp.
+__device__ __forceinline__ u32x2 quant_chunk(u32x4 v, bool ue8m0, float *scale, int *scale_exp)
 {
     float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                   bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
@@ -173,6 +179,21 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float *scale)
 #pragma unroll
     for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
     a = row16_max(a);
+    if (ue8m0) {
+        int ex = 0;
+        const float m = frexpf(a, &ex);
+        int e = a > 0.0f ? ex - 9 + (m > 0.875f ? 1 : 0) : -127;
+        e = e < -127 ? -127 : e;
+        float q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = ldexpf(f[i], -e);
+        *scale = ldexpf(1.0f, e);
+        *scale_exp = e;
+        const uint32_t lo = pack2_e4m3(q[0], q[1]) | (pack2_e4m3(q[2], q[3]) << 16);
+        const uint32_t hi = pack2_e4m3(q[4], q[5]) | (pack2_e4m3(q[6], q[7]) << 16);
+        return u32x2{lo, hi};
+    }
+    *scale_exp = 0;
     const float s = a / 448.0f;                 // correctly rounded binary32 division
     float q[8];
     if (a >= kFastQuotientMinAmax) {
@@ -195,16 +216,37 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, float *scale)
     return u32x2{lo, hi};
 }
 
-// Quantises chunks [U0, U0 + NQ) of a lane's pass (chunk u of the pass is row
-// chunk c0 + u*64 + lane) and stores the e4m3fn bytes and the group scales to
-// every valid destination in dlist[0..k).  A row pass is quantised in parts so
-// that only NQ chunks of quantisation temporaries are live at a time while all
-// of the pass's loads were issued together.
-template <int U0, int NQ, int NCH>
-__device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], const int32_t *dlist, int k,
-                                               int lane, int64_t c0, int64_t chunks,
-                                               u32x2 *out_q, float *out_s, int64_t cap_rows,
-                                               int32_t *status);
+// Where fp8 rows and their scales go.  Scale layouts (CDL_FP8_SCALE_*):
+// row-major fp32 [rows][groups]; column-major: every rows_per_mat rows form a
+// matrix stored [groups][ld], ld = rows_per_mat rounded up to 4; packed: the
+// exponent byte log2(p) + 127, four groups per 32-bit word (group g in byte
+// g % 4), in either order.
+struct Fp8Out {
+    u32x2 *q;              // e4m3fn rows, 8 bytes per 16-byte input chunk
+    uint8_t *s;            // scale buffer
+    int32_t flags;
+    int64_t groups;        // scales per row (H / 128)
+    int64_t rows_per_mat;  // rows of one column-major matrix
+    int64_t ld;            // column stride of a column-major matrix
+};
+
+__device__ __forceinline__ void put_scale(const Fp8Out &o, int64_t row, int64_t g, float p, int e)
+{
+    const bool packed = (o.flags & CDL_FP8_SCALE_PACKED) != 0;
+    const int64_t words = packed ? (o.groups + 3) / 4 : o.groups;
+    const int64_t col = packed ? g / 4 : g;
+    int64_t word;
+    if (o.flags & CDL_FP8_SCALE_COLMAJOR) {
+        const int64_t mat = row / o.rows_per_mat;
+        word = mat * words * o.ld + col * o.ld + (row - mat * o.rows_per_mat);
+    } else {
+        word = row * words + col;
+    }
+    if (packed)
+        o.s[word * 4 + (g & 3)] = (uint8_t)(e + 127);
+    else
+        reinterpret_cast<float *>(o.s)[word] = p;
+}
 
 // ---------------------------------------------------------------------------
 // layout plan
@@ -294,33 +336,48 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     for (int e = threadIdx.x; e < L; e += kCountThreads) row[e] = hist[e];
 }
 
-template <int U0, int NQ, int NCH>
-__device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], const int32_t *dlist, int k,
-                                               int lane, int64_t c0, int64_t chunks,
-                                               u32x2 *out_q, float *out_s, int64_t cap_rows,
-                                               int32_t *status)
+// Quantises chunks [U0, U0 + NQ) of a lane's pass (chunk u of the pass is row
+// chunk c0 + u*64 + lane) and stores the e4m3fn bytes and the group scales to
+// every destination row dst_of(j) >= 0, j < k.  A row pass is quantised in
+// parts so that only NQ chunks of quantisation temporaries are live at a
+// time while all of the pass's loads were issued together.  dst_of(j, first)
+// returns -1 to skip a slot; `first` is true for the first part of the first
+// pass, where capacity faults are reported.
+template <int U0, int NQ, int NCH, typename DstFn>
+__device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], int k, int lane, int64_t c0,
+                                               int64_t chunks, const Fp8Out &o, bool ue8m0,
+                                               DstFn dst_of)
 {
     u32x2 q[NQ];
     float sc[NQ];
+    int ex[NQ];
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) q[u] = quant_chunk(v[U0 + u], &sc[u]);
+    for (int u = 0; u < NQ; ++u) q[u] = quant_chunk(v[U0 + u], ue8m0, &sc[u], &ex[u]);
     const uint32_t q_bytes = (uint32_t)(chunks * 8);
     const uint32_t s_bytes = (uint32_t)(chunks / 16 * 4);
     const bool group_head = (lane & 15) == 0;       // one scale per 16-lane group
+    const bool row_major_f32 = (o.flags & (CDL_FP8_SCALE_COLMAJOR | CDL_FP8_SCALE_PACKED)) == 0;
     for (int j = 0; j < k; ++j) {
-        const int32_t dst = uniform(dlist[j]);
+        // readfirstlane: the row is wave-uniform, but a status report inside
+        // dst_of hides that from the compiler (the descriptors must be scalar)
+        const int64_t dst = uniform((int32_t)dst_of(j, c0 == 0 && U0 == 0));
         if (dst < 0) continue;
-        if ((int64_t)dst >= cap_rows) {
-            if (c0 == 0 && U0 == 0 && lane == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
-            continue;
-        }
-        const rsrc_t oq = make_rsrc(out_q + (int64_t)dst * chunks, q_bytes);
-        const rsrc_t os = make_rsrc(out_s + (int64_t)dst * (chunks / 16), s_bytes);
+        const rsrc_t oq = make_rsrc(o.q + dst * chunks, q_bytes);
 #pragma unroll
-        for (int u = 0; u < NQ; ++u) {
+        for (int u = 0; u < NQ; ++u)
             buf_st8(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + (U0 + u) * kWave * 8);
-            if (group_head)
-                buf_st4(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + (U0 + u) * 16);
+        if (row_major_f32) {
+            const rsrc_t os = make_rsrc(reinterpret_cast<float *>(o.s) + dst * (chunks / 16), s_bytes);
+#pragma unroll
+            for (int u = 0; u < NQ; ++u)
+                if (group_head)
+                    buf_st4(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + (U0 + u) * 16);
+        } else if (group_head) {
+#pragma unroll
+            for (int u = 0; u < NQ; ++u) {
+                const int64_t c = c0 + (U0 + u) * kWave + lane;
+                if (c < chunks) put_scale(o, dst, c >> 4, sc[u], ex[u]);
+            }
         }
     }
 }
@@ -377,8 +434,7 @@ struct PermuteArgs {
     const u32x4 *x;
     int64_t chunks;       // H / 8
     u32x4 *out;           // bf16 rows
-    u32x2 *out_q;         // fp8 rows (8 bytes per chunk)
-    float *out_s;         // fp8 scales, chunks / 16 per row
+    Fp8Out fp8;           // fp8 rows and scales
     int64_t cap_rows;
     int32_t *status;
 };
@@ -558,9 +614,18 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
                 for (int u = 0; u < NC; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
             }
         } else {
-            store_fp8_part<0, NC / 2>(v, my, k, lane, c0, a.chunks, a.out_q, a.out_s, a.cap_rows, a.status);
-            store_fp8_part<NC / 2, NC / 2>(v, my, k, lane, c0, a.chunks, a.out_q, a.out_s, a.cap_rows,
-                                          a.status);
+            auto dst_of = [&](int j, bool report) -> int64_t {
+                const int32_t d = uniform(my[j]);
+                if (d < 0) return -1;
+                if ((int64_t)d >= a.cap_rows) {
+                    if (report && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
+                    return -1;
+                }
+                return d;
+            };
+            const bool ue8m0 = (a.fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
+            store_fp8_part<0, NC / 2>(v, k, lane, c0, a.chunks, a.fp8, ue8m0, dst_of);
+            store_fp8_part<NC / 2, NC / 2>(v, k, lane, c0, a.chunks, a.fp8, ue8m0, dst_of);
         }
     }
 }
@@ -577,8 +642,8 @@ constexpr int kRowThreads = kRowTok * kWave;
 template <bool FP8>
 __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
     const u32x4 *__restrict__ x, int64_t T, int64_t chunks, int32_t k,
-    const int32_t *__restrict__ src2dst, u32x4 *__restrict__ out, u32x2 *__restrict__ out_q,
-    float *__restrict__ out_s, int64_t cap_rows, int32_t *__restrict__ status)
+    const int32_t *__restrict__ src2dst, u32x4 *__restrict__ out, Fp8Out fp8, int64_t cap_rows,
+    int32_t *__restrict__ status)
 {
     constexpr int NC = FP8 ? kMaxChunksFp8 : kMaxChunks;
     const int lane = threadIdx.x & (kWave - 1);
@@ -597,8 +662,18 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
 #pragma unroll
         for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         if (FP8) {
-            store_fp8_part<0, NC / 2>(v, d, k, lane, c0, chunks, out_q, out_s, cap_rows, status);
-            store_fp8_part<NC / 2, NC / 2>(v, d, k, lane, c0, chunks, out_q, out_s, cap_rows, status);
+            auto dst_of = [&](int j, bool report) -> int64_t {
+                const int32_t dd = d[j];
+                if (dd < 0) return -1;
+                if ((int64_t)dd >= cap_rows) {
+                    if (report && lane == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
+                    return -1;
+                }
+                return dd;
+            };
+            const bool ue8m0 = (fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
+            store_fp8_part<0, NC / 2>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of);
+            store_fp8_part<NC / 2, NC / 2>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of);
             continue;
         }
         for (int j = 0; j < k; ++j) {
@@ -725,14 +800,16 @@ __device__ __forceinline__ int64_t ll_row(const int32_t *__restrict__ ids, int32
 
 // One wave per token (kRowTok per workgroup); workgroups whose index is below
 // ceil(L / threads) also write masked_m; waves at or beyond T stop there.
+template <bool FP8>
 __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
     const u32x4 *__restrict__ x, int64_t T, int64_t chunks, int32_t k,
     const int32_t *__restrict__ ids, int32_t expert_begin, int32_t L,
     const int32_t *__restrict__ src2dst, const int64_t *__restrict__ seg_indptr,
-    const int32_t *__restrict__ counts, int64_t cap, u32x4 *__restrict__ out,
+    const int32_t *__restrict__ counts, int64_t cap, u32x4 *__restrict__ out, Fp8Out fp8,
     int32_t *__restrict__ masked_m, int32_t *__restrict__ ll_src2dst,
     int32_t *__restrict__ status)
 {
+    constexpr int NC = FP8 ? kMaxChunksFp8 : kMaxChunks;
     {
         const int64_t e = (int64_t)blockIdx.x * kRowThreads + threadIdx.x;
         if (e < L) masked_m[e] = (int32_t)((int64_t)counts[e] < cap ? counts[e] : cap);
@@ -755,18 +832,28 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
     const uint32_t row_bytes = (uint32_t)(chunks * 16);
     const uint32_t voff = (uint32_t)lane * 16u;
     const rsrc_t xr = make_rsrc(x + t * chunks, row_bytes);
-    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kMaxChunks * kWave) {
+    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
-        u32x4 v[kMaxChunks];
+        u32x4 v[NC];
 #pragma unroll
-        for (int u = 0; u < kMaxChunks; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+        for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+        if (FP8) {
+            auto dst_of = [&](int j, bool) -> int64_t {
+                bool ovf;
+                return ll_row(ids, expert_begin, L, src2dst, seg_indptr, cap, t * k + j, &ovf);
+            };
+            const bool ue8m0 = (fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
+            store_fp8_part<0, NC / 2>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of);
+            store_fp8_part<NC / 2, NC / 2>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of);
+            continue;
+        }
         for (int j = 0; j < k; ++j) {
             bool ovf;
             const int64_t row = ll_row(ids, expert_begin, L, src2dst, seg_indptr, cap, t * k + j, &ovf);
             if (row < 0) continue;
             const rsrc_t o = make_rsrc(out + row * chunks, row_bytes);
 #pragma unroll
-            for (int u = 0; u < kMaxChunks; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
+            for (int u = 0; u < NC; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
         }
     }
 }
@@ -899,6 +986,37 @@ inline int check_layout_args(const int32_t *topk_ids, int64_t T, int32_t k, int3
     return CDL_OK;
 }
 
+inline bool valid_scale_flags(int32_t f)
+{
+    if (f & ~(CDL_FP8_SCALE_UE8M0 | CDL_FP8_SCALE_COLMAJOR | CDL_FP8_SCALE_PACKED)) return false;
+    return !(f & CDL_FP8_SCALE_PACKED) || (f & CDL_FP8_SCALE_UE8M0);
+}
+
+inline Fp8Out make_fp8_out(uint8_t *q, void *s, int32_t flags, int64_t H, int64_t rows_per_mat)
+{
+    Fp8Out o;
+    o.q = (u32x2 *)q;
+    o.s = (uint8_t *)s;
+    o.flags = flags;
+    o.groups = H / CDL_FP8_GROUP;
+    o.rows_per_mat = rows_per_mat > 0 ? rows_per_mat : 1;
+    o.ld = (o.rows_per_mat + 3) / 4 * 4;
+    return o;
+}
+
+// Bytes of a scale buffer for `rows` rows of H elements in the given format.
+inline int64_t scale_bytes(int64_t rows, int64_t H, int32_t flags, int64_t rows_per_mat)
+{
+    const int64_t G = H / CDL_FP8_GROUP;
+    const int64_t words = (flags & CDL_FP8_SCALE_PACKED) ? (G + 3) / 4 : G;
+    if (flags & CDL_FP8_SCALE_COLMAJOR) {
+        const int64_t rpm = rows_per_mat > 0 ? rows_per_mat : 1;
+        const int64_t nmat = (rows + rpm - 1) / rpm;
+        return nmat * words * ((rpm + 3) / 4 * 4) * 4;
+    }
+    return rows * words * 4;
+}
+
 template <int MODE>
 int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
 {
@@ -1011,17 +1129,25 @@ int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_
     return run_layout<kRowsBf16>(a, ws, (hipStream_t)stream);
 }
 
+size_t cdl_fp8_scale_bytes(int64_t rows, int64_t H, int32_t scale_flags, int64_t rows_per_mat)
+{
+    if (rows < 0 || H < CDL_FP8_GROUP || H % CDL_FP8_GROUP != 0 || !valid_scale_flags(scale_flags))
+        return 0;
+    if ((scale_flags & CDL_FP8_SCALE_COLMAJOR) && rows_per_mat < 1) return 0;
+    return (size_t)scale_bytes(rows, H, scale_flags, rows_per_mat);
+}
+
 int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
                     int32_t expert_begin, int32_t L, int32_t alignment, int32_t *counts,
                     int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
-                    int64_t reorder_cap, uint8_t *out_q, float *out_scales, int64_t cap_rows,
-                    int32_t *status, void *ws, size_t ws_bytes, void *stream)
+                    int64_t reorder_cap, uint8_t *out_q, void *out_scales, int32_t scale_flags,
+                    int64_t cap_rows, int32_t *status, void *ws, size_t ws_bytes, void *stream)
 {
     int rc = check_layout_args(topk_ids, T, k, L, alignment, counts, seg_indptr, src2dst,
                                reorder_topk_ids, reorder_cap, ws, ws_bytes);
     if (rc != CDL_OK) return rc;
     if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
-    if (H % CDL_FP8_GROUP != 0) return CDL_ERR_UNSUPPORTED;
+    if (H % CDL_FP8_GROUP != 0 || !valid_scale_flags(scale_flags)) return CDL_ERR_UNSUPPORTED;
     if (cap_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
     if (T > 0 && !x) return CDL_ERR_NULL_POINTER;
     if (cap_rows > 0 && (!out_q || !out_scales)) return CDL_ERR_NULL_POINTER;
@@ -1030,8 +1156,7 @@ int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
                                 src2dst, reorder_topk_ids, reorder_cap, status);
     a.x = (const u32x4 *)x;
     a.chunks = H / 8;
-    a.out_q = (u32x2 *)out_q;
-    a.out_s = out_scales;
+    a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap_rows);
     a.cap_rows = cap_rows;
     return run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
 }
@@ -1094,7 +1219,7 @@ int cdl_dispatch(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32
     hipStream_t s = (hipStream_t)stream;
     if (H % 8 == 0 && aligned(x, 16) && aligned(out, 16)) {
         scatter_rows_kernel<false><<<dim3((unsigned)((T + kRowTok - 1) / kRowTok)), dim3(kRowThreads), 0, s>>>(
-            (const u32x4 *)x, T, H / 8, k, src2dst, (u32x4 *)out, nullptr, nullptr, cap_rows, status);
+            (const u32x4 *)x, T, H / 8, k, src2dst, (u32x4 *)out, Fp8Out{}, cap_rows, status);
     } else {
         scatter_rows_u16<<<dim3((unsigned)T), dim3(128), 0, s>>>(x, H, k, src2dst, out, cap_rows,
                                                                   status);
@@ -1106,10 +1231,18 @@ int cdl_dispatch_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const i
                      uint8_t *out_q, float *out_scales, int64_t cap_rows, int32_t *status,
                      void *stream)
 {
+    return cdl_dispatch_fp8_ex(x, T, H, k, src2dst, out_q, out_scales, 0, cap_rows, status,
+                               stream);
+}
+
+int cdl_dispatch_fp8_ex(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                        const int32_t *src2dst, uint8_t *out_q, void *out_scales,
+                        int32_t scale_flags, int64_t cap_rows, int32_t *status, void *stream)
+{
     int rc = check_tk(T, k);
     if (rc != CDL_OK) return rc;
     if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
-    if (H % CDL_FP8_GROUP != 0) return CDL_ERR_UNSUPPORTED;
+    if (H % CDL_FP8_GROUP != 0 || !valid_scale_flags(scale_flags)) return CDL_ERR_UNSUPPORTED;
     if (T == 0) return CDL_OK;
     if (!x || !src2dst) return CDL_ERR_NULL_POINTER;
     if (cap_rows > 0 && (!out_q || !out_scales)) return CDL_ERR_NULL_POINTER;
@@ -1119,15 +1252,15 @@ int cdl_dispatch_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const i
         return CDL_ERR_UNSUPPORTED;
     hipStream_t s = (hipStream_t)stream;
     scatter_rows_kernel<true><<<dim3((unsigned)((T + kRowTok - 1) / kRowTok)), dim3(kRowThreads), 0, s>>>(
-        (const u32x4 *)x, T, H / 8, k, src2dst, nullptr, (u32x2 *)out_q, out_scales, cap_rows,
-        status);
+        (const u32x4 *)x, T, H / 8, k, src2dst, nullptr,
+        make_fp8_out(out_q, out_scales, scale_flags, H, cap_rows), cap_rows, status);
     return launch_status();
 }
 
-int cdl_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
-                    int32_t expert_begin, int32_t L, const int32_t *src2dst,
-                    const int64_t *seg_indptr, const int32_t *counts, int64_t cap, uint16_t *out,
-                    int32_t *masked_m, int32_t *ll_src2dst, int32_t *status, void *stream)
+static int check_ll_args(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                         const int32_t *topk_ids, int32_t L, const int32_t *src2dst,
+                         const int64_t *seg_indptr, const int32_t *counts, int64_t cap,
+                         const void *out, int32_t *masked_m, int32_t *ll_src2dst)
 {
     int rc = check_tk(T, k);
     if (rc != CDL_OK) return rc;
@@ -1137,15 +1270,49 @@ int cdl_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
     if (!counts || !seg_indptr || !masked_m) return CDL_ERR_NULL_POINTER;
     if (T > 0 && (!x || !topk_ids || !src2dst || !ll_src2dst)) return CDL_ERR_NULL_POINTER;
     if (cap > 0 && !out) return CDL_ERR_NULL_POINTER;
-    if ((T > 0 && !aligned(x, 16)) || (cap > 0 && !aligned(out, 16))) return CDL_ERR_UNSUPPORTED;
-    hipStream_t s = (hipStream_t)stream;
-    // one wave per token; at least enough workgroups to write masked_m
+    if (T > 0 && !aligned(x, 16)) return CDL_ERR_UNSUPPORTED;
+    return CDL_OK;
+}
+
+// one wave per token; at least enough workgroups to write masked_m
+static dim3 ll_grid(int64_t T, int32_t L)
+{
     const int64_t mm_blocks = (L + kRowThreads - 1) / kRowThreads;
     const int64_t tok_blocks = (T + kRowTok - 1) / kRowTok;
-    const int64_t grid = tok_blocks > mm_blocks ? tok_blocks : mm_blocks;
-    scatter_rows_ll<<<dim3((unsigned)grid), dim3(kRowThreads), 0, s>>>(
+    return dim3((unsigned)(tok_blocks > mm_blocks ? tok_blocks : mm_blocks));
+}
+
+int cdl_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
+                    int32_t expert_begin, int32_t L, const int32_t *src2dst,
+                    const int64_t *seg_indptr, const int32_t *counts, int64_t cap, uint16_t *out,
+                    int32_t *masked_m, int32_t *ll_src2dst, int32_t *status, void *stream)
+{
+    int rc = check_ll_args(x, T, H, k, topk_ids, L, src2dst, seg_indptr, counts, cap, out,
+                           masked_m, ll_src2dst);
+    if (rc != CDL_OK) return rc;
+    if (cap > 0 && !aligned(out, 16)) return CDL_ERR_UNSUPPORTED;
+    scatter_rows_ll<false><<<ll_grid(T, L), dim3(kRowThreads), 0, (hipStream_t)stream>>>(
         (const u32x4 *)x, T, H / 8, k, topk_ids, expert_begin, L, src2dst, seg_indptr, counts,
-        cap, (u32x4 *)out, masked_m, ll_src2dst, status);
+        cap, (u32x4 *)out, Fp8Out{}, masked_m, ll_src2dst, status);
+    return launch_status();
+}
+
+int cdl_dispatch_ll_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                        const int32_t *topk_ids, int32_t expert_begin, int32_t L,
+                        const int32_t *src2dst, const int64_t *seg_indptr, const int32_t *counts,
+                        int64_t cap, uint8_t *out_q, void *out_scales, int32_t scale_flags,
+                        int32_t *masked_m, int32_t *ll_src2dst, int32_t *status, void *stream)
+{
+    int rc = check_ll_args(x, T, H, k, topk_ids, L, src2dst, seg_indptr, counts, cap, out_q,
+                           masked_m, ll_src2dst);
+    if (rc != CDL_OK) return rc;
+    if (H % CDL_FP8_GROUP != 0 || !valid_scale_flags(scale_flags)) return CDL_ERR_UNSUPPORTED;
+    if (cap > 0 && !out_scales) return CDL_ERR_NULL_POINTER;
+    if (cap > 0 && (!aligned(out_q, 8) || !aligned(out_scales, 4))) return CDL_ERR_UNSUPPORTED;
+    scatter_rows_ll<true><<<ll_grid(T, L), dim3(kRowThreads), 0, (hipStream_t)stream>>>(
+        (const u32x4 *)x, T, H / 8, k, topk_ids, expert_begin, L, src2dst, seg_indptr, counts,
+        cap, nullptr, make_fp8_out(out_q, out_scales, scale_flags, H, cap), masked_m, ll_src2dst,
+        status);
     return launch_status();
 }
 

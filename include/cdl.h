@@ -72,6 +72,11 @@ extern "C" {
 #define CDL_MAX_TOPK 64
 #define CDL_MAX_LOCAL_EXPERTS 2048
 #define CDL_FP8_GROUP 128
+
+/* fp8 scale formats (bit flags) -- see cdl_dispatch_fp8_ex */
+#define CDL_FP8_SCALE_UE8M0 1       /* power-of-two scales */
+#define CDL_FP8_SCALE_COLMAJOR 2    /* group-major, TMA-aligned columns */
+#define CDL_FP8_SCALE_PACKED 4      /* exponent bytes, 4 groups per 32-bit word (needs UE8M0) */
 #define CDL_MAX_ALIGNMENT 1024
 #define CDL_MAX_EXPERTS 8192        /* global experts for cdl_rank_layout */
 #define CDL_MAX_RANKS 1024
@@ -167,16 +172,17 @@ int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_
 
 /*
  * cdl_permute_fp8 -- cdl_permute with the per-token, per-128-group fp8
- * quantisation of cdl_dispatch_fp8 on the scatter ([deepep.py],
- * _DeepEPDispatcherImplNormal.dispatch_a).  out_q [cap_rows, H] E4M3FN bytes,
- * out_scales [cap_rows, H/128] fp32.  Requires H % 128 == 0, 16-byte aligned
- * x, 8-byte aligned out_q and 4-byte aligned out_scales.
+ * quantisation of cdl_dispatch_fp8_ex on the scatter ([deepep.py],
+ * _DeepEPDispatcherImplNormal.dispatch_a).  out_q [cap_rows, H] E4M3FN bytes;
+ * out_scales in the scale_flags format for cap_rows rows (one column-major
+ * matrix of cap_rows rows).  Requires H % 128 == 0, 16-byte aligned x,
+ * 8-byte aligned out_q and 4-byte aligned out_scales.
  */
 int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
                     int32_t expert_begin, int32_t L, int32_t alignment, int32_t *counts,
                     int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
-                    int64_t reorder_cap, uint8_t *out_q, float *out_scales, int64_t cap_rows,
-                    int32_t *status, void *ws, size_t ws_bytes, void *stream);
+                    int64_t reorder_cap, uint8_t *out_q, void *out_scales, int32_t scale_flags,
+                    int64_t cap_rows, int32_t *status, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * cdl_rank_layout_workspace_size -- device workspace bytes for
@@ -254,6 +260,43 @@ int cdl_dispatch_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
                      int64_t cap_rows, int32_t *status, void *stream);
 
 /*
+ * cdl_fp8_scale_bytes -- bytes of a scale buffer for `rows` destination rows
+ * of H elements in the scale_flags format; for column-major formats every
+ * rows_per_mat rows form one matrix (normal dispatch: rows_per_mat = rows =
+ * cap_rows; low latency: rows = L*cap, rows_per_mat = cap).  0 for invalid
+ * arguments.
+ */
+size_t cdl_fp8_scale_bytes(int64_t rows, int64_t H, int32_t scale_flags, int64_t rows_per_mat);
+
+/*
+ * cdl_dispatch_fp8_ex -- cdl_dispatch_fp8 with a choice of scale format, the
+ * switches of the group quant that feeds DeepGEMM ([deepep.py],
+ * _DeepEPDispatcherImplNormal.dispatch_a: column_major_scales,
+ * scale_tma_aligned, scale_ue8m0; _DeepEPDispatcherImplLowLatency.
+ * _dispatch_core: round_scale / use_ue8m0 give int32-packed UE8M0 scales).
+ * scale_flags, a combination of:
+ *   0                        fp32 scales s = amax / 448, row-major [rows][G]
+ *                            (exactly cdl_dispatch_fp8)
+ *   CDL_FP8_SCALE_UE8M0      the scale is the smallest power of two p >=
+ *                            2^-127 with 448 * p >= amax; q = e4m3(x / p) is
+ *                            an exact scaling (no clamp); a zero group gets
+ *                            p = 2^-127
+ *   CDL_FP8_SCALE_COLMAJOR   scales stored group-major, [G][ld] fp32 with
+ *                            ld = cap_rows rounded up to a multiple of 4 (every
+ *                            column 16-byte aligned); rows [cap_rows, ld) of
+ *                            each column are never written
+ *   CDL_FP8_SCALE_PACKED     (requires UE8M0) the exponent byte log2(p) + 127,
+ *                            four consecutive groups per 32-bit word, group g
+ *                            in byte g % 4; row-major [rows][ceil(G/4)] words
+ *                            or, with COLMAJOR, [ceil(G/4)][ld] words
+ * out_scales must hold cdl_fp8_scale_bytes(cap_rows, H, scale_flags,
+ * cap_rows) bytes.  CDL_ERR_UNSUPPORTED for an invalid combination.
+ */
+int cdl_dispatch_fp8_ex(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                        const int32_t *src2dst, uint8_t *out_q, void *out_scales,
+                        int32_t scale_flags, int64_t cap_rows, int32_t *status, void *stream);
+
+/*
  * cdl_dispatch_ll -- low-latency dispatch into a padded per-expert buffer
  * ([deepep.py], _DeepEPDispatcherImplLowLatency._dispatch_core:
  * low_latency_dispatch returns the packed receive buffer and its per-expert
@@ -276,6 +319,21 @@ int cdl_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k,
                     const int32_t *counts, int64_t cap, uint16_t *out,
                     int32_t *masked_m, int32_t *ll_src2dst, int32_t *status,
                     void *stream);
+
+/*
+ * cdl_dispatch_ll_fp8 -- cdl_dispatch_ll with fp8 rows ([deepep.py],
+ * _DeepEPDispatcherImplLowLatency._dispatch_core: low_latency_dispatch with
+ * use_fp8 returns the packed rows with their scales).  out_q [L, cap, H]
+ * E4M3FN bytes; out_scales in the scale_flags format of cdl_dispatch_fp8_ex
+ * for L*cap rows where every expert's cap rows form one column-major matrix
+ * (rows_per_mat = cap).  Slots, masked_m, ll_src2dst and overflow handling
+ * are those of cdl_dispatch_ll.
+ */
+int cdl_dispatch_ll_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                        const int32_t *topk_ids, int32_t expert_begin, int32_t L,
+                        const int32_t *src2dst, const int64_t *seg_indptr, const int32_t *counts,
+                        int64_t cap, uint8_t *out_q, void *out_scales, int32_t scale_flags,
+                        int32_t *masked_m, int32_t *ll_src2dst, int32_t *status, void *stream);
 
 /*
  * cdl_combine -- gather the expert outputs back and form each token's

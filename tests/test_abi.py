@@ -205,9 +205,9 @@ def test_permute_rejects():
 def test_permute_fp8_rejects():
     lib = cdl.library()
     names = ["x", "T", "H", "k", "ids", "b", "L", "A", "counts", "seg", "s2d", "reorder", "rcap",
-             "q", "s", "cap", "status", "ws", "wsb", "stream"]
-    base = [FAKE, 4, 256, 2, FAKE, 0, 8, 1, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 16, NULL, FAKE,
-            1 << 20, NULL]
+             "q", "s", "sf", "cap", "status", "ws", "wsb", "stream"]
+    base = [FAKE, 4, 256, 2, FAKE, 0, 8, 1, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, 0, 16, NULL,
+            FAKE, 1 << 20, NULL]
 
     def call(**over):
         a = list(base)
@@ -220,6 +220,36 @@ def test_permute_fp8_rejects():
     assert call(s=NULL) == ENULL
     assert call(q=ctypes.c_void_p(0x1004)) == EUNSUP
     assert call(counts=NULL) == ENULL
+    assert call(sf=4) == EUNSUP                      # packed needs UE8M0
+    assert call(sf=8) == EUNSUP                      # unknown flag
+
+
+def test_fp8_scale_bytes():
+    f = cdl.library().cdl_fp8_scale_bytes
+    assert f(10, 256, 0, 10) == 10 * 2 * 4
+    assert f(10, 256, 2, 10) == 2 * 12 * 4          # [G][ld], ld = 12
+    assert f(10, 640, 5, 10) == 10 * 2 * 4          # 5 groups -> 2 words per row
+    assert f(10, 640, 7, 3) == 4 * 2 * 4 * 4        # 4 matrices of [2 words][ld 4]
+    assert f(10, 200, 0, 10) == 0                   # H % 128
+    assert f(10, 256, 4, 10) == 0                   # packed without UE8M0
+
+
+def test_dispatch_fp8_ex_and_ll_fp8_reject():
+    lib = cdl.library()
+    f = lib.cdl_dispatch_fp8_ex
+    # x, T, H, k, s2d, q, s, sf, cap, status, stream
+    assert f(FAKE, 4, 256, 2, FAKE, FAKE, FAKE, 6, 8, NULL, NULL) == EUNSUP
+    assert f(FAKE, 4, 200, 2, FAKE, FAKE, FAKE, 0, 8, NULL, NULL) == EUNSUP
+    assert f(FAKE, 4, 256, 2, FAKE, NULL, FAKE, 0, 8, NULL, NULL) == ENULL
+    g = lib.cdl_dispatch_ll_fp8
+    # x, T, H, k, ids, b, L, s2d, seg, counts, cap, q, s, sf, mm, ll, status, stream
+    args = [FAKE, 4, 256, 2, FAKE, 0, 8, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 0, FAKE, FAKE, NULL, NULL]
+    a = list(args); a[13] = 4
+    assert g(*a) == EUNSUP
+    a = list(args); a[12] = NULL
+    assert g(*a) == ENULL
+    a = list(args); a[2] = 200
+    assert g(*a) == EUNSUP
 
 
 def test_rank_layout_rejects():

@@ -637,3 +637,102 @@ def test_rank_layout_edge_cases():
     assert np.array_equal(npy(rl.is_token_in_rank), ir)
     with pytest.raises(cdl.CdlError):
         cdl.rank_layout(ids.to(DEV), 100, 8, 1)
+
+
+# --------------------------------------------------------------------------
+# fp8 scale formats and fp8 on the low-latency path
+# --------------------------------------------------------------------------
+
+UE, CM, PK = cdl.FP8_SCALE_UE8M0, cdl.FP8_SCALE_COLMAJOR, cdl.FP8_SCALE_PACKED
+FORMATS = [0, UE, CM, UE | CM, UE | PK, UE | CM | PK]
+
+
+def raw_bytes(t):
+    return t.detach().contiguous().cpu().view(torch.uint8).numpy().reshape(-1)
+
+
+def filled_scales(nbytes, fill=0xEE):
+    return torch.full((max(nbytes, 1),), fill, dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("flags", FORMATS)
+def test_fp8_scale_formats_parity(flags):
+    w = W.WORKLOADS["fp8_dispatch"].scaled(T=517, H=640)          # 5 groups: ragged packing
+    announce("fp8 format %d" % flags)
+    x, ids, wts = W.make_inputs(w)
+    c, s, d, r = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s[-1])
+    cap = R + 3                                                     # ld = roundup(cap, 4)
+    Q, S = oracle.dispatch_fp8_fmt(W.bf16_bits(x), d, w.k, cap, flags, rows_per_mat=cap,
+                                   fill=0xEE)
+    nbytes = cdl.fp8_scale_bytes(cap, w.H, flags, cap)
+    assert nbytes == S.size
+    # unfused scatter from a layout
+    lay = cdl.dispatch_layout(ids.to(DEV), w.expert_begin, w.L)
+    q = torch.zeros(cap, w.H, dtype=torch.uint8, device=DEV)
+    sb = filled_scales(nbytes)
+    st = status_word()
+    cdl.dispatch_fp8(x.to(DEV), lay, out_q=q, out_scales=sb, status=st, scale_flags=flags)
+    # fused permute
+    q2 = torch.zeros(cap, w.H, dtype=torch.uint8, device=DEV)
+    sb2 = filled_scales(nbytes)
+    cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q2, out_scales=sb2,
+                    status=st, scale_flags=flags)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(u8(q), Q) and np.array_equal(u8(q2), Q)
+    assert np.array_equal(raw_bytes(sb), S) and np.array_equal(raw_bytes(sb2), S)
+
+
+def test_fp8_ue8m0_group_magnitudes():
+    """Power-of-two scales over every binary magnitude, zero groups and
+    subnormal groups, in the packed column-major format."""
+    announce("fp8 ue8m0 magnitudes")
+    g = torch.Generator().manual_seed(77)
+    exps = list(range(-133, 125))
+    vals = (torch.randn(len(exps), 128, generator=g).double()
+            * torch.tensor([2.0 ** e for e in exps], dtype=torch.float64)[:, None])
+    vals = vals.clamp(-3.3e38, 3.3e38).float().to(torch.bfloat16)
+    xb = W.bf16_bits(vals).copy()
+    xb[0, :] = 0
+    xb[2, ::2] = 0x8000
+    G8 = 8
+    rows = -(-xb.shape[0] // G8)
+    xfull = np.zeros((rows * G8, 128), np.uint16)
+    xfull[:xb.shape[0]] = xb
+    xfull = xfull.reshape(rows, 128 * G8)
+    ids = torch.arange(rows, dtype=torch.int32).reshape(rows, 1)
+    _, _, d, _ = oracle.layout(ids.numpy(), 0, rows)
+    for flags in (UE, UE | CM | PK):
+        Q, S = oracle.dispatch_fp8_fmt(xfull, d, 1, rows, flags, rows_per_mat=rows, fill=0xEE)
+        lay = cdl.dispatch_layout(ids.to(DEV), 0, rows)
+        q = torch.zeros(rows, 128 * G8, dtype=torch.uint8, device=DEV)
+        sb = filled_scales(S.size)
+        cdl.dispatch_fp8(W.bits_to_bf16(xfull).to(DEV), lay, out_q=q, out_scales=sb,
+                         scale_flags=flags)
+        torch.cuda.synchronize()
+        assert np.array_equal(u8(q), Q)
+        assert np.array_equal(raw_bytes(sb), S)
+
+
+@pytest.mark.parametrize("flags,cap", [(0, 1024), (UE, 1024), (CM, 1024), (UE | CM | PK, 1024),
+                                       (UE | CM, 5)])
+def test_ll_fp8_parity(flags, cap):
+    w = W.WORKLOADS["ll_decode"]
+    if cap < 100:
+        w = w.scaled(T=100, H=512)
+    announce("ll fp8 flags=%d cap=%d" % (flags, cap))
+    x, ids, wts = W.make_inputs(w)
+    Q, S, mm, ll, ovf = oracle.dispatch_ll_fp8(W.bf16_bits(x), ids.numpy(), w.expert_begin, w.L,
+                                               cap, flags, fill=0xEE)
+    lay = cdl.dispatch_layout(ids.to(DEV), w.expert_begin, w.L)
+    q = torch.zeros(w.L, cap, w.H, dtype=torch.uint8, device=DEV)
+    sb = filled_scales(S.size)
+    st = status_word()
+    q, sb, gmm, gll = cdl.dispatch_ll_fp8(x.to(DEV), lay, cap, scale_flags=flags, out_q=q,
+                                          out_scales=sb, status=st)
+    torch.cuda.synchronize()
+    assert np.array_equal(npy(gmm), mm) and np.array_equal(npy(gll), ll)
+    assert (int(st.item()) != 0) == bool(ovf)
+    assert np.array_equal(u8(q).reshape(-1), Q.reshape(-1))
+    assert np.array_equal(raw_bytes(sb), S)
