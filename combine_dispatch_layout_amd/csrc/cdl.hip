@@ -440,8 +440,9 @@ struct PermuteArgs {
 };
 
 // One workgroup per TPB tokens, one wave per token.
-//  0. the wave of token t loads its row (first NC chunks per lane)
-//     if the token has a valid slot;
+//  0. every thread loads its first batch of layout operands, then the wave
+//     of token t loads its row (first NC chunks per lane) if the token has
+//     a valid slot;
 //  1. tot[e] = all valid slots of e; cur[e] = valid slots of e before this
 //     workgroup's first slot (superblock counts of earlier superblocks plus a
 //     recount of this superblock's earlier slots);
@@ -475,7 +476,28 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     const int64_t slot_begin = t_begin * k;
     const int nslots = (int)((t_end > t_begin ? t_end - t_begin : 0) * k);
 
-    // 0. row prefetch
+    // 0. loads.  The layout's own operands go first (the first batch of
+    //    superblock counts and of the recount, and the 64 slots this wave
+    //    ranks), then the token's row.  A wave's loads complete in issue
+    //    order, so the offsets below wait only for those small loads while
+    //    the row is still in flight.
+    constexpr int kBatch = 8;
+    const int64_t s_me = blk / a.sbb;
+    const int64_t nsc = a.S * L;
+    const int64_t rc_begin = s_me * a.sb_slots;
+    const int64_t nrc = slot_begin - rc_begin;
+    const rsrc_t r_sc = make_rsrc(a.sb_counts, (uint32_t)(nsc * 4));
+    const rsrc_t r_rc = make_rsrc(a.ids + rc_begin, (uint32_t)(nrc * 4));
+    const rsrc_t r_my = make_rsrc(a.ids + slot_begin, (uint32_t)(nslots * 4));
+    int32_t c[kBatch], id[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) c[q] = buf_ld4(r_sc, (uint32_t)(q * NT + tid) * 4u, 0);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) id[q] = buf_ld4(r_rc, (uint32_t)(q * NT + tid) * 4u, 0);
+    // nslots <= TPB * 64 (k <= 64), so wave w ranks exactly round w
+    const int my_rel = wave * kWave + lane;
+    const int32_t my_id = buf_ld4(r_my, (uint32_t)my_rel * 4u, 0);
+
     const int64_t t = t_begin + wave;
     bool tok_valid = false;
     if (MODE != kLayoutOnly && t < a.T) {
@@ -496,41 +518,34 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
         cur[e] = 0;
     }
     __syncthreads();
-    const int64_t s_me = blk / a.sbb;
-    const int64_t nsc = a.S * L;
-    {
-        // superblock counts, kBatch per thread per round, loads first
-        constexpr int kBatch = 8;
-        const rsrc_t r = make_rsrc(a.sb_counts, (uint32_t)(nsc * 4));
-        for (int64_t b0 = 0; b0 < nsc; b0 += (int64_t)NT * kBatch) {
-            int32_t c[kBatch];
+    // superblock counts, kBatch per thread per round
+    for (int64_t b0 = 0; b0 < nsc; b0 += (int64_t)NT * kBatch) {
+        if (b0 > 0) {
 #pragma unroll
             for (int q = 0; q < kBatch; ++q)
-                c[q] = buf_ld4(r, (uint32_t)(q * NT + tid) * 4u, (uint32_t)(b0 * 4));
+                c[q] = buf_ld4(r_sc, (uint32_t)(q * NT + tid) * 4u, (uint32_t)(b0 * 4));
+        }
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int64_t idx = b0 + q * NT + tid;
-                if (idx < nsc && c[q]) {
-                    const int e = (int)(idx % L);
-                    atomicAdd(&tot[e], c[q]);
-                    if (idx / L < s_me) atomicAdd(&cur[e], c[q]);
-                }
+        for (int q = 0; q < kBatch; ++q) {
+            const int64_t idx = b0 + q * NT + tid;
+            if (idx < nsc && c[q]) {
+                const int e = (int)(idx % L);
+                atomicAdd(&tot[e], c[q]);
+                if (idx / L < s_me) atomicAdd(&cur[e], c[q]);
             }
         }
-        // recount of this superblock's slots before the workgroup
-        const int64_t rc_begin = s_me * a.sb_slots;
-        const int64_t nrc = slot_begin - rc_begin;
-        const rsrc_t ri = make_rsrc(a.ids + rc_begin, (uint32_t)(nrc * 4));
-        for (int64_t b0 = 0; b0 < nrc; b0 += (int64_t)NT * kBatch) {
-            int32_t id[kBatch];
+    }
+    // recount of this superblock's slots before the workgroup
+    for (int64_t b0 = 0; b0 < nrc; b0 += (int64_t)NT * kBatch) {
+        if (b0 > 0) {
 #pragma unroll
             for (int q = 0; q < kBatch; ++q)
-                id[q] = buf_ld4(ri, (uint32_t)(q * NT + tid) * 4u, (uint32_t)(b0 * 4));
+                id[q] = buf_ld4(r_rc, (uint32_t)(q * NT + tid) * 4u, (uint32_t)(b0 * 4));
+        }
 #pragma unroll
-            for (int q = 0; q < kBatch; ++q) {
-                const int32_t e = b0 + q * NT + tid < nrc ? local_expert(id[q], a.expert_begin, L) : -1;
-                if (e >= 0) atomicAdd(&cur[e], 1);
-            }
+        for (int q = 0; q < kBatch; ++q) {
+            const int32_t e = b0 + q * NT + tid < nrc ? local_expert(id[q], a.expert_begin, L) : -1;
+            if (e >= 0) atomicAdd(&cur[e], 1);
         }
     }
     __syncthreads();
@@ -571,7 +586,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
         if (wave == rw) {
             const int rel = r0 + lane;
             const int64_t i = slot_begin + rel;
-            const int32_t e = rel < nslots ? local_expert(a.ids[i], a.expert_begin, L) : -1;
+            const int32_t e = rel < nslots ? local_expert(my_id, a.expert_begin, L) : -1;
             uint64_t pending = __ballot(e >= 0);
             int32_t dst = -1;
             while (pending) {
