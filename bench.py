@@ -17,7 +17,8 @@ Reported (one JSON line on stdout):
                definition / measured step time), unit GB/s
   tokens_per_s T / step time
   roofline     the dominant kernel (combine): algorithmic bytes per launch /
-               its average launch time from HIP events on the launch stream,
+               its average duration inside the timed step loop, from HIP
+               events carried by the combine's own launch (cdl_combine_timed),
                against the 8 TB/s HBM3E peak; `traffic` = HBM bytes per launch
                from rocprofv3 FETCH_SIZE + WRITE_SIZE when a summary taken on
                the current kernel source is committed, else null
@@ -163,6 +164,15 @@ class NormalSet:
         if rc:
             raise RuntimeError("cdl_combine failed: %d" % rc)
 
+    def combine_timed(self, start, stop):
+        """The combine with its kernel's own begin / end recorded into two
+        torch.cuda.Event objects (created with enable_timing)."""
+        P = ctypes.c_void_p
+        a = self.a_combine
+        rc = self.lib.cdl_combine_timed(*a[:-1], P(start.cuda_event), P(stop.cuda_event), a[-1])
+        if rc:
+            raise RuntimeError("cdl_combine_timed failed: %d" % rc)
+
     def permute(self):
         rc = self.lib.cdl_permute(*self.a_permute)
         if rc:
@@ -215,26 +225,33 @@ def time_steps(torch, sets, fn, steps, warmup):
 
 
 def time_kernels(torch, sets, steps, warmup):
-    """Per-call average time (µs) from HIP events recorded on the launch
-    stream around the permute (two kernels) and the combine of each step."""
+    """The combine kernel's average duration inside the timed step loop: its
+    launch carries two HIP events that receive the kernel's own begin and end
+    (cdl_combine_timed), so nothing is added to the stream between the
+    kernels.  Also returns the mean step time of that same loop, to show the
+    events do not perturb it."""
     n = len(sets)
     for i in range(warmup):
         sets[i % n].step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:             # torch creates the HIP event at its first record
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
     for i in range(steps):
         s = sets[i % n]
-        e = ev[i]
-        e[0].record()
         s.permute()
-        e[1].record()
-        s.combine()
-        e[2].record()
+        s.combine_timed(*ev[i])
+    end.record()
     torch.cuda.synchronize()
-    per = [e[0].elapsed_time(e[1]) * 1e3 for e in ev]
-    com = [e[1].elapsed_time(e[2]) * 1e3 for e in ev]
-    return {"permute_us": statistics.mean(per), "combine_us": statistics.mean(com),
-            "permute_us_median": statistics.median(per), "combine_us_median": statistics.median(com)}
+    com = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    return {"combine_us": statistics.mean(com), "combine_us_median": statistics.median(com),
+            "step_us_same_loop": start.elapsed_time(end) * 1e3 / steps}
 
 
 # ---------------------------------------------------------------------------

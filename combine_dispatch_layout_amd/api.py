@@ -94,6 +94,8 @@ def library():
         L.cdl_dispatch_ll.restype = ctypes.c_int
         L.cdl_combine.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, vp, vp]
         L.cdl_combine.restype = ctypes.c_int
+        L.cdl_combine_timed.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, vp, vp, vp, vp]
+        L.cdl_combine_timed.restype = ctypes.c_int
         L.cdl_ll_expected_m.argtypes = [i64, i32, i32, i32]
         L.cdl_ll_expected_m.restype = i64
         L.cdl_status_string.argtypes = [ctypes.c_int]

@@ -26,6 +26,7 @@
 //     finds them in the Infinity Cache; the combine loads and stores
 //     non-temporally (measured fastest of the policy combinations).
 //   * Routing indices are wave-uniform and are kept in scalar registers.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1331,9 +1332,9 @@ int cdl_dispatch_ll_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
     return launch_status();
 }
 
-int cdl_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32_t *map,
-                const float *topk_weights, int64_t T, int32_t k, uint16_t *out, int32_t *status,
-                void *stream)
+static int run_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32_t *map,
+                       const float *topk_weights, int64_t T, int32_t k, uint16_t *out,
+                       int32_t *status, hipEvent_t start, hipEvent_t stop, void *stream)
 {
     int rc = check_tk(T, k);
     if (rc != CDL_OK) return rc;
@@ -1344,13 +1345,30 @@ int cdl_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32_t *map
     if (y_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
     hipStream_t s = (hipStream_t)stream;
     if (H % 8 == 0 && aligned(y, 16) && aligned(out, 16)) {
-        combine_rows_v16<<<dim3((unsigned)T), dim3(kCombThreads), 0, s>>>(
-            (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k, (u32x4 *)out, status);
+        // with events: the launch itself carries them (no extra queue packets)
+        hipExtLaunchKernelGGL(combine_rows_v16, dim3((unsigned)T), dim3(kCombThreads), 0, s, start, stop,
+                              0, (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k, (u32x4 *)out,
+                              status);
     } else {
-        combine_rows_u16<<<dim3((unsigned)T), dim3(128), 0, s>>>(y, y_rows, H, map, topk_weights,
-                                                                  k, out, status);
+        hipExtLaunchKernelGGL(combine_rows_u16, dim3((unsigned)T), dim3(128), 0, s, start, stop, 0, y,
+                              y_rows, H, map, topk_weights, k, out, status);
     }
     return launch_status();
+}
+
+int cdl_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32_t *map,
+                const float *topk_weights, int64_t T, int32_t k, uint16_t *out, int32_t *status,
+                void *stream)
+{
+    return run_combine(y, y_rows, H, map, topk_weights, T, k, out, status, nullptr, nullptr, stream);
+}
+
+int cdl_combine_timed(const uint16_t *y, int64_t y_rows, int64_t H, const int32_t *map,
+                      const float *topk_weights, int64_t T, int32_t k, uint16_t *out,
+                      int32_t *status, void *start_event, void *stop_event, void *stream)
+{
+    return run_combine(y, y_rows, H, map, topk_weights, T, k, out, status, (hipEvent_t)start_event,
+                       (hipEvent_t)stop_event, stream);
 }
 
 int64_t cdl_ll_expected_m(int64_t T, int32_t num_ranks, int32_t k, int32_t E)

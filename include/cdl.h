@@ -360,6 +360,19 @@ int cdl_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32_t *map
                 int32_t *status, void *stream);
 
 /*
+ * cdl_combine_timed -- cdl_combine whose kernel launch carries two events
+ * for measurement: start_event and stop_event (hipEvent_t created with
+ * timing enabled, either may be NULL) receive the begin and end of the
+ * combine kernel itself, so hipEventElapsedTime between them is the
+ * kernel's duration, without the extra queue packets (and the dependency
+ * round trips) that a separate event record adds between kernels.  Results
+ * and errors are those of cdl_combine.
+ */
+int cdl_combine_timed(const uint16_t *y, int64_t y_rows, int64_t H, const int32_t *map,
+                      const float *topk_weights, int64_t T, int32_t k, uint16_t *out,
+                      int32_t *status, void *start_event, void *stop_event, void *stream);
+
+/*
  * cdl_ll_expected_m -- host-side hint for the masked grouped GEMM after a
  * low-latency dispatch ([deepep.py], _DeepEPDispatcherImplLowLatency.dispatch_a):
  * (T * num_ranks * k + E) / E with integer division.  Returns -1 for E <= 0 or

@@ -329,6 +329,37 @@ def test_combine_map_range_flag():
     assert np.array_equal(bits16(out[1]), bits16(y[3]))
 
 
+@pytest.mark.parametrize("H", [7168, 200])
+def test_combine_timed_matches_combine(H):
+    """cdl_combine_timed: the same bits as cdl_combine (vector and element
+    paths), and its launch events hold the kernel's duration."""
+    import ctypes
+    announce("combine timed H=%d" % H)
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=900, H=H)
+    x, ids, wts = W.make_inputs(w)
+    _, s_, d, _ = oracle.layout(ids.numpy(), 0, w.L)
+    R = int(s_[-1])
+    y = torch.randn(R, H, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).to(DEV)
+    m = torch.from_numpy(d).to(DEV)
+    wd = wts.to(DEV)
+    ref = cdl.combine(y, m, wd)
+    out = torch.empty(w.T, H, dtype=torch.bfloat16, device=DEV)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    P = ctypes.c_void_p
+    rc = cdl.library().cdl_combine_timed(
+        P(y.data_ptr()), R, H, P(m.data_ptr()), P(wd.data_ptr()), w.T, w.k, P(out.data_ptr()),
+        None, P(e0.cuda_event), P(e1.cuda_event), P(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    torch.cuda.synchronize()
+    assert np.array_equal(bits16(out), bits16(ref))
+    want = oracle.combine(W.bf16_bits(y.cpu()), d, wts.numpy(), w.T, w.k)
+    assert np.array_equal(bits16(out), want)
+    assert e0.elapsed_time(e1) > 0
+
+
 def test_fp8_rejects_ragged_groups():
     ids = torch.zeros(2, 1, dtype=torch.int32, device=DEV)
     lay = cdl.dispatch_layout(ids, 0, 1)
@@ -352,7 +383,10 @@ def test_deterministic_repeats():
 # --------------------------------------------------------------------------
 
 PERMUTE = PARITY + [W.WORKLOADS["dsv3_prefill"], W.WORKLOADS["ll_decode"].scaled(mode="normal"),
-                    W.WORKLOADS["zipf_prefill"].scaled(T=5000, H=256)]
+                    W.WORKLOADS["zipf_prefill"].scaled(T=5000, H=256),
+                    # last workgroup only partly filled, expert 0 local: its
+                    # past-the-end waves must neither load nor store a row
+                    W.WORKLOADS["dsv3_prefill"].scaled(T=1001, H=512)]
 
 
 @pytest.mark.parametrize("w", PERMUTE, ids=lambda w: "%s_T%d_H%d_b%d" % (w.name, w.T, w.H, w.expert_begin))
@@ -388,6 +422,33 @@ def test_permute_default_capacity_and_repeat():
     assert torch.equal(out1[:R].view(torch.int16), out2[:R].view(torch.int16))
     _, s, d, _ = check_layout(lay1, ids, 0, w.L)
     assert np.array_equal(bits16(out1[:R]), oracle.dispatch(W.bf16_bits(x), d, w.k, R))
+
+
+def test_layout_workspace_reuse_across_shapes():
+    """One workspace, never initialised, serves a sequence of layouts and
+    permutes of different shapes (including T = 0 and T = 1); every call
+    matches the oracle."""
+    shapes = [W.WORKLOADS["dsv3_prefill"], W.WORKLOADS["tiny"],
+              W.WORKLOADS["zipf_prefill"].scaled(T=5000, H=256),
+              W.WORKLOADS["dsv3_prefill"].scaled(T=0), W.WORKLOADS["ll_decode"],
+              W.WORKLOADS["dsv3_prefill"].scaled(T=1), W.WORKLOADS["dsv3_prefill"]]
+    big = max(cdl.layout_workspace_size(w.T, w.k, w.L) for w in shapes)
+    ws = torch.full((big,), 0xA5, dtype=torch.uint8, device=DEV)
+    st = status_word()
+    for n, w in enumerate(shapes):
+        announce("workspace reuse %d: %s T=%d" % (n, w.name, w.T))
+        ids = W.make_topk_ids(w)
+        lay = cdl.dispatch_layout(ids.to(DEV), w.expert_begin, w.L, workspace=ws)
+        x = W.make_hidden(w) if w.T else torch.zeros(0, w.H, dtype=torch.bfloat16)
+        lay2, rows = cdl.permute(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, workspace=ws,
+                                 status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        _, s_, d, _ = check_layout(lay, ids, w.expert_begin, w.L)
+        check_layout(lay2, ids, w.expert_begin, w.L)
+        R = int(s_[-1])
+        if w.T:
+            assert np.array_equal(bits16(rows[:R]), oracle.dispatch(W.bf16_bits(x), d, w.k, R))
 
 
 def test_permute_rows_overflow_flag():
