@@ -136,23 +136,34 @@ __device__ __forceinline__ void set_status(int32_t *status, int32_t bit)
 // 16 lanes of a DPP row hold one group of 128 elements.
 // ---------------------------------------------------------------------------
 
-// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), which hold one
-// 128-element group: quad_perm swaps at distance 1 and 2 give each quad its
-// maximum, row_half_mirror pairs the two quads of each half row, row_mirror
-// the two halves.  Four VALU ops, no LDS traffic.
+// Group amax.  Magnitudes of floats order like their bit patterns, so the
+// maximum is taken on integers (no NaN canonicalisation, and the DPP moves
+// fuse into the max): per lane over the eight bf16 magnitudes in 16-bit
+// halves, then over the 16 lanes of a DPP row (lanes 16r .. 16r+15), which
+// hold one 128-element group: quad_perm swaps at distance 1 and 2 give each
+// quad its maximum, row_half_mirror pairs the two quads of each half row,
+// row_mirror the two halves.  About 12 VALU ops, no LDS traffic.
 template <int CTRL>
-__device__ __forceinline__ float dpp_max_step(float a)
+__device__ __forceinline__ uint32_t dpp_umax_step(uint32_t a)
 {
-    const int b = __builtin_amdgcn_update_dpp(0, __float_as_int(a), CTRL, 0xF, 0xF, false);
-    return fmaxf(a, __int_as_float(b));
+    const uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, 0xF, 0xF, false);
+    return a > b ? a : b;
 }
-__device__ __forceinline__ float row16_max(float a)
+__device__ __forceinline__ float group_amax(u32x4 v)
 {
-    a = dpp_max_step<0xB1>(a);    // quad_perm [1,0,3,2]
-    a = dpp_max_step<0x4E>(a);    // quad_perm [2,3,0,1]
-    a = dpp_max_step<0x141>(a);   // row_half_mirror
-    a = dpp_max_step<0x140>(a);   // row_mirror
-    return a;
+    using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+    const u16x2 m0 = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
+    const u16x2 m1 = __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu);
+    const u16x2 m2 = __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu);
+    const u16x2 m3 = __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu);
+    const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
+                                              __builtin_elementwise_max(m2, m3));
+    uint32_t a = (uint32_t)(m.x > m.y ? m.x : m.y) << 16;
+    a = dpp_umax_step<0xB1>(a);    // quad_perm [1,0,3,2]
+    a = dpp_umax_step<0x4E>(a);    // quad_perm [2,3,0,1]
+    a = dpp_umax_step<0x141>(a);   // row_half_mirror
+    a = dpp_umax_step<0x140>(a);   // row_mirror
+    return __uint_as_float(a);
 }
 
 // Groups with amax >= kFastQuotientMinAmax divide by the scale with one
@@ -161,8 +172,8 @@ __device__ __forceinline__ float row16_max(float a)
 // An exhaustive check over every bf16 amax and every bf16 x with |x| <= amax
 // (about 1.06e9 pairs, tests/fast_quotient_check.c) finds the e4m3fn code of
 // this quotient equal to that of the correctly rounded x / s whenever
-// amax >= 3.3e-32; below 2^-96 the element-wise division is kept.  x = +-0 keeps its sign explicitly (the
-// correction step would return +0).
+// amax >= 3.3e-32; below 2^-96 the element-wise division is kept.  copysign
+// keeps the sign of x = +-0 (the correction step would return +0).
 constexpr float kFastQuotientMinAmax = 0x1p-96f;
 
 // Returns the 8 e4m3fn bytes of the chunk; *scale receives the group scale
@@ -176,10 +187,7 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, bool ue8m0, float *scale, 
 {
     float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                   bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(f[e]));
-    a = row16_max(a);
+    const float a = group_amax(v);
     if (ue8m0) {
         int ex = 0;
         const float m = frexpf(a, &ex);
@@ -195,22 +203,29 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, bool ue8m0, float *scale, 
         return u32x2{lo, hi};
     }
     *scale_exp = 0;
-    const float s = a / 448.0f;                 // correctly rounded binary32 division
+    float s;
     float q[8];
     if (a >= kFastQuotientMinAmax) {
-        const float y = 1.0f / s;               // correctly rounded reciprocal
+        // s = fl(a / 448) = fl((a * 2^-6) / 7) by one correction step with
+        // fl(1/7); y = fl(1 / s) by one correction step from v_rcp_f32 (within
+        // 1 ulp); both exact for every bf16 a >= 2^-96 (exhaustive CPU check)
+        const float c7 = 1.0f / 7.0f;
+        const float t = a * 0x1p-6f;
+        const float s0 = t * c7;
+        s = fmaf(fmaf(-s0, 7.0f, t), c7, s0);
+        const float r0 = __builtin_amdgcn_rcpf(s);
+        const float y = fmaf(fmaf(-s, r0, 1.0f), r0, r0);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float q0 = f[e] * y;
-            const float q1 = fmaf(fmaf(-q0, s, f[e]), y, q0);
-            q[e] = f[e] == 0.0f ? f[e] : q1;
+            // clamp the magnitude, then take the sign of x
+            q[e] = copysignf(fminf(fabsf(fmaf(fmaf(-q0, s, f[e]), y, q0)), 448.0f), f[e]);
         }
     } else {
+        s = a / 448.0f;                         // correctly rounded binary32 division
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = a > 0.0f ? f[e] / s : f[e];
+        for (int e = 0; e < 8; ++e) q[e] = fminf(fmaxf(a > 0.0f ? f[e] / s : f[e], -448.0f), 448.0f);
     }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] = fminf(fmaxf(q[e], -448.0f), 448.0f);
     const uint32_t lo = pack2_e4m3(q[0], q[1]) | (pack2_e4m3(q[2], q[3]) << 16);
     const uint32_t hi = pack2_e4m3(q[4], q[5]) | (pack2_e4m3(q[6], q[7]) << 16);
     *scale = s;
@@ -254,8 +269,8 @@ __device__ __forceinline__ void put_scale(const Fp8Out &o, int64_t row, int64_t 
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxChunks = 16;          // 16-byte chunks a lane holds per pass (bf16 rows)
-constexpr int kMaxChunksFp8 = 8;        // the same for rows quantised on the way: fewer live
-                                        // registers for the quantisation temporaries
+constexpr int kMaxChunksFp8 = 14;       // the same for rows quantised on the way (one pass at
+                                        // H = 7168; quantised kFp8Part chunks at a time)
 constexpr int kCountThreads = 256;
 
 struct Plan {
@@ -380,6 +395,43 @@ __device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], int k, int
                 if (c < chunks) put_scale(o, dst, c >> 4, sc[u], ex[u]);
             }
         }
+    }
+}
+
+// All chunks of a pass, kFp8Part at a time, with at most kFp8Ahead parts of
+// loads in flight: the caller loads the first kFp8Ahead parts, and the loads
+// of part p + kFp8Ahead are issued once part p is stored.  If every wave
+// asked for its whole row at once, the rows would all arrive near the end of
+// the read phase and the waves would then quantise together and store
+// together; with a short window the three phases overlap.
+constexpr int kFp8Part = 3;
+constexpr int kFp8Ahead = 1;
+template <int NCH>
+__device__ __forceinline__ void load_fp8_part(u32x4 (&v)[NCH], int part, rsrc_t xr, uint32_t voff,
+                                              uint32_t pass)
+{
+#pragma unroll
+    for (int u = 0; u < NCH; ++u)
+        if (u / kFp8Part == part) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+}
+template <int NCH>
+__device__ __forceinline__ void load_fp8_first_parts(u32x4 (&v)[NCH], rsrc_t xr, uint32_t voff, uint32_t pass)
+{
+#pragma unroll
+    for (int u = 0; u < NCH; ++u)
+        if (u < kFp8Ahead * kFp8Part) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+}
+template <int U0, int NCH, typename DstFn>
+__device__ __forceinline__ void store_fp8_parts(u32x4 (&v)[NCH], int k, int lane, int64_t c0,
+                                                int64_t chunks, const Fp8Out &o, bool ue8m0,
+                                                DstFn dst_of, rsrc_t xr, uint32_t voff, uint32_t pass)
+{
+    if constexpr (U0 < NCH) {
+        constexpr int NQ = NCH - U0 < kFp8Part ? NCH - U0 : kFp8Part;
+        store_fp8_part<U0, NQ>(v, k, lane, c0, chunks, o, ue8m0, dst_of);
+        constexpr int next = U0 / kFp8Part + kFp8Ahead;
+        if constexpr (next * kFp8Part < NCH) load_fp8_part(v, next, xr, voff, pass);
+        store_fp8_parts<U0 + NQ>(v, k, lane, c0, chunks, o, ue8m0, dst_of, xr, voff, pass);
     }
 }
 
@@ -508,7 +560,9 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     const uint32_t row_bytes = (uint32_t)(a.chunks * 16);
     const uint32_t voff = (uint32_t)lane * 16u;
     const rsrc_t xr = make_rsrc(a.x + (tok_valid ? t * a.chunks : 0), row_bytes);
-    if (MODE != kLayoutOnly && tok_valid) {
+    if (MODE == kRowsFp8 && tok_valid) {
+        load_fp8_first_parts(v, xr, voff, 0);
+    } else if (MODE != kLayoutOnly && tok_valid) {
 #pragma unroll
         for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, u * kWave * 16);
     }
@@ -610,16 +664,20 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 
     // 4. rows
     if (MODE == kLayoutOnly || !tok_valid) return;
-    const int32_t *my = dsts + wave * k;
+    // lane j < k holds the destination of the token's slot j (readlane below:
+    // no memory access per destination)
+    const int32_t dlane = lane < k ? dsts[wave * k + lane] : -1;
     for (int64_t c0 = 0; c0 < a.chunks; c0 += (int64_t)NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
-        if (c0 > 0) {
+        if (c0 > 0 && MODE == kRowsFp8) {
+            load_fp8_first_parts(v, xr, voff, pass);
+        } else if (c0 > 0) {
 #pragma unroll
             for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         }
         if (MODE == kRowsBf16) {
             for (int j = 0; j < k; ++j) {
-                const int32_t dst = uniform(my[j]);
+                const int32_t dst = __builtin_amdgcn_readlane(dlane, j);
                 if (dst < 0) continue;
                 if ((int64_t)dst >= a.cap_rows) {
                     if (c0 == 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
@@ -631,7 +689,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
             }
         } else {
             auto dst_of = [&](int j, bool report) -> int64_t {
-                const int32_t d = uniform(my[j]);
+                const int32_t d = __builtin_amdgcn_readlane(dlane, j);
                 if (d < 0) return -1;
                 if ((int64_t)d >= a.cap_rows) {
                     if (report && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
@@ -640,8 +698,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
                 return d;
             };
             const bool ue8m0 = (a.fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            store_fp8_part<0, NC / 2>(v, k, lane, c0, a.chunks, a.fp8, ue8m0, dst_of);
-            store_fp8_part<NC / 2, NC / 2>(v, k, lane, c0, a.chunks, a.fp8, ue8m0, dst_of);
+            store_fp8_parts<0>(v, k, lane, c0, a.chunks, a.fp8, ue8m0, dst_of, xr, voff, pass);
         }
     }
 }
@@ -665,21 +722,25 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t t = (int64_t)blockIdx.x * kRowTok + wave_id();
     if (t >= T) return;
-    const int32_t *d = src2dst + t * k;
-    bool any = false;
-    for (int j = 0; j < k; ++j) any |= d[j] >= 0;
-    if (!any) return;
+    // lane j < k holds the destination of slot j: one load for all slots,
+    // then readlane per destination
+    const int32_t dlane = lane < k ? src2dst[t * k + lane] : -1;
+    if (__ballot(dlane >= 0) == 0) return;
     const uint32_t row_bytes = (uint32_t)(chunks * 16);
     const uint32_t voff = (uint32_t)lane * 16u;
     const rsrc_t xr = make_rsrc(x + t * chunks, row_bytes);
     for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
         u32x4 v[NC];
+        if (FP8) {
+            load_fp8_first_parts(v, xr, voff, pass);
+        } else {
 #pragma unroll
-        for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+            for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+        }
         if (FP8) {
             auto dst_of = [&](int j, bool report) -> int64_t {
-                const int32_t dd = d[j];
+                const int32_t dd = __builtin_amdgcn_readlane(dlane, j);
                 if (dd < 0) return -1;
                 if ((int64_t)dd >= cap_rows) {
                     if (report && lane == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
@@ -688,12 +749,11 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
                 return dd;
             };
             const bool ue8m0 = (fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            store_fp8_part<0, NC / 2>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of);
-            store_fp8_part<NC / 2, NC / 2>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of);
+            store_fp8_parts<0>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of, xr, voff, pass);
             continue;
         }
         for (int j = 0; j < k; ++j) {
-            const int32_t dst = d[j];
+            const int32_t dst = __builtin_amdgcn_readlane(dlane, j);
             if (dst < 0) continue;
             if (dst >= cap_rows) {
                 if (c0 == 0 && lane == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
@@ -833,39 +893,35 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t t = (int64_t)blockIdx.x * kRowTok + wave_id();
     if (t >= T) return;
-    bool any = false;
-    for (int j = 0; j < k; ++j) {
-        const int64_t i = t * k + j;
-        bool ovf;
-        const int64_t row = ll_row(ids, expert_begin, L, src2dst, seg_indptr, cap, i, &ovf);
-        if (lane == 0) {
-            ll_src2dst[i] = (int32_t)row;
-            if (ovf) set_status(status, CDL_STATUS_LL_OVERFLOW);
-        }
-        any |= row >= 0;
-    }
-    if (!any) return;
+    // lane j < k computes the padded-buffer row of slot j (one dependent load
+    // chain for all slots); readlane gives it to the whole wave below
+    bool ovf = false;
+    const int32_t rlane = lane < k ? (int32_t)ll_row(ids, expert_begin, L, src2dst, seg_indptr, cap,
+                                                     t * k + lane, &ovf)
+                                   : -1;
+    if (lane < k) ll_src2dst[t * k + lane] = rlane;
+    if (__ballot(ovf) != 0 && lane == 0) set_status(status, CDL_STATUS_LL_OVERFLOW);
+    if (__ballot(rlane >= 0) == 0) return;
     const uint32_t row_bytes = (uint32_t)(chunks * 16);
     const uint32_t voff = (uint32_t)lane * 16u;
     const rsrc_t xr = make_rsrc(x + t * chunks, row_bytes);
     for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
         u32x4 v[NC];
-#pragma unroll
-        for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         if (FP8) {
-            auto dst_of = [&](int j, bool) -> int64_t {
-                bool ovf;
-                return ll_row(ids, expert_begin, L, src2dst, seg_indptr, cap, t * k + j, &ovf);
-            };
+            load_fp8_first_parts(v, xr, voff, pass);
+        } else {
+#pragma unroll
+            for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+        }
+        if (FP8) {
+            auto dst_of = [&](int j, bool) -> int64_t { return __builtin_amdgcn_readlane(rlane, j); };
             const bool ue8m0 = (fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            store_fp8_part<0, NC / 2>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of);
-            store_fp8_part<NC / 2, NC / 2>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of);
+            store_fp8_parts<0>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of, xr, voff, pass);
             continue;
         }
         for (int j = 0; j < k; ++j) {
-            bool ovf;
-            const int64_t row = ll_row(ids, expert_begin, L, src2dst, seg_indptr, cap, t * k + j, &ovf);
+            const int64_t row = __builtin_amdgcn_readlane(rlane, j);
             if (row < 0) continue;
             const rsrc_t o = make_rsrc(out + row * chunks, row_bytes);
 #pragma unroll

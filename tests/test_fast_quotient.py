@@ -1,6 +1,7 @@
-"""The fp8 kernels' fast quotient gives the same e4m3fn code as x / s for
-every group they apply it to (exhaustive over bf16 inputs; CPU only, about
-half a minute)."""
+"""The fp8 kernels' division-free group arithmetic (scale, reciprocal and
+quotient) gives the correctly rounded scale and reciprocal and the same
+e4m3fn codes as x / s for every group it is applied to (exhaustive over bf16
+inputs; CPU only, about a minute)."""
 import os
 import subprocess
 
