@@ -311,20 +311,31 @@ def measure_ll(torch, cdl, W, dev, steps):
                 P(llm.data_ptr()), P(base.status.data_ptr()), base.stream)
         a_cb = (P(B.data_ptr()), w.L * w.cap, w.H, P(llm.data_ptr()), P(base.wts.data_ptr()),
                 w.T, w.k, P(base.out.data_ptr()), P(base.status.data_ptr()), base.stream)
-        runs.append((base, a_ll, a_cb, B, mm, llm))
+        a_pll = (P(base.x.data_ptr()), w.T, w.H, w.k, P(base.ids.data_ptr()), w.expert_begin, w.L,
+                 P(base.counts.data_ptr()), P(base.seg.data_ptr()), P(base.src2dst.data_ptr()),
+                 P(base.reorder.data_ptr()), base.reorder.numel(), w.cap, P(B.data_ptr()),
+                 P(mm.data_ptr()), P(llm.data_ptr()), P(base.status.data_ptr()),
+                 P(base.ws.data_ptr()), base.ws.numel(), base.stream)
+        runs.append((base, a_ll, a_cb, B, mm, llm, a_pll))
 
     def fn(r):
+        if lib.cdl_permute_ll(*r[6]) or lib.cdl_combine(*r[2]):
+            raise RuntimeError("low-latency step failed")
+
+    def fn_separate(r):
         r[0].layout()
         if lib.cdl_dispatch_ll(*r[1]) or lib.cdl_combine(*r[2]):
             raise RuntimeError("low-latency step failed")
 
     ms, _ = time_steps(torch, runs, fn, steps, 5)
+    ms_sep, _ = time_steps(torch, runs, fn_separate, steps, 5)
     b = runs[0][0]
     byts = (b.bytes_layout() + 4 * w.L + 4 * w.T * w.k + 2 * b.U * w.H + 2 * b.R * w.H
             + b.bytes_combine())
     return {"workload": "ll_decode (T=128, H=7168, 32 of 256 experts, top-8, cap 1024; "
-                        "layout + padded dispatch + combine)",
+                        "layout + padded dispatch (one call) + combine)",
             "us_per_step": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9,
+            "us_per_step_separate_calls": ms_sep * 1e3,
             "expected_m": cdl.ll_expected_m(w.T, w.num_ranks, w.k, w.E)}
 
 

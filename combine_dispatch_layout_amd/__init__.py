@@ -28,6 +28,8 @@ from .api import (  # noqa: F401
     library,
     ll_expected_m,
     permute,
+    permute_ll,
+    permute_ll_fp8,
     permute_fp8,
     rank_layout,
     RankLayout,

@@ -91,6 +91,12 @@ def library():
         L.cdl_dispatch_fp8.restype = ctypes.c_int
         L.cdl_dispatch_ll.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, i64, vp, vp,
                                       vp, vp, vp]
+        L.cdl_permute_ll.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, vp, i64, i64, vp,
+                                     vp, vp, vp, vp, sz, vp]
+        L.cdl_permute_ll.restype = ctypes.c_int
+        L.cdl_permute_ll_fp8.argtypes = [vp, i64, i64, i32, vp, i32, i32, vp, vp, vp, vp, i64, i64,
+                                         vp, vp, i32, vp, vp, vp, vp, sz, vp]
+        L.cdl_permute_ll_fp8.restype = ctypes.c_int
         L.cdl_dispatch_ll.restype = ctypes.c_int
         L.cdl_combine.argtypes = [vp, i64, i64, vp, vp, i64, i32, vp, vp, vp]
         L.cdl_combine.restype = ctypes.c_int
@@ -464,6 +470,71 @@ def dispatch_ll_fp8(x: torch.Tensor, layout: Layout, cap: int, scale_flags: int 
                                        _stream(x.device))
     _check(rc, "cdl_dispatch_ll_fp8")
     return out_q, out_scales, masked_m, ll_map
+
+
+def permute_ll(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
+               num_local_experts: int, cap: int, out: Optional[torch.Tensor] = None,
+               status: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """The low-latency dispatch in one call: layout + padded [L, cap, H]
+    scatter.  Returns (layout, out, masked_m, ll_src2dst)."""
+    _need(x, "x", torch.bfloat16)
+    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace, 1)
+    T, k, L = lay.T, lay.k, lay.num_local_experts
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T = %d" % T)
+    H = x.shape[1]
+    if out is None:
+        out = torch.empty(L, cap, H, dtype=torch.bfloat16, device=x.device)
+    _need(out, "out", torch.bfloat16, (L, cap, H))
+    masked_m = torch.empty(L, dtype=torch.int32, device=x.device)
+    ll_map = torch.empty(T * k, dtype=torch.int32, device=x.device)
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_permute_ll(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
+                                  _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
+                                  _ptr(lay.reorder_buf), lay.reorder_buf.numel(), int(cap),
+                                  _ptr(out), _ptr(masked_m), _ptr(ll_map), _ptr(status), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(x.device))
+    _check(rc, "cdl_permute_ll")
+    return lay, out, masked_m, ll_map
+
+
+def permute_ll_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
+                   num_local_experts: int, cap: int, scale_flags: int = 0,
+                   out_q: Optional[torch.Tensor] = None,
+                   out_scales: Optional[torch.Tensor] = None,
+                   status: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None):
+    """permute_ll with fp8 rows.  Returns (layout, q [L, cap, H] uint8,
+    scales, masked_m, ll_src2dst)."""
+    _need(x, "x", torch.bfloat16)
+    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace, 1)
+    T, k, L = lay.T, lay.k, lay.num_local_experts
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T = %d" % T)
+    H = x.shape[1]
+    if H % FP8_GROUP:
+        raise CdlError(-3, "permute_ll_fp8 (H must be a multiple of 128)")
+    if out_q is None:
+        out_q = torch.empty(L, cap, H, dtype=torch.uint8, device=x.device)
+    _need(out_q, "out_q", torch.uint8, (L, cap, H))
+    if out_scales is None:
+        out_scales = new_scale_tensor(L * cap, H, scale_flags, x.device, rows_per_mat=cap)
+        if not scale_flags & FP8_SCALE_COLMAJOR:
+            out_scales = out_scales.view(L, cap, -1)
+    _check_scale_buffer(out_scales, L * cap, H, scale_flags, cap)
+    masked_m = torch.empty(L, dtype=torch.int32, device=x.device)
+    ll_map = torch.empty(T * k, dtype=torch.int32, device=x.device)
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_permute_ll_fp8(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
+                                      _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
+                                      _ptr(lay.reorder_buf), lay.reorder_buf.numel(), int(cap),
+                                      _ptr(out_q), _ptr(out_scales), int(scale_flags),
+                                      _ptr(masked_m), _ptr(ll_map), _ptr(status), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(x.device))
+    _check(rc, "cdl_permute_ll_fp8")
+    return lay, out_q, out_scales, masked_m, ll_map
 
 
 def combine(y: torch.Tensor, map_: torch.Tensor, topk_weights: torch.Tensor,

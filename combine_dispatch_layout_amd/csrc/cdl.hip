@@ -439,7 +439,7 @@ __device__ __forceinline__ void store_fp8_parts(u32x4 (&v)[NCH], int k, int lane
 // layout kernel B (+ fused row scatter): the permute
 // ---------------------------------------------------------------------------
 
-enum PermuteMode { kLayoutOnly = 0, kRowsBf16 = 1, kRowsFp8 = 2 };
+enum PermuteMode { kLayoutOnly = 0, kRowsBf16 = 1, kRowsFp8 = 2, kRowsLL = 3, kRowsLLFp8 = 4 };
 
 // Block-wide exclusive scan of one int32 per thread (NW waves).
 template <int NW>
@@ -490,6 +490,12 @@ struct PermuteArgs {
     Fp8Out fp8;           // fp8 rows and scales
     int64_t cap_rows;
     int32_t *status;
+    // small batches: every workgroup counts all slots itself (no count kernel)
+    int32_t self_count;
+    // low-latency modes: rows go to [L, ll_cap, H]
+    int64_t ll_cap;
+    int32_t *masked_m;
+    int32_t *ll_src2dst;
 };
 
 // One workgroup per TPB tokens, one wave per token.
@@ -511,7 +517,9 @@ template <int TPB, int MODE>
 __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 {
     constexpr int NT = TPB * kWave;
-    constexpr int NC = MODE == kRowsFp8 ? kMaxChunksFp8 : kMaxChunks;
+    constexpr bool kFp8Mode = MODE == kRowsFp8 || MODE == kRowsLLFp8;
+    constexpr bool kLLMode = MODE == kRowsLL || MODE == kRowsLLFp8;
+    constexpr int NC = kFp8Mode ? kMaxChunksFp8 : kMaxChunks;
     extern __shared__ int32_t lds[];
     const int L = a.L;
     int32_t *tot = lds;
@@ -535,11 +543,15 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     //    order, so the offsets below wait only for those small loads while
     //    the row is still in flight.
     constexpr int kBatch = 8;
+    // self-counting: the first loop reads every id instead of superblock
+    // counts, and nothing is recounted
+    const bool self = a.self_count != 0;
+    const int64_t n_all = a.T * k;
     const int64_t s_me = blk / a.sbb;
-    const int64_t nsc = a.S * L;
+    const int64_t nsc = self ? n_all : a.S * L;
     const int64_t rc_begin = s_me * a.sb_slots;
-    const int64_t nrc = slot_begin - rc_begin;
-    const rsrc_t r_sc = make_rsrc(a.sb_counts, (uint32_t)(nsc * 4));
+    const int64_t nrc = self ? 0 : slot_begin - rc_begin;
+    const rsrc_t r_sc = self ? make_rsrc(a.ids, (uint32_t)(n_all * 4)) : make_rsrc(a.sb_counts, (uint32_t)(nsc * 4));
     const rsrc_t r_rc = make_rsrc(a.ids + rc_begin, (uint32_t)(nrc * 4));
     const rsrc_t r_my = make_rsrc(a.ids + slot_begin, (uint32_t)(nslots * 4));
     int32_t c[kBatch], id[kBatch];
@@ -560,11 +572,18 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     const uint32_t row_bytes = (uint32_t)(a.chunks * 16);
     const uint32_t voff = (uint32_t)lane * 16u;
     const rsrc_t xr = make_rsrc(a.x + (tok_valid ? t * a.chunks : 0), row_bytes);
-    if (MODE == kRowsFp8 && tok_valid) {
+    if (kFp8Mode && tok_valid) {
         load_fp8_first_parts(v, xr, voff, 0);
     } else if (MODE != kLayoutOnly && tok_valid) {
 #pragma unroll
         for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, u * kWave * 16);
+    }
+    // low latency: lane j < k holds the local expert of this wave's slot j
+    int32_t ll_e = -1;
+    if (kLLMode) {
+        const bool real = t < a.T;
+        const rsrc_t r_tok = make_rsrc(a.ids + (real ? t * k : 0), real ? (uint32_t)k * 4u : 0u);
+        ll_e = lane < k ? local_expert(buf_ld4(r_tok, (uint32_t)lane * 4u, 0), a.expert_begin, L) : -1;
     }
 
     // 1. totals and offsets before this workgroup
@@ -583,7 +602,13 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
             const int64_t idx = b0 + q * NT + tid;
-            if (idx < nsc && c[q]) {
+            if (self) {
+                const int32_t e = idx < nsc ? local_expert(c[q], a.expert_begin, L) : -1;
+                if (e >= 0) {
+                    atomicAdd(&tot[e], 1);
+                    if (idx < slot_begin) atomicAdd(&cur[e], 1);
+                }
+            } else if (idx < nsc && c[q]) {
                 const int e = (int)(idx % L);
                 atomicAdd(&tot[e], c[q]);
                 if (idx / L < s_me) atomicAdd(&cur[e], c[q]);
@@ -621,7 +646,9 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
             if (blk == 0) {
                 a.counts[e] = c;
                 a.seg_indptr[e] = excl;
+                if (kLLMode) a.masked_m[e] = (int32_t)((int64_t)c < a.ll_cap ? c : a.ll_cap);
             }
+            if (kLLMode) tot[e] = excl;          // segment start, for the padded rows
             cur[e] += excl;
             if (padded > c && (int64_t)(e % gridDim.x) == blk) {
                 for (int64_t r = excl + c; r < excl + padded && r < a.reorder_cap; ++r) a.reorder[r] = -1;
@@ -662,20 +689,38 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
         __syncthreads();
     }
 
-    // 4. rows
-    if (MODE == kLayoutOnly || !tok_valid) return;
-    // lane j < k holds the destination of the token's slot j (readlane below:
-    // no memory access per destination)
-    const int32_t dlane = lane < k ? dsts[wave * k + lane] : -1;
+    // 4. rows; lane j < k holds the destination of the token's slot j
+    //    (readlane below: no memory access per destination)
+    if (MODE == kLayoutOnly) return;
+    int32_t dlane = -1;
+    if (kLLMode) {
+        // padded-buffer row e * ll_cap + (dst - seg_indptr[e]); rows past the
+        // expert's capacity are dropped
+        bool ovf = false;
+        if (t < a.T && lane < k) {
+            const int32_t d = dsts[wave * k + lane];
+            if (d >= 0) {
+                const int64_t slot = (int64_t)d - tot[ll_e];
+                if (slot < a.ll_cap)
+                    dlane = (int32_t)(ll_e * a.ll_cap + slot);
+                else
+                    ovf = true;
+            }
+            a.ll_src2dst[t * k + lane] = dlane;
+        }
+        if (__ballot(ovf) != 0 && lane == 0) set_status(a.status, CDL_STATUS_LL_OVERFLOW);
+    }
+    if (!tok_valid) return;
+    if (!kLLMode) dlane = lane < k ? dsts[wave * k + lane] : -1;
     for (int64_t c0 = 0; c0 < a.chunks; c0 += (int64_t)NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
-        if (c0 > 0 && MODE == kRowsFp8) {
+        if (c0 > 0 && kFp8Mode) {
             load_fp8_first_parts(v, xr, voff, pass);
         } else if (c0 > 0) {
 #pragma unroll
             for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         }
-        if (MODE == kRowsBf16) {
+        if (!kFp8Mode) {
             for (int j = 0; j < k; ++j) {
                 const int32_t dst = __builtin_amdgcn_readlane(dlane, j);
                 if (dst < 0) continue;
@@ -1112,7 +1157,10 @@ int run_layout(PermuteArgs a, void *ws, hipStream_t s)
     a.S = p.S;
     a.sbb = p.sbb;
     a.sb_slots = p.sb_slots;
-    if (p.S > 0) {
+    // a batch of at most two id loads per thread of a permute workgroup is
+    // counted by every workgroup itself, without the count kernel
+    a.self_count = p.n <= (int64_t)16 * kWave * p.tpb ? 1 : 0;
+    if (p.S > 0 && !a.self_count) {
         layout_count_kernel<<<dim3((unsigned)p.S), dim3(kCountThreads), a.L * sizeof(int32_t), s>>>(
             a.ids, p.n, p.sb_slots, a.expert_begin, a.L, (int32_t *)ws);
         int rc = launch_status();
@@ -1345,6 +1393,66 @@ static int check_ll_args(const uint16_t *x, int64_t T, int64_t H, int32_t k,
     if (T > 0 && !aligned(x, 16)) return CDL_ERR_UNSUPPORTED;
     return CDL_OK;
 }
+
+// Layout and low-latency scatter in one call.
+static int permute_ll_common(PermuteArgs &a, const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                             const int32_t *topk_ids, int32_t L, int32_t *counts,
+                             int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
+                             int64_t reorder_cap, int64_t cap, const void *out, int32_t *masked_m,
+                             int32_t *ll_src2dst, const void *ws, size_t ws_bytes)
+{
+    int rc = check_layout_args(topk_ids, T, k, L, 1, counts, seg_indptr, src2dst, reorder_topk_ids,
+                               reorder_cap, ws, ws_bytes);
+    if (rc != CDL_OK) return rc;
+    rc = check_ll_args(x, T, H, k, topk_ids, L, src2dst, seg_indptr, counts, cap, out, masked_m,
+                       ll_src2dst);
+    if (rc != CDL_OK) return rc;
+    a.x = (const u32x4 *)x;
+    a.chunks = H / 8;
+    a.cap_rows = (int64_t)L * cap;
+    a.ll_cap = cap;
+    a.masked_m = masked_m;
+    a.ll_src2dst = ll_src2dst;
+    return CDL_OK;
+}
+
+int cdl_permute_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
+                   int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
+                   int32_t *src2dst, int32_t *reorder_topk_ids, int64_t reorder_cap, int64_t cap,
+                   uint16_t *out, int32_t *masked_m, int32_t *ll_src2dst, int32_t *status, void *ws,
+                   size_t ws_bytes, void *stream)
+{
+    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, 1, counts, seg_indptr, src2dst,
+                                reorder_topk_ids, reorder_cap, status);
+    int rc = permute_ll_common(a, x, T, H, k, topk_ids, L, counts, seg_indptr, src2dst,
+                               reorder_topk_ids, reorder_cap, cap, out, masked_m, ll_src2dst, ws,
+                               ws_bytes);
+    if (rc != CDL_OK) return rc;
+    if (cap > 0 && !aligned(out, 16)) return CDL_ERR_UNSUPPORTED;
+    a.out = (u32x4 *)out;
+    return run_layout<kRowsLL>(a, ws, (hipStream_t)stream);
+}
+
+int cdl_permute_ll_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                       const int32_t *topk_ids, int32_t expert_begin, int32_t L, int32_t *counts,
+                       int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
+                       int64_t reorder_cap, int64_t cap, uint8_t *out_q, void *out_scales,
+                       int32_t scale_flags, int32_t *masked_m, int32_t *ll_src2dst,
+                       int32_t *status, void *ws, size_t ws_bytes, void *stream)
+{
+    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, 1, counts, seg_indptr, src2dst,
+                                reorder_topk_ids, reorder_cap, status);
+    int rc = permute_ll_common(a, x, T, H, k, topk_ids, L, counts, seg_indptr, src2dst,
+                               reorder_topk_ids, reorder_cap, cap, out_q, masked_m, ll_src2dst, ws,
+                               ws_bytes);
+    if (rc != CDL_OK) return rc;
+    if (H % CDL_FP8_GROUP != 0 || !valid_scale_flags(scale_flags)) return CDL_ERR_UNSUPPORTED;
+    if (cap > 0 && !out_scales) return CDL_ERR_NULL_POINTER;
+    if (cap > 0 && (!aligned(out_q, 8) || !aligned(out_scales, 4))) return CDL_ERR_UNSUPPORTED;
+    a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap);
+    return run_layout<kRowsLLFp8>(a, ws, (hipStream_t)stream);
+}
+
 
 // one wave per token; at least enough workgroups to write masked_m
 static dim3 ll_grid(int64_t T, int32_t L)

@@ -115,6 +115,9 @@ size_t cdl_dispatch_layout_workspace_size(int64_t T, int32_t k, int32_t L);
  *                         its contents need no initialisation
  * T == 0 is allowed: counts and seg_indptr are zero-filled (as the pages'
  * empty-batch path), topk_ids/src2dst/reorder may be NULL.
+ * Two kernel launches: per-superblock counts, then the offsets and ranks;
+ * one for small batches (T*k up to 16 ids per thread of a layout workgroup,
+ * which then counts every slot itself).
  */
 int cdl_dispatch_layout(const int32_t *topk_ids, int64_t T, int32_t k,
                         int32_t expert_begin, int32_t L, int32_t *counts,
@@ -151,8 +154,9 @@ int cdl_dispatch_layout_aligned(const int32_t *topk_ids, int64_t T, int32_t k,
  * dispatcher's permute step ([0.4.4 diff],
  * _DeepEPDispatcherImplNormal._deepep_permute: preprocess the received top-k
  * ids into reorder_topk_ids / src2dst / seg_indptr, then copy every token row
- * to its destination rows).  Two kernel launches; the row loads are issued
- * before the layout arithmetic, inside the second.
+ * to its destination rows).  Two kernel launches (one for small batches:
+ * T*k up to 16 ids per thread of a layout workgroup); the row loads are
+ * issued before the layout arithmetic.
  *
  * Layout arguments and outputs are exactly those of
  * cdl_dispatch_layout_aligned (alignment 1 gives cdl_dispatch_layout's; same
@@ -319,6 +323,39 @@ int cdl_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k,
                     const int32_t *counts, int64_t cap, uint16_t *out,
                     int32_t *masked_m, int32_t *ll_src2dst, int32_t *status,
                     void *stream);
+
+/*
+ * cdl_permute_ll -- the low-latency dispatch in one call: the routing layout
+ * and the scatter into the padded per-expert buffer ([deepep.py],
+ * _DeepEPDispatcherImplLowLatency._dispatch_core: one low_latency_dispatch
+ * call returns the packed receive buffer and the per-expert counts).
+ *
+ * Outputs are exactly those of cdl_dispatch_layout (counts, seg_indptr,
+ * src2dst, and reorder_topk_ids if reorder_cap > 0; it may be NULL with
+ * reorder_cap 0) followed by cdl_dispatch_ll on them (out [L, cap, H] bf16,
+ * masked_m, ll_src2dst, CDL_STATUS_LL_OVERFLOW); ws as for
+ * cdl_dispatch_layout.  One kernel launch for small batches (T*k up to 16
+ * ids per thread of a layout workgroup, e.g. 128 tokens of top-8), two
+ * otherwise.  Requires H % 8 == 0 and 16-byte aligned x and out.
+ */
+int cdl_permute_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
+                   int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,
+                   int32_t *src2dst, int32_t *reorder_topk_ids, int64_t reorder_cap, int64_t cap,
+                   uint16_t *out, int32_t *masked_m, int32_t *ll_src2dst, int32_t *status, void *ws,
+                   size_t ws_bytes, void *stream);
+
+/*
+ * cdl_permute_ll_fp8 -- cdl_permute_ll with the fp8 rows and scales of
+ * cdl_dispatch_ll_fp8 (out_q [L, cap, H] E4M3FN bytes; out_scales in the
+ * scale_flags format for L*cap rows, every expert's cap rows one
+ * column-major matrix).  Requires H % 128 == 0.
+ */
+int cdl_permute_ll_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                       const int32_t *topk_ids, int32_t expert_begin, int32_t L, int32_t *counts,
+                       int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
+                       int64_t reorder_cap, int64_t cap, uint8_t *out_q, void *out_scales,
+                       int32_t scale_flags, int32_t *masked_m, int32_t *ll_src2dst,
+                       int32_t *status, void *ws, size_t ws_bytes, void *stream);
 
 /*
  * cdl_dispatch_ll_fp8 -- cdl_dispatch_ll with fp8 rows ([deepep.py],

@@ -150,6 +150,43 @@ def test_dispatch_ll_rejects():
     assert call(x=ctypes.c_void_p(0x1002)) == EUNSUP
 
 
+def test_permute_ll_rejects():
+    lib = cdl.library()
+    f = lib.cdl_permute_ll
+    names = ["x", "T", "H", "k", "ids", "b", "L", "counts", "seg", "s2d", "reorder", "rcap", "cap",
+             "out", "mm", "ll", "status", "ws", "wsb", "stream"]
+    args = [FAKE, 4, 256, 2, FAKE, 0, 8, FAKE, FAKE, FAKE, NULL, 0, 16, FAKE, FAKE, FAKE, NULL,
+            FAKE, 1 << 20, NULL]
+
+    def call(fn=f, extra=None, **over):
+        a = list(args)
+        for n, v in over.items():
+            a[names.index(n)] = v
+        if extra is not None:
+            a = a[:14] + extra + a[14:]
+        return fn(*a)
+
+    assert call(H=100) == EUNSUP
+    assert call(L=0) == ESIZE
+    assert call(cap=-1) == ESIZE
+    assert call(cap=1 << 28, L=16) == EBIG
+    assert call(mm=NULL) == ENULL
+    assert call(ll=NULL) == ENULL
+    assert call(out=NULL) == ENULL
+    assert call(counts=NULL) == ENULL
+    assert call(ws=NULL) == ENULL
+    assert call(wsb=8) == EWS
+    assert call(rcap=5) == ENULL                       # capacity without a buffer
+    assert call(x=ctypes.c_void_p(0x1002)) == EUNSUP
+    assert call(out=ctypes.c_void_p(0x1008)) == EUNSUP
+    g = lib.cdl_permute_ll_fp8
+    # the same arguments with out_scales and scale_flags after out_q
+    assert call(g, [FAKE, 0], H=200) == EUNSUP
+    assert call(g, [FAKE, 4]) == EUNSUP                # packed needs UE8M0
+    assert call(g, [NULL, 0]) == ENULL
+    assert call(g, [FAKE, 0], mm=NULL) == ENULL
+
+
 def test_combine_rejects():
     lib = cdl.library()
     f = lib.cdl_combine

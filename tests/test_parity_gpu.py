@@ -24,6 +24,8 @@ import oracle
 from combine_dispatch_layout_amd import workloads as W
 from gpu_util import DEV, announce, bf16_filled, bits16, npy, status_word, u8
 
+UE_, CM_, PK_ = cdl.FP8_SCALE_UE8M0, cdl.FP8_SCALE_COLMAJOR, cdl.FP8_SCALE_PACKED
+
 pytestmark = pytest.mark.gpu
 
 REL_TOL = 7.9e-3
@@ -184,6 +186,74 @@ def test_low_latency_parity(cap_mode):
                               OB.reshape(-1, w.H)[rows])
     want = oracle.combine(OB.reshape(-1, w.H), oll, wts.numpy(), w.T, w.k)
     assert np.array_equal(bits16(out), want)
+
+
+@pytest.mark.parametrize("case", ["full", "tight", "ragged_b32", "T0"])
+def test_permute_ll_parity(case):
+    """cdl_permute_ll (layout + padded scatter in one call) against the
+    oracle's layout and low-latency dispatch."""
+    w = W.WORKLOADS["ll_decode"]
+    if case == "tight":
+        w = w.scaled(T=96, H=512, cap=3)                       # forces overflow
+    elif case == "ragged_b32":
+        w = w.scaled(T=777, H=256, cap=300, expert_begin=32)   # several workgroups per token batch
+    elif case == "T0":
+        w = w.scaled(T=0, H=256)
+    announce("permute_ll %s T=%d H=%d cap=%d" % (case, w.T, w.H, w.cap))
+    ids = W.make_topk_ids(w)
+    x = W.make_hidden(w) if w.T else torch.zeros(0, w.H, dtype=torch.bfloat16)
+    st = status_word()
+    B = bf16_filled(w.L * w.cap, w.H, 0x7F7F).view(w.L, w.cap, w.H)
+    lay, B, mm, llmap = cdl.permute_ll(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, w.cap, out=B,
+                                       status=st)
+    torch.cuda.synchronize()
+    check_layout(lay, ids, w.expert_begin, w.L)
+    OB, omm, oll, ovf = oracle.dispatch_ll(W.bf16_bits(x), ids.numpy(), w.expert_begin, w.L, w.cap,
+                                           fill=0x7F7F)
+    assert np.array_equal(npy(mm), omm)
+    assert np.array_equal(npy(llmap), oll)
+    assert int(st.item()) == (cdl.CDL_STATUS_LL_OVERFLOW if ovf else 0)
+    assert np.array_equal(bits16(B.view(w.L * w.cap, w.H)), OB.reshape(-1, w.H))
+
+
+@pytest.mark.parametrize("flags,cap", [(0, 1024), (UE_ | CM_ | PK_, 1024), (UE_ | CM_, 5)])
+def test_permute_ll_fp8_parity(flags, cap):
+    w = W.WORKLOADS["ll_decode"]
+    if cap < 100:
+        w = w.scaled(T=100, H=512)
+    announce("permute_ll fp8 flags=%d cap=%d" % (flags, cap))
+    x, ids, wts = W.make_inputs(w)
+    Q, S, mm, ll, ovf = oracle.dispatch_ll_fp8(W.bf16_bits(x), ids.numpy(), w.expert_begin, w.L,
+                                               cap, flags, fill=0xEE)
+    q = torch.zeros(w.L, cap, w.H, dtype=torch.uint8, device=DEV)
+    sb = torch.full((max(S.size, 1),), 0xEE, dtype=torch.uint8, device=DEV)
+    st = status_word()
+    lay, q, sb, gmm, gll = cdl.permute_ll_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, cap,
+                                              scale_flags=flags, out_q=q, out_scales=sb, status=st)
+    torch.cuda.synchronize()
+    check_layout(lay, ids, w.expert_begin, w.L)
+    assert np.array_equal(npy(gmm), mm) and np.array_equal(npy(gll), ll)
+    assert (int(st.item()) != 0) == bool(ovf)
+    assert np.array_equal(u8(q).reshape(-1), Q.reshape(-1))
+    assert np.array_equal(sb.cpu().numpy().reshape(-1)[:S.size], S)
+
+
+@pytest.mark.parametrize("T,k", [(128, 8), (129, 8), (256, 8), (257, 8), (600, 2), (1024, 8),
+                                 (2048, 4), (2049, 4)])
+def test_layout_self_count_threshold(T, k):
+    """Batches just below and above the size where every layout workgroup
+    counts all slots itself (16 ids per thread) give the oracle's layout and
+    rows."""
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=T, k=k, H=64)
+    announce("self-count threshold T=%d k=%d" % (T, k))
+    x, ids, wts = W.make_inputs(w)
+    lay = cdl.dispatch_layout(ids.to(DEV), 0, w.L)
+    lay2, rows = cdl.permute(x.to(DEV), ids.to(DEV), 0, w.L)
+    torch.cuda.synchronize()
+    _, s_, d, _ = check_layout(lay, ids, 0, w.L)
+    check_layout(lay2, ids, 0, w.L)
+    R = int(s_[-1])
+    assert np.array_equal(bits16(rows[:R]), oracle.dispatch(W.bf16_bits(x), d, k, R))
 
 
 def test_full_size_dsv3_prefill():
