@@ -67,6 +67,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-modes", action="store_true",
                    help="skip the fp8 / low-latency / Zipf side measurements")
+    p.add_argument("--only", choices=["fp8_dispatch", "ll_decode", "zipf_prefill"],
+                   help="run just this side measurement and print its JSON (for profiling)")
     p.add_argument("--calibration-copy", type=int, default=0, metavar="MB",
                    help="first run 5 plain device copies of MB MiB (torch copy_), the "
                         "known-size reference for scaling rocprofv3 byte counters")
@@ -406,6 +408,18 @@ def main():
         torch.cuda.synchronize()
         log("calibration copies: 5 x %d bytes read + %d bytes written" % (nbytes, nbytes))
         del a, b
+    if args.only:
+        if args.only == "fp8_dispatch":
+            wf = W.WORKLOADS["fp8_dispatch"].scaled(mode="normal")
+            fsets = [NormalSet(torch, cdl, W, wf.scaled(seed_base=wf.seed_base + 7919 * i), dev)
+                     for i in range(args.sets)]
+            r = measure_fp8(torch, cdl, fsets, args.steps)
+        elif args.only == "ll_decode":
+            r = measure_ll(torch, cdl, W, dev, args.steps)
+        else:
+            r = measure_zipf(torch, cdl, W, dev, args.steps)
+        print(json.dumps({"only": args.only, **r}), flush=True)
+        return
     w = W.WORKLOADS[args.workload]
     if w.mode != "normal":
         raise SystemExit("the timed step is the normal-mode path; pick a normal workload")

@@ -272,6 +272,7 @@ constexpr int kMaxChunks = 16;          // 16-byte chunks a lane holds per pass 
 constexpr int kMaxChunksFp8 = 14;       // the same for rows quantised on the way (one pass at
                                         // H = 7168; quantised kFp8Part chunks at a time)
 constexpr int kCountThreads = 256;
+constexpr int kSelfCountIds = 8;        // ids per thread when workgroups count every slot
 
 struct Plan {
     int64_t n;            // slots, T * k
@@ -292,6 +293,11 @@ inline Plan make_plan(int64_t T, int32_t k, int32_t L)
     p.n = T * k;
     int tpb = 1;
     while (tpb < 8 && (T + tpb - 1) / tpb > 512) tpb *= 2;
+    // a batch small enough for every workgroup to count all of its slots:
+    // enough tokens per workgroup that the ids fit the one batch of loads
+    // issued before the rows (kSelfCountIds per thread)
+    if (p.n <= (int64_t)kSelfCountIds * kWave * 8)
+        while (p.n > (int64_t)kSelfCountIds * kWave * tpb) tpb *= 2;
     p.tpb = tpb;
     p.nblocks = (T + tpb - 1) / tpb;
     const int64_t bs = (int64_t)tpb * k;
@@ -1157,9 +1163,9 @@ int run_layout(PermuteArgs a, void *ws, hipStream_t s)
     a.S = p.S;
     a.sbb = p.sbb;
     a.sb_slots = p.sb_slots;
-    // a batch of at most two id loads per thread of a permute workgroup is
-    // counted by every workgroup itself, without the count kernel
-    a.self_count = p.n <= (int64_t)16 * kWave * p.tpb ? 1 : 0;
+    // a batch of at most kSelfCountIds ids per thread of a permute workgroup
+    // is counted by every workgroup itself, without the count kernel
+    a.self_count = p.n <= (int64_t)kSelfCountIds * kWave * p.tpb ? 1 : 0;
     if (p.S > 0 && !a.self_count) {
         layout_count_kernel<<<dim3((unsigned)p.S), dim3(kCountThreads), a.L * sizeof(int32_t), s>>>(
             a.ids, p.n, p.sb_slots, a.expert_begin, a.L, (int32_t *)ws);

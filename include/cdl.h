@@ -116,8 +116,8 @@ size_t cdl_dispatch_layout_workspace_size(int64_t T, int32_t k, int32_t L);
  * T == 0 is allowed: counts and seg_indptr are zero-filled (as the pages'
  * empty-batch path), topk_ids/src2dst/reorder may be NULL.
  * Two kernel launches: per-superblock counts, then the offsets and ranks;
- * one for small batches (T*k up to 16 ids per thread of a layout workgroup,
- * which then counts every slot itself).
+ * one for small batches (T*k <= 4096, where every layout workgroup counts
+ * all slots itself).
  */
 int cdl_dispatch_layout(const int32_t *topk_ids, int64_t T, int32_t k,
                         int32_t expert_begin, int32_t L, int32_t *counts,
@@ -154,9 +154,8 @@ int cdl_dispatch_layout_aligned(const int32_t *topk_ids, int64_t T, int32_t k,
  * dispatcher's permute step ([0.4.4 diff],
  * _DeepEPDispatcherImplNormal._deepep_permute: preprocess the received top-k
  * ids into reorder_topk_ids / src2dst / seg_indptr, then copy every token row
- * to its destination rows).  Two kernel launches (one for small batches:
- * T*k up to 16 ids per thread of a layout workgroup); the row loads are
- * issued before the layout arithmetic.
+ * to its destination rows).  Two kernel launches (one for small batches,
+ * T*k <= 4096); the row loads are issued before the layout arithmetic.
  *
  * Layout arguments and outputs are exactly those of
  * cdl_dispatch_layout_aligned (alignment 1 gives cdl_dispatch_layout's; same
@@ -334,9 +333,8 @@ int cdl_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k,
  * src2dst, and reorder_topk_ids if reorder_cap > 0; it may be NULL with
  * reorder_cap 0) followed by cdl_dispatch_ll on them (out [L, cap, H] bf16,
  * masked_m, ll_src2dst, CDL_STATUS_LL_OVERFLOW); ws as for
- * cdl_dispatch_layout.  One kernel launch for small batches (T*k up to 16
- * ids per thread of a layout workgroup, e.g. 128 tokens of top-8), two
- * otherwise.  Requires H % 8 == 0 and 16-byte aligned x and out.
+ * cdl_dispatch_layout.  One kernel launch for small batches (T*k <= 4096,
+ * e.g. 128 tokens of top-8), two otherwise.  Requires H % 8 == 0 and 16-byte aligned x and out.
  */
 int cdl_permute_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
                    int32_t expert_begin, int32_t L, int32_t *counts, int64_t *seg_indptr,

@@ -238,12 +238,12 @@ def test_permute_ll_fp8_parity(flags, cap):
     assert np.array_equal(sb.cpu().numpy().reshape(-1)[:S.size], S)
 
 
-@pytest.mark.parametrize("T,k", [(128, 8), (129, 8), (256, 8), (257, 8), (600, 2), (1024, 8),
-                                 (2048, 4), (2049, 4)])
+@pytest.mark.parametrize("T,k", [(1, 8), (64, 8), (128, 8), (129, 8), (600, 2), (512, 8), (513, 8),
+                                 (1024, 4), (1025, 4), (2048, 2), (2049, 2)])
 def test_layout_self_count_threshold(T, k):
-    """Batches just below and above the size where every layout workgroup
-    counts all slots itself (16 ids per thread) give the oracle's layout and
-    rows."""
+    """Batches just below and above the size (T*k = 4096) up to which every
+    layout workgroup counts all slots itself, and the sizes where its tokens
+    per workgroup change, give the oracle's layout and rows."""
     w = W.WORKLOADS["dsv3_prefill"].scaled(T=T, k=k, H=64)
     announce("self-count threshold T=%d k=%d" % (T, k))
     x, ids, wts = W.make_inputs(w)
