@@ -359,6 +359,17 @@ def measure_zipf(torch, cdl, W, dev, steps):
 # CPU baseline (the oracle as it stands)
 # ---------------------------------------------------------------------------
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(W, s, budget_s=12.0, max_reps=8):
     import numpy as np  # noqa: F401
     import oracle
@@ -366,19 +377,59 @@ def cpu_baseline(W, s, budget_s=12.0, max_reps=8):
     xb = W.bf16_bits(s.x_host)
     ids = s.ids_host.numpy()
     wts = s.w_host.numpy()
-    times = []
+    times, parts = [], []
     t_start = time.perf_counter()
     while len(times) < max_reps and (not times or time.perf_counter() - t_start < budget_s):
         t0 = time.perf_counter()
         c, seg, d, r = oracle.layout(ids, 0, s.L)
+        t1 = time.perf_counter()
         P = oracle.dispatch(xb, d, s.k, int(seg[-1]))
+        t2 = time.perf_counter()
         oracle.combine(P, d, wts, s.T, s.k)
-        times.append(time.perf_counter() - t0)
+        t3 = time.perf_counter()
+        times.append(t3 - t0)
+        parts.append((t1 - t0, t2 - t1, t3 - t2))
     t = statistics.median(times)
     return {"value": s.bytes_step() / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "tokens_per_s": s.T / t, "ms_per_step": t * 1e3,
+            "ms_layout_dispatch_combine": [round(statistics.median(p[i] for p in parts) * 1e3, 3)
+                                           for i in range(3)],
+            "cpu_model": cpu_model(),
             "sample": "%d full steps (layout+dispatch+combine) of the same T=%d workload, "
                       "single-threaded C oracle, median" % (len(times), s.T)}
+
+
+def step_spread(torch, sets, fn, steps, warmup, loops=10):
+    """Median, p10 and p90 (us) of the mean step time of `loops` separate
+    loops of steps // loops steps each (no event inside a loop)."""
+    per = max(steps // loops, 1)
+    vals = sorted(time_steps(torch, sets, fn, per, warmup if i == 0 else 2)[0] * 1e3
+                  for i in range(loops))
+    q = lambda f: vals[min(int(f * (len(vals) - 1) + 0.5), len(vals) - 1)]
+    return {"loops": loops, "steps_per_loop": per, "p10_us": round(q(0.1), 3),
+            "median_us": round(q(0.5), 3), "p90_us": round(q(0.9), 3)}
+
+
+def copy_ceiling(torch, dev, step_bytes, sets=6, reps=50):
+    """A device-to-device copy moving the step's algorithmic bytes (half read,
+    half written), rotating `sets` buffer pairs so no copy finds its source in
+    the Infinity Cache: its GB/s is the achievable ceiling of this part."""
+    n = int(step_bytes // 2) // 16 * 16
+    pairs = [(torch.empty(n, dtype=torch.uint8, device=dev).fill_(i + 1),
+              torch.empty(n, dtype=torch.uint8, device=dev)) for i in range(sets)]
+    ms, _ = time_steps(torch, pairs, lambda p: p[1].copy_(p[0]), reps, 5)
+    del pairs
+    torch.cuda.empty_cache()
+    return {"bytes_moved": 2 * n, "us": round(ms * 1e3, 3), "gbps": round(2 * n / (ms * 1e-3) / 1e9, 2)}
+
+
+def inputs_digest(torch, s):
+    import hashlib as hl
+    h = {}
+    for name, t in (("hidden_bf16", s.x_host), ("topk_ids", s.ids_host), ("topk_weights", s.w_host)):
+        h[name] = hl.sha256(t.contiguous().view(torch.uint8).numpy().tobytes()).hexdigest()[:16]
+    h["torch"] = torch.__version__
+    return h
 
 
 # ---------------------------------------------------------------------------
@@ -432,6 +483,7 @@ def main():
     log("cold step: %.2f us (wall %.2f us)" % (ms * 1e3, wall_ms * 1e3))
     warm_ms, _ = time_steps(torch, sets[:1], NormalSet.step, args.steps, args.warmup)
     unfused_ms, _ = time_steps(torch, sets, NormalSet.step_unfused, args.steps, args.warmup)
+    spread = step_spread(torch, sets, NormalSet.step, args.steps, args.warmup)
     kern = time_kernels(torch, sets, args.steps, args.warmup)
     log("kernels: %s" % kern)
     st = int(sum(int(s.status.item()) for s in sets))
@@ -443,6 +495,7 @@ def main():
     comb_bytes = statistics.mean(s.bytes_combine() for s in sets)
     comb_gbps = comb_bytes / (kern["combine_us"] * 1e-6) / 1e9
     traffic = committed_traffic()
+    ceiling = copy_ceiling(torch, dev, step_bytes)
 
     result = {
         "metric": METRIC,
@@ -463,6 +516,9 @@ def main():
         "tokens_per_s": round(w.T / (ms * 1e-3), 1),
         "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
         "algorithmic_bytes_per_step": int(step_bytes),
+        "step_spread": spread,
+        "copy_ceiling": {**ceiling, "frac_of_copy": round(gbps / ceiling["gbps"], 4)},
+        "inputs_sha256": inputs_digest(torch, sets[0]),
         "warm_single_set": {"ms_per_step": round(warm_ms, 6),
                             "gbps": round(step_bytes / (warm_ms * 1e-3) / 1e9, 2)},
         "unfused_step": {"ms_per_step": round(unfused_ms, 6),
