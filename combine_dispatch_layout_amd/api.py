@@ -223,7 +223,7 @@ def permute(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int, num_loca
             status: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None,
             alignment: int = 1) -> Tuple[Layout, torch.Tensor]:
-    """Layout + normal-mode scatter in one call (two kernels).  `out` holds
+    """Layout + normal-mode scatter in one call (two kernels, one for T*k <= 4096).  `out` holds
     `rows` rows (default T*k + L*(alignment-1), an upper bound on R); the
     first R rows receive the dispatched rows (padding rows are not written).
     Returns (layout, out)."""
