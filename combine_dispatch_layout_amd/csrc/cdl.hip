@@ -73,13 +73,13 @@ __device__ __forceinline__ void buf_st16_stream(rsrc_t r, u32x4 v, uint32_t voff
 {
     __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, kPolicyNT);
 }
-__device__ __forceinline__ void buf_st8(rsrc_t r, u32x2 v, uint32_t voff, uint32_t soff)
+__device__ __forceinline__ void buf_st8_stream(rsrc_t r, u32x2 v, uint32_t voff, uint32_t soff)
 {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, kPolicyNT);
 }
-__device__ __forceinline__ void buf_st4(rsrc_t r, float v, uint32_t voff, uint32_t soff)
+__device__ __forceinline__ void buf_st4_stream(rsrc_t r, float v, uint32_t voff, uint32_t soff)
 {
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, kPolicyNT);
 }
 __device__ __forceinline__ int32_t buf_ld4(rsrc_t r, uint32_t voff, uint32_t soff)
 {
@@ -365,6 +365,11 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
 // time while all of the pass's loads were issued together.  dst_of(j, first)
 // returns -1 to skip a slot; `first` is true for the first part of the first
 // pass, where capacity faults are reported.
+// fp8 rows and scales are stored non-temporally: nothing in this library
+// reads them back (unlike the bf16 permuted rows, which the combine re-reads
+// from the Infinity Cache), and back-to-back fp8 dispatches measured faster
+// without the dirty lines they would leave there (scatter 20.7 -> 18.9 us at
+// T = 4096, H = 7168).
 template <int U0, int NQ, int NCH, typename DstFn>
 __device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], int k, int lane, int64_t c0,
                                                int64_t chunks, const Fp8Out &o, bool ue8m0,
@@ -387,13 +392,13 @@ __device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], int k, int
         const rsrc_t oq = make_rsrc(o.q + dst * chunks, q_bytes);
 #pragma unroll
         for (int u = 0; u < NQ; ++u)
-            buf_st8(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + (U0 + u) * kWave * 8);
+            buf_st8_stream(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + (U0 + u) * kWave * 8);
         if (row_major_f32) {
             const rsrc_t os = make_rsrc(reinterpret_cast<float *>(o.s) + dst * (chunks / 16), s_bytes);
 #pragma unroll
             for (int u = 0; u < NQ; ++u)
                 if (group_head)
-                    buf_st4(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + (U0 + u) * 16);
+                    buf_st4_stream(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + (U0 + u) * 16);
         } else if (group_head) {
 #pragma unroll
             for (int u = 0; u < NQ; ++u) {
@@ -581,8 +586,10 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     if (kFp8Mode && tok_valid) {
         load_fp8_first_parts(v, xr, voff, 0);
     } else if (MODE != kLayoutOnly && tok_valid) {
+        // source rows are read once: streaming loads leave the Infinity Cache
+        // to the permuted rows, which the combine reads back
 #pragma unroll
-        for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, u * kWave * 16);
+        for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, u * kWave * 16);
     }
     // low latency: lane j < k holds the local expert of this wave's slot j
     int32_t ll_e = -1;
@@ -724,7 +731,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
             load_fp8_first_parts(v, xr, voff, pass);
         } else if (c0 > 0) {
 #pragma unroll
-            for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+            for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, pass + u * kWave * 16);
         }
         if (!kFp8Mode) {
             for (int j = 0; j < k; ++j) {
