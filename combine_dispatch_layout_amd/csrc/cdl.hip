@@ -993,7 +993,7 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
 // ---------------------------------------------------------------------------
 
 constexpr int kCombThreads = 128;
-constexpr int kCombUnroll = 8;       // chunks per lane per pass
+constexpr int kCombUnroll = 7;       // chunks per lane per pass: 7 x 128 = 896, one row at H = 7168
 
 // One workgroup per token.  acc = fma(w_j, y_j, acc) over the valid slots j in
 // ascending order from +0 (v_fma_f32 is correctly rounded), one bf16 rounding.
@@ -1003,8 +1003,11 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows_v16(
     int32_t *__restrict__ status)
 {
     const int64_t t = blockIdx.x;
-    const int32_t *m = map + t * k;
-    const float *w = wts + t * k;
+    // lane j < k of each wave holds slot j's row and weight (readlane below:
+    // no dependent load per slot)
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t mlane = lane < k ? map[t * k + lane] : -1;
+    const float wlane = lane < k ? wts[t * k + lane] : 0.0f;
     const uint32_t row_bytes = (uint32_t)(chunks * 16);
     const uint32_t voff = threadIdx.x * 16u;
     const rsrc_t orow = make_rsrc(out + t * chunks, row_bytes);
@@ -1016,13 +1019,13 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows_v16(
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
         for (int j = 0; j < k; ++j) {
-            const int32_t r = m[j];
+            const int32_t r = __builtin_amdgcn_readlane(mlane, j);
             if (r < 0) continue;
             if ((int64_t)r >= y_rows) {
                 if (c0 == 0 && threadIdx.x == 0) set_status(status, CDL_STATUS_MAP_RANGE);
                 continue;
             }
-            const float wj = w[j];
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), j));
             const rsrc_t yr = make_rsrc(y + (int64_t)r * chunks, row_bytes);
             u32x4 v[kCombUnroll];
 #pragma unroll
