@@ -268,7 +268,7 @@ __device__ __forceinline__ void put_scale(const Fp8Out &o, int64_t row, int64_t 
 // layout plan
 // ---------------------------------------------------------------------------
 
-constexpr int kMaxChunks = 16;          // 16-byte chunks a lane holds per pass (bf16 rows)
+constexpr int kMaxChunks = 14;          // 16-byte chunks a lane holds per pass (bf16 rows): 14 x 64 = 896, one row at H = 7168
 constexpr int kMaxChunksFp8 = 14;       // the same for rows quantised on the way (one pass at
                                         // H = 7168; quantised kFp8Part chunks at a time)
 constexpr int kCountThreads = 256;
