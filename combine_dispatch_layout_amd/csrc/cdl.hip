@@ -1252,6 +1252,7 @@ int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_
                                reorder_topk_ids, reorder_cap, ws, ws_bytes);
     if (rc != CDL_OK) return rc;
     if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
+    if (H > CDL_MAX_HIDDEN) return CDL_ERR_TOO_LARGE;
     if (cap_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
     if (T > 0 && !x) return CDL_ERR_NULL_POINTER;
     if (cap_rows > 0 && !out) return CDL_ERR_NULL_POINTER;
@@ -1283,6 +1284,7 @@ int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
                                reorder_topk_ids, reorder_cap, ws, ws_bytes);
     if (rc != CDL_OK) return rc;
     if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
+    if (H > CDL_MAX_HIDDEN) return CDL_ERR_TOO_LARGE;
     if (H % CDL_FP8_GROUP != 0 || !valid_scale_flags(scale_flags)) return CDL_ERR_UNSUPPORTED;
     if (cap_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
     if (T > 0 && !x) return CDL_ERR_NULL_POINTER;
@@ -1348,6 +1350,7 @@ int cdl_dispatch(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32
     int rc = check_tk(T, k);
     if (rc != CDL_OK) return rc;
     if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
+    if (H > CDL_MAX_HIDDEN) return CDL_ERR_TOO_LARGE;
     if (T == 0) return CDL_OK;
     if (!x || !src2dst) return CDL_ERR_NULL_POINTER;
     if (cap_rows > 0 && !out) return CDL_ERR_NULL_POINTER;
@@ -1378,6 +1381,7 @@ int cdl_dispatch_fp8_ex(const uint16_t *x, int64_t T, int64_t H, int32_t k,
     int rc = check_tk(T, k);
     if (rc != CDL_OK) return rc;
     if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
+    if (H > CDL_MAX_HIDDEN) return CDL_ERR_TOO_LARGE;
     if (H % CDL_FP8_GROUP != 0 || !valid_scale_flags(scale_flags)) return CDL_ERR_UNSUPPORTED;
     if (T == 0) return CDL_OK;
     if (!x || !src2dst) return CDL_ERR_NULL_POINTER;
@@ -1401,6 +1405,7 @@ static int check_ll_args(const uint16_t *x, int64_t T, int64_t H, int32_t k,
     int rc = check_tk(T, k);
     if (rc != CDL_OK) return rc;
     if (H < 1 || cap < 0 || L < 1 || L > CDL_MAX_LOCAL_EXPERTS) return CDL_ERR_BAD_SIZE;
+    if (H > CDL_MAX_HIDDEN) return CDL_ERR_TOO_LARGE;
     if (H % 8 != 0) return CDL_ERR_UNSUPPORTED;
     if ((int64_t)L * cap > INT32_MAX) return CDL_ERR_TOO_LARGE;
     if (!counts || !seg_indptr || !masked_m) return CDL_ERR_NULL_POINTER;
@@ -1519,6 +1524,7 @@ static int run_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32
     int rc = check_tk(T, k);
     if (rc != CDL_OK) return rc;
     if (H < 1 || y_rows < 0) return CDL_ERR_BAD_SIZE;
+    if (H > CDL_MAX_HIDDEN) return CDL_ERR_TOO_LARGE;
     if (T == 0) return CDL_OK;
     if (!map || !topk_weights || !out) return CDL_ERR_NULL_POINTER;
     if (y_rows > 0 && !y) return CDL_ERR_NULL_POINTER;

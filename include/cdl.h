@@ -70,6 +70,8 @@ extern "C" {
 #define CDL_STATUS_REORDER_OVERFLOW 8 /* padded rows exceed the reorder_topk_ids capacity */
 
 #define CDL_MAX_TOPK 64
+#define CDL_MAX_HIDDEN (1 << 24)    /* hidden size limit of the row calls (rows are addressed
+                                       with 32-bit byte offsets); larger H is CDL_ERR_TOO_LARGE */
 #define CDL_MAX_LOCAL_EXPERTS 2048
 #define CDL_FP8_GROUP 128
 

@@ -187,6 +187,24 @@ def test_permute_ll_rejects():
     assert call(g, [FAKE, 0], mm=NULL) == ENULL
 
 
+def test_hidden_size_limit():
+    """Rows are addressed with 32-bit byte offsets: H above CDL_MAX_HIDDEN is
+    rejected by every row call before any launch."""
+    lib = cdl.library()
+    big = (1 << 24) + 128
+    # x, T, H, k, s2d, out, cap_rows, status, stream
+    assert lib.cdl_dispatch(FAKE, 4, big, 2, FAKE, FAKE, 8, NULL, NULL) == EBIG
+    assert lib.cdl_dispatch_fp8(FAKE, 4, big, 2, FAKE, FAKE, FAKE, 8, NULL, NULL) == EBIG
+    # y, y_rows, H, map, w, T, k, out, status, stream
+    assert lib.cdl_combine(FAKE, 8, big, FAKE, FAKE, 4, 2, FAKE, NULL, NULL) == EBIG
+    # x, T, H, k, ids, b, L, s2d, seg, counts, cap, out, mm, ll, status, stream
+    assert lib.cdl_dispatch_ll(FAKE, 4, big, 2, FAKE, 0, 8, FAKE, FAKE, FAKE, 16, FAKE, FAKE, FAKE,
+                               NULL, NULL) == EBIG
+    # x, T, H, k, ids, b, L, A, counts, seg, s2d, reorder, rcap, out, cap_rows, status, ws, wsb, stream
+    assert lib.cdl_permute(FAKE, 4, big, 2, FAKE, 0, 8, 1, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 8, NULL,
+                           FAKE, 1 << 20, NULL) == EBIG
+
+
 def test_combine_rejects():
     lib = cdl.library()
     f = lib.cdl_combine
