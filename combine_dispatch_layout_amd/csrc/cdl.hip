@@ -415,7 +415,7 @@ __device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], int k, int
 // asked for its whole row at once, the rows would all arrive near the end of
 // the read phase and the waves would then quantise together and store
 // together; with a short window the three phases overlap.
-constexpr int kFp8Part = 3;
+constexpr int kFp8Part = 7;
 constexpr int kFp8Ahead = 1;
 template <int NCH>
 __device__ __forceinline__ void load_fp8_part(u32x4 (&v)[NCH], int part, rsrc_t xr, uint32_t voff,
