@@ -136,6 +136,21 @@ def test_layout_invariants(name):
         assert np.all(np.diff(src_of_row[seg[e]:seg[e + 1]]) > 0)
 
 
+EXTREME_IDS = [-2**31, -2**31 + 1, -101, -100, -69, -68, -1, 0, 1, 31, 32,
+               2**31 - 41, 2**31 - 40, 2**31 - 9, 2**31 - 8, 2**31 - 1]
+
+
+@pytest.mark.parametrize("b", [0, -100, 2**31 - 40, -2**31])
+def test_layout_int32_extreme_ids(b):
+    """Ids and expert ranges at the ends of int32: the local expert is
+    id - b over the integers (no wrap-around), as the definition says."""
+    rng = np.random.default_rng(b & 0xFFFF)
+    for _ in range(40):
+        ids = rng.choice(EXTREME_IDS + list(range(b, b + 4)), size=(6, 3)).astype(np.int64)
+        ids = np.clip(ids, -2**31, 2**31 - 1).astype(np.int32)
+        check_same(ids, b, 32)
+
+
 def test_layout_empty_batch():
     c, s, d, r = oracle.layout(np.zeros((0, 8), np.int32), 0, 32)
     assert c.tolist() == [0] * 32 and s.tolist() == [0] * 33

@@ -430,6 +430,45 @@ def test_combine_timed_matches_combine(H):
     assert e0.elapsed_time(e1) > 0
 
 
+def test_combine_extreme_values():
+    """Combine on rows of bf16 subnormals, values near the bf16 maximum (sums
+    that overflow to infinity), exact cancellations and negative or large
+    weights: bit-exact against the oracle (fp32 fma chain, subnormals kept,
+    one bf16 rounding)."""
+    announce("combine extreme values")
+    g = torch.Generator().manual_seed(31)
+    T, k, H, R = 256, 4, 512, 600
+    pats = []
+    sub = torch.randint(1, 0x80, (R // 4, H), generator=g, dtype=torch.int32)          # +subnormals
+    pats.append(sub | (torch.randint(0, 2, sub.shape, generator=g, dtype=torch.int32) << 15))
+    big = torch.randint(0x7F00, 0x7F7F, (R // 4, H), generator=g, dtype=torch.int32)   # near max
+    pats.append(big | (torch.randint(0, 2, big.shape, generator=g, dtype=torch.int32) << 15))
+    nrm = W.bf16_bits(torch.randn(R // 4, H, generator=g).to(torch.bfloat16)).astype(np.int32)
+    pats.append(torch.from_numpy(nrm))
+    pats.append(torch.from_numpy(nrm) ^ 0x8000)                                         # negations
+    ybits = torch.cat(pats).to(torch.int32).numpy().astype(np.uint16)
+    y = W.bits_to_bf16(ybits)
+    m = torch.randint(-1, R, (T, k), generator=g, dtype=torch.int32)
+    # rows [R/2, 3R/4) hold normal values and rows [3R/4, R) their negations:
+    # every third token adds a row and its negation with equal weights (exact 0)
+    pick = torch.randint(0, R // 4, (T,), generator=g, dtype=torch.int32)
+    m[::3, 0] = 2 * (R // 4) + pick[::3]
+    m[::3, 1] = 3 * (R // 4) + pick[::3]
+    m[::3, 2:] = -1
+    w = torch.randn(T, k, generator=g) * 4.0
+    w[::5] = 1.0
+    w[1::7, 0] = -1.0
+    w[::3, :2] = 1.0
+    out = cdl.combine(y.to(DEV), m.reshape(-1).to(DEV), w.to(DEV))
+    torch.cuda.synchronize()
+    want = oracle.combine(ybits, m.reshape(-1).numpy(), w.numpy(), T, k)
+    got = bits16(out)
+    assert np.array_equal(got, want)
+    assert np.any((got & 0x7FFF) == 0x7F80)                                            # infinities reached
+    assert np.any(((got & 0x7F80) == 0) & ((got & 0x7F) != 0))                          # subnormal results
+    assert np.all(got[::3] == 0)                                                        # cancellations give +0
+
+
 def test_fp8_rejects_ragged_groups():
     ids = torch.zeros(2, 1, dtype=torch.int32, device=DEV)
     lay = cdl.dispatch_layout(ids, 0, 1)
@@ -536,6 +575,25 @@ def test_permute_rows_overflow_flag():
     P = oracle.dispatch(W.bf16_bits(x), d, w.k, R)
     got = bits16(buf)
     assert np.array_equal(got[:cap], P[:cap]) and np.all(got[cap:] == 0x7F7F)
+
+
+@pytest.mark.parametrize("b", [0, -100, 2**31 - 40, -2**31])
+def test_permute_int32_extreme_ids(b):
+    """Ids at the ends of int32 and expert ranges next to them: same layout
+    and rows as the oracle (the local expert is computed without wrap-around)."""
+    announce("permute extreme ids b=%d" % b)
+    g = np.random.default_rng(b & 0xFFFF)
+    ext = [-2**31, -2**31 + 1, -101, -100, -69, -1, 0, 1, 31, 32, 2**31 - 41, 2**31 - 40,
+           2**31 - 9, 2**31 - 8, 2**31 - 1]
+    T, k, L, H = 300, 4, 32, 64
+    ids = g.choice(ext + [min(b + i, 2**31 - 1) for i in range(0, 32, 3)], size=(T, k))
+    ids = torch.from_numpy(np.clip(ids, -2**31, 2**31 - 1).astype(np.int32))
+    x = torch.randn(T, H, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    lay, rows = cdl.permute(x.to(DEV), ids.to(DEV), b, L)
+    torch.cuda.synchronize()
+    _, s_, d, _ = check_layout(lay, ids, b, L)
+    R = int(s_[-1])
+    assert np.array_equal(bits16(rows[:R]), oracle.dispatch(W.bf16_bits(x), d, k, R))
 
 
 @pytest.mark.parametrize("case", ["T0", "T1", "all_invalid", "max_k", "max_L", "H8"])
