@@ -76,8 +76,16 @@ def parse():
 
 
 def source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256 prefix of the kernel source with comments and whitespace
+    removed: a comment edit does not change a kernel, so it keeps a counter
+    summary valid; any change to the code does not."""
+    import re
+    with open(KERNEL_SOURCE) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    src = " ".join(src.split())
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def committed_traffic():

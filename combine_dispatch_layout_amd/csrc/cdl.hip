@@ -11,21 +11,28 @@
 // contraction and no MFMA.  Design points for CDNA4:
 //   * Layout in two launches with no atomics across workgroups and no state
 //     kept between calls: (A) per-superblock expert histograms; (B) every
-//     workgroup of 8 tokens (one wave per token) derives its own expert
-//     offsets from the superblock counts plus a recount of the slots of its
-//     superblock that precede it, then ranks its slots with wave ballots
-//     (__ballot / popcount / readlane), so src2dst is deterministic and stable
-//     by flat slot index.
-//   * The permute fuses (B) with the row scatter: each wave issues the loads
-//     of its token's row before the layout arithmetic starts, so HBM reads
-//     are in flight while the offsets are computed.
+//     workgroup (one wave per token) derives its own expert offsets from the
+//     superblock counts plus a recount of the slots of its superblock that
+//     precede it, then ranks its slots with wave ballots (__ballot /
+//     popcount / readlane), so src2dst is deterministic and stable by flat
+//     slot index.  Small batches (T*k <= 4096) skip (A): every workgroup
+//     counts all slots itself.
+//   * The permute fuses (B) with the row scatter (bf16, fp8, or into the
+//     low-latency padded buffer): the layout's small loads are issued first,
+//     then the token's row, so HBM reads are in flight while the offsets are
+//     computed.
 //   * Rows move as 16-byte lane accesses (buffer_load/store_dwordx4 through a
-//     per-row buffer resource); a wave holds up to 16 chunks (256 bytes) of a
-//     row per lane, so a source row is read once whatever its fan-out.
-//   * Dispatched rows are stored with the temporal policy so the combine
-//     finds them in the Infinity Cache; the combine loads and stores
-//     non-temporally (measured fastest of the policy combinations).
-//   * Routing indices are wave-uniform and are kept in scalar registers.
+//     per-row buffer resource); a wave holds 14 chunks (224 bytes) of a row
+//     per lane, one 7168-wide row, so a source row is read once whatever its
+//     fan-out.  Each wave holds its token's k destinations in lanes and takes
+//     them with readlane.
+//   * Cache policies, measured: source rows are streamed in; dispatched bf16
+//     rows are stored with the temporal policy so the combine finds them in
+//     the Infinity Cache; the combine loads and stores non-temporally; fp8
+//     rows and scales (read by no kernel here) are stored non-temporally.
+//   * fp8 groups are quantised without a division (correctly rounded scale
+//     and reciprocal from one correction step each, Markstein's correction
+//     per element; checked exhaustively over bf16 inputs on the CPU).
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -511,19 +518,21 @@ struct PermuteArgs {
 
 // One workgroup per TPB tokens, one wave per token.
 //  0. every thread loads its first batch of layout operands, then the wave
-//     of token t loads its row (first NC chunks per lane) if the token has
-//     a valid slot;
+//     of token t loads its row (all NC chunks per lane; the first part in
+//     fp8 modes) if the token has a valid slot;
 //  1. tot[e] = all valid slots of e; cur[e] = valid slots of e before this
 //     workgroup's first slot (superblock counts of earlier superblocks plus a
-//     recount of this superblock's earlier slots);
+//     recount of this superblock's earlier slots; with self_count, a count
+//     of every slot);
 //  2. exclusive scan over e of tot rounded up to the alignment gives
-//     seg_indptr (workgroup 0 publishes counts and seg_indptr) and
-//     cur[e] += seg_indptr[e]; the padding rows of expert e get reorder id -1
-//     from workgroup e mod gridDim;
+//     seg_indptr (workgroup 0 publishes counts and seg_indptr, and masked_m
+//     in low-latency modes) and cur[e] += seg_indptr[e]; the padding rows of
+//     expert e get reorder id -1 from workgroup e mod gridDim;
 //  3. the workgroup's TPB*k slots are ranked 64 at a time, wave by wave in
 //     slot order, with ballots; the leader of each expert match advances
 //     cur[e]; dst = cur[e] + rank in the match;
-//  4. each wave stores its row to its token's destinations.
+//  4. each wave stores its row to its token's destinations (in low-latency
+//     modes the padded-buffer rows e * cap + (dst - seg_indptr[e])).
 template <int TPB, int MODE>
 __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 {
@@ -768,7 +777,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 constexpr int kRowTok = 4;                       // tokens (waves) per workgroup
 constexpr int kRowThreads = kRowTok * kWave;
 
-// One wave per token: the wave loads up to NC 16-byte chunks per
+// One wave per token: the wave loads NC 16-byte chunks per
 // lane of the row once, then stores them to every valid destination.
 template <bool FP8>
 __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
@@ -1164,7 +1173,7 @@ int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
     return launch_status();
 }
 
-// Kernel A then kernel B in the given mode.
+// Kernel A (unless the batch counts itself) then kernel B in the given mode.
 template <int MODE>
 int run_layout(PermuteArgs a, void *ws, hipStream_t s)
 {
