@@ -339,6 +339,7 @@ def measure_ll(torch, cdl, W, dev, steps):
 
     ms, _ = time_steps(torch, runs, fn, steps, 5)
     ms_sep, _ = time_steps(torch, runs, fn_separate, steps, 5)
+    ms_graph = ll_graph_step(torch, lib, runs, steps)
     b = runs[0][0]
     byts = (b.bytes_layout() + 4 * w.L + 4 * w.T * w.k + 2 * b.U * w.H + 2 * b.R * w.H
             + b.bytes_combine())
@@ -346,7 +347,33 @@ def measure_ll(torch, cdl, W, dev, steps):
                         "layout + padded dispatch (one call) + combine)",
             "us_per_step": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9,
             "us_per_step_separate_calls": ms_sep * 1e3,
+            "us_per_step_hip_graph": ms_graph * 1e3,
             "expected_m": cdl.ll_expected_m(w.T, w.num_ranks, w.k, w.E)}
+
+
+def ll_graph_step(torch, lib, runs, steps):
+    """The one-call low-latency step of each run captured once in a HIP graph
+    (on the capture stream), then the graphs replayed alternately: the step
+    without host launch overhead, as a decode loop would run it."""
+    P = ctypes.c_void_p
+    side = torch.cuda.Stream()
+    graphs = []
+    for r in runs:
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            s = P(torch.cuda.current_stream().cuda_stream)
+            lib.cdl_permute_ll(*r[6][:-1], s)
+            lib.cdl_combine(*r[2][:-1], s)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s = P(torch.cuda.current_stream().cuda_stream)
+            if lib.cdl_permute_ll(*r[6][:-1], s) or lib.cdl_combine(*r[2][:-1], s):
+                raise RuntimeError("low-latency step failed during capture")
+        graphs.append(g)
+    ms, _ = time_steps(torch, graphs, lambda g: g.replay(), steps, 5)
+    return ms
 
 
 def measure_zipf(torch, cdl, W, dev, steps):

@@ -1539,14 +1539,22 @@ static int run_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32
     if (y_rows > 0 && !y) return CDL_ERR_NULL_POINTER;
     if (y_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
     hipStream_t s = (hipStream_t)stream;
+    const bool timed = start != nullptr || stop != nullptr;
     if (H % 8 == 0 && aligned(y, 16) && aligned(out, 16)) {
-        // with events: the launch itself carries them (no extra queue packets)
-        hipExtLaunchKernelGGL(combine_rows_v16, dim3((unsigned)T), dim3(kCombThreads), 0, s, start, stop,
-                              0, (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k, (u32x4 *)out,
-                              status);
+        if (timed)   // the launch itself carries the events
+            hipExtLaunchKernelGGL(combine_rows_v16, dim3((unsigned)T), dim3(kCombThreads), 0, s, start,
+                                  stop, 0, (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k,
+                                  (u32x4 *)out, status);
+        else
+            combine_rows_v16<<<dim3((unsigned)T), dim3(kCombThreads), 0, s>>>(
+                (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k, (u32x4 *)out, status);
     } else {
-        hipExtLaunchKernelGGL(combine_rows_u16, dim3((unsigned)T), dim3(128), 0, s, start, stop, 0, y,
-                              y_rows, H, map, topk_weights, k, out, status);
+        if (timed)
+            hipExtLaunchKernelGGL(combine_rows_u16, dim3((unsigned)T), dim3(128), 0, s, start, stop, 0,
+                                  y, y_rows, H, map, topk_weights, k, out, status);
+        else
+            combine_rows_u16<<<dim3((unsigned)T), dim3(128), 0, s>>>(y, y_rows, H, map, topk_weights,
+                                                                      k, out, status);
     }
     return launch_status();
 }

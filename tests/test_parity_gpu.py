@@ -216,6 +216,42 @@ def test_permute_ll_parity(case):
     assert np.array_equal(bits16(B.view(w.L * w.cap, w.H)), OB.reshape(-1, w.H))
 
 
+def test_graph_replay_low_latency_step():
+    """cdl_permute_ll + cdl_combine captured in a HIP graph (no memset nodes:
+    the library issues none): every replay, with eager work and
+    synchronisations between replays, gives the eager result bit for bit."""
+    w = W.WORKLOADS["ll_decode"]
+    announce("graph replay ll step")
+    x, ids, wts = W.make_inputs(w)
+    xd, idd, wd = x.to(DEV), ids.to(DEV), wts.to(DEV)
+    lay, B, mm, llm = cdl.permute_ll(xd, idd, w.expert_begin, w.L, w.cap)
+    ref = cdl.combine(B, llm, wd)
+    torch.cuda.synchronize()
+    ref_bits, ref_mm, ref_llm = bits16(ref), npy(mm), npy(llm)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                     # warm-up on the capture stream
+        _, B_w, _, llm_w = cdl.permute_ll(xd, idd, w.expert_begin, w.L, w.cap)
+        cdl.combine(B_w, llm_w, wd)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lay_g, B_g, mm_g, llm_g = cdl.permute_ll(xd, idd, w.expert_begin, w.L, w.cap)
+        out_g = cdl.combine(B_g, llm_g, wd)
+    for rep in range(4):
+        out_g.fill_(1.0)                               # eager work between replays
+        mm_g.fill_(-7)
+        llm_g.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits16(out_g), ref_bits), rep
+        assert np.array_equal(npy(mm_g), ref_mm), rep
+        assert np.array_equal(npy(llm_g), ref_llm), rep
+        check_layout(lay_g, ids, w.expert_begin, w.L)
+
+
 @pytest.mark.parametrize("flags,cap", [(0, 1024), (UE_ | CM_ | PK_, 1024), (UE_ | CM_, 5)])
 def test_permute_ll_fp8_parity(flags, cap):
     w = W.WORKLOADS["ll_decode"]
