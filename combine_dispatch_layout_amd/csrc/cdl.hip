@@ -533,7 +533,10 @@ struct PermuteArgs {
 //     cur[e]; dst = cur[e] + rank in the match;
 //  4. each wave stores its row to its token's destinations (in low-latency
 //     modes the padded-buffer rows e * cap + (dst - seg_indptr[e])).
-template <int TPB, int MODE>
+// ALL_ROWS (small self-counted batches): every token's row is loaded at once,
+// without first reading the token's ids to see whether it has a local slot,
+// so the row and the ids arrive together instead of one after the other.
+template <int TPB, int MODE, bool ALL_ROWS>
 __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
 {
     constexpr int NT = TPB * kWave;
@@ -584,28 +587,38 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     const int32_t my_id = buf_ld4(r_my, (uint32_t)my_rel * 4u, 0);
 
     const int64_t t = t_begin + wave;
-    bool tok_valid = false;
-    if (MODE != kLayoutOnly && t < a.T) {
-        for (int j = 0; j < k; ++j) tok_valid |= local_expert(a.ids[t * k + j], a.expert_begin, L) >= 0;
-    }
-    u32x4 v[NC];
-    const uint32_t row_bytes = (uint32_t)(a.chunks * 16);
-    const uint32_t voff = (uint32_t)lane * 16u;
-    const rsrc_t xr = make_rsrc(a.x + (tok_valid ? t * a.chunks : 0), row_bytes);
-    if (kFp8Mode && tok_valid) {
-        load_fp8_first_parts(v, xr, voff, 0);
-    } else if (MODE != kLayoutOnly && tok_valid) {
-        // source rows are read once: streaming loads leave the Infinity Cache
-        // to the permuted rows, which the combine reads back
-#pragma unroll
-        for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, u * kWave * 16);
-    }
     // low latency: lane j < k holds the local expert of this wave's slot j
+    // (loaded ahead of the row, so that reading it does not wait for the row)
     int32_t ll_e = -1;
     if (kLLMode) {
         const bool real = t < a.T;
         const rsrc_t r_tok = make_rsrc(a.ids + (real ? t * k : 0), real ? (uint32_t)k * 4u : 0u);
         ll_e = lane < k ? local_expert(buf_ld4(r_tok, (uint32_t)lane * 4u, 0), a.expert_begin, L) : -1;
+    }
+    // tok_valid: the token's row is loaded and stored to its destinations
+    bool tok_valid = false;
+    if (MODE != kLayoutOnly && t < a.T) {
+        if (ALL_ROWS)
+            tok_valid = true;
+        else
+            for (int j = 0; j < k; ++j) tok_valid |= local_expert(a.ids[t * k + j], a.expert_begin, L) >= 0;
+    }
+    u32x4 v[NC];
+    const uint32_t row_bytes = (uint32_t)(a.chunks * 16);
+    const uint32_t voff = (uint32_t)lane * 16u;
+    // ALL_ROWS: the loads are issued by every wave (a wave past the last
+    // token gets an empty range: its loads return 0 and touch no memory), so
+    // the compiler's wait counts for the layout operands above are exact
+    const rsrc_t xr = make_rsrc(a.x + (tok_valid ? t * a.chunks : 0), tok_valid ? row_bytes : 0u);
+    if (MODE != kLayoutOnly && (ALL_ROWS || tok_valid)) {
+        if (kFp8Mode) {
+            load_fp8_first_parts(v, xr, voff, 0);
+        } else {
+            // source rows are read once: streaming loads leave the Infinity
+            // Cache to the permuted rows, which the combine reads back
+#pragma unroll
+            for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, u * kWave * 16);
+        }
     }
 
     // 1. totals and offsets before this workgroup
@@ -1060,6 +1073,76 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows_v16(
     }
 }
 
+// Small batches: one workgroup per token and one 16-byte chunk per thread, so
+// that the loads of all of a token's slots are in flight together (the
+// kernel above reads a token's slots one after another, which sets the time
+// of a batch too small to fill the GPU).  Same fma order as above: ascending
+// valid slots from +0, one bf16 rounding.  k <= kWideK, y_rows >= 1.
+constexpr int kWideK = 8;
+constexpr int kWideMaxThreads = 1024;
+constexpr int64_t kWideMaxTokens = 256;   // batches up to this size use it
+
+__global__ __launch_bounds__(kWideMaxThreads) void combine_rows_wide(
+    const u32x4 *__restrict__ y, int64_t y_rows, int64_t chunks, const int32_t *__restrict__ map,
+    const float *__restrict__ wts, int32_t k, u32x4 *__restrict__ out,
+    int32_t *__restrict__ status)
+{
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t mlane = lane < k ? map[t * k + lane] : -1;
+    const float wlane = lane < k ? wts[t * k + lane] : 0.0f;
+    // every slot's row (-1: none) in scalars before any row load, so that no
+    // wait for the map falls between the row loads
+    int32_t rs[kWideK];
+    bool bad = false;
+#pragma unroll
+    for (int j = 0; j < kWideK; ++j) {
+        int32_t r = j < k ? __builtin_amdgcn_readlane(mlane, j) : -1;
+        if ((int64_t)r >= y_rows) {
+            bad = true;
+            r = -1;
+        }
+        rs[j] = r;
+    }
+    if (bad && threadIdx.x == 0) set_status(status, CDL_STATUS_MAP_RANGE);
+    const uint32_t row_bytes = (uint32_t)(chunks * 16);
+    const uint32_t voff = threadIdx.x * 16u;
+    const rsrc_t orow = make_rsrc(out + t * chunks, row_bytes);
+    for (int64_t c0 = 0; c0 < chunks; c0 += blockDim.x) {
+        const uint32_t pass = (uint32_t)(c0 * 16);
+        // issued for every slot: an unused slot gets an empty range (its loads
+        // return 0 and touch no memory), so the wait for slot j's data counts
+        // exactly the loads issued after it
+        u32x4 v[kWideK];
+#pragma unroll
+        for (int j = 0; j < kWideK; ++j) {
+            const bool use = rs[j] >= 0;
+            v[j] = buf_ld16_stream(make_rsrc(y + (use ? (int64_t)rs[j] * chunks : 0), use ? row_bytes : 0u),
+                                   voff, pass);
+        }
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kWideK; ++j) {
+            if (rs[j] < 0) continue;
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), j));
+            acc[0] = fmaf(wj, bf16_lo(v[j].x), acc[0]);
+            acc[1] = fmaf(wj, bf16_hi(v[j].x), acc[1]);
+            acc[2] = fmaf(wj, bf16_lo(v[j].y), acc[2]);
+            acc[3] = fmaf(wj, bf16_hi(v[j].y), acc[3]);
+            acc[4] = fmaf(wj, bf16_lo(v[j].z), acc[4]);
+            acc[5] = fmaf(wj, bf16_hi(v[j].z), acc[5]);
+            acc[6] = fmaf(wj, bf16_lo(v[j].w), acc[6]);
+            acc[7] = fmaf(wj, bf16_hi(v[j].w), acc[7]);
+        }
+        buf_st16_stream(orow,
+                        u32x4{pack_bf16_rne(acc[0], acc[1]), pack_bf16_rne(acc[2], acc[3]),
+                              pack_bf16_rne(acc[4], acc[5]), pack_bf16_rne(acc[6], acc[7])},
+                        voff, pass);
+    }
+}
+
 // Any H, any 2-byte alignment.
 __global__ __launch_bounds__(128) void combine_rows_u16(
     const uint16_t *__restrict__ y, int64_t y_rows, int64_t H, const int32_t *__restrict__ map,
@@ -1159,17 +1242,33 @@ inline int64_t scale_bytes(int64_t rows, int64_t H, int32_t flags, int64_t rows_
     return rows * words * 4;
 }
 
-template <int MODE>
-int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
+template <int MODE, bool ALL_ROWS>
+void launch_permute_tpb(const PermuteArgs &a, const Plan &p, hipStream_t s)
 {
     const size_t lds = (size_t)(2 * a.L + p.tpb * a.k) * sizeof(int32_t);
     const dim3 grid((unsigned)(p.nblocks > 0 ? p.nblocks : 1));
     switch (p.tpb) {
-    case 1: permute_kernel<1, MODE><<<grid, dim3(1 * kWave), lds, s>>>(a); break;
-    case 2: permute_kernel<2, MODE><<<grid, dim3(2 * kWave), lds, s>>>(a); break;
-    case 4: permute_kernel<4, MODE><<<grid, dim3(4 * kWave), lds, s>>>(a); break;
-    default: permute_kernel<8, MODE><<<grid, dim3(8 * kWave), lds, s>>>(a); break;
+    case 1: permute_kernel<1, MODE, ALL_ROWS><<<grid, dim3(1 * kWave), lds, s>>>(a); break;
+    case 2: permute_kernel<2, MODE, ALL_ROWS><<<grid, dim3(2 * kWave), lds, s>>>(a); break;
+    case 4: permute_kernel<4, MODE, ALL_ROWS><<<grid, dim3(4 * kWave), lds, s>>>(a); break;
+    default: permute_kernel<8, MODE, ALL_ROWS><<<grid, dim3(8 * kWave), lds, s>>>(a); break;
     }
+}
+
+// Batches of at most this many tokens that count themselves load every row
+// (at most this many rows read in vain, 1.8 MB at H = 7168) rather than first
+// checking each token for a local slot.
+constexpr int64_t kAllRowsMaxTokens = 128;
+
+template <int MODE>
+int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
+{
+    if constexpr (MODE == kLayoutOnly)
+        launch_permute_tpb<MODE, false>(a, p, s);
+    else if (a.self_count && a.T > 0 && a.T <= kAllRowsMaxTokens)
+        launch_permute_tpb<MODE, true>(a, p, s);
+    else
+        launch_permute_tpb<MODE, false>(a, p, s);
     return launch_status();
 }
 
@@ -1540,7 +1639,18 @@ static int run_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32
     if (y_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
     hipStream_t s = (hipStream_t)stream;
     const bool timed = start != nullptr || stop != nullptr;
-    if (H % 8 == 0 && aligned(y, 16) && aligned(out, 16)) {
+    if (H % 8 == 0 && aligned(y, 16) && aligned(out, 16) && k <= kWideK && T <= kWideMaxTokens &&
+        y_rows > 0) {
+        const int64_t chunks = H / 8;
+        const unsigned nt = (unsigned)(chunks >= kWideMaxThreads ? kWideMaxThreads : (chunks + kWave - 1) / kWave * kWave);
+        if (timed)
+            hipExtLaunchKernelGGL(combine_rows_wide, dim3((unsigned)T), dim3(nt), 0, s, start, stop, 0,
+                                  (const u32x4 *)y, y_rows, chunks, map, topk_weights, k,
+                                  (u32x4 *)out, status);
+        else
+            combine_rows_wide<<<dim3((unsigned)T), dim3(nt), 0, s>>>(
+                (const u32x4 *)y, y_rows, chunks, map, topk_weights, k, (u32x4 *)out, status);
+    } else if (H % 8 == 0 && aligned(y, 16) && aligned(out, 16)) {
         if (timed)   // the launch itself carries the events
             hipExtLaunchKernelGGL(combine_rows_v16, dim3((unsigned)T), dim3(kCombThreads), 0, s, start,
                                   stop, 0, (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k,

@@ -689,6 +689,67 @@ def test_permute_fp8_parity(w):
     assert np.all(gq[R:] == 0xA5) and np.all(gs[R:] == -7.0)
 
 
+@pytest.mark.parametrize("T,L,fp8", [(1, 32, False), (5, 8, False), (100, 8, False), (128, 32, False),
+                                    (129, 32, False), (100, 8, True), (128, 32, True), (129, 32, True)])
+def test_permute_small_batches_all_rows(T, L, fp8):
+    """Batches of up to 128 tokens that count themselves load every token's
+    row whether or not it has a local slot.  With few local experts most
+    tokens have none: their rows must not be stored anywhere (canary rows
+    past R stay untouched), and the rows of the others match the oracle; 129
+    tokens take the path that checks each token first."""
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=T, L=L, H=1024, expert_begin=256 - L)
+    announce("permute small batch T=%d L=%d fp8=%d" % (T, L, fp8))
+    x, ids, wts = W.make_inputs(w)
+    _, s, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s[-1])
+    st = status_word()
+    if fp8:
+        q = torch.full((R + 2, w.H), 0xA5, dtype=torch.uint8, device=DEV)
+        sc = torch.full((R + 2, w.H // 128), -7.0, dtype=torch.float32, device=DEV)
+        lay, _, _ = cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q[:R],
+                                    out_scales=sc[:R], status=st)
+        torch.cuda.synchronize()
+        Q, S = oracle.dispatch_fp8(W.bf16_bits(x), d, w.k, R)
+        gq, gs = u8(q), npy(sc)
+        assert np.array_equal(gq[:R], Q)
+        assert np.array_equal(gs[:R].view(np.uint32), S.view(np.uint32))
+        assert np.all(gq[R:] == 0xA5) and np.all(gs[R:] == -7.0)
+    else:
+        buf = bf16_filled(R + 3, w.H, 0x7F7F)
+        lay, _ = cdl.permute(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out=buf[:R], status=st)
+        torch.cuda.synchronize()
+        got = bits16(buf)
+        assert np.array_equal(got[:R], oracle.dispatch(W.bf16_bits(x), d, w.k, R))
+        assert np.all(got[R:] == 0x7F7F)
+    assert int(st.item()) == 0
+    check_layout(lay, ids, w.expert_begin, w.L)
+
+
+@pytest.mark.parametrize("T,k,H", [(1, 8, 7168), (256, 8, 7168), (257, 8, 7168), (200, 9, 512),
+                                   (100, 8, 9000), (64, 8, 8), (40, 1, 200), (3, 8, 8192)])
+def test_combine_small_batch_kernel(T, k, H):
+    """Batches of up to 256 tokens with k <= 8 use the combine kernel that
+    loads all of a token's slots at once (one chunk per thread, a second pass
+    past 1024 chunks); 257 tokens and k = 9 take the other one.  Both give
+    the oracle's bits and write nothing past the T output rows."""
+    announce("combine small batch T=%d k=%d H=%d" % (T, k, H))
+    g = torch.Generator().manual_seed(T * 131 + k * 7 + H)
+    R = max(1, (T * k) // 2)
+    y = torch.randn(R, H, generator=g).to(torch.bfloat16)
+    m = torch.randint(-R // 2, R, (T * k,), generator=g, dtype=torch.int32)
+    m[m < 0] = -1
+    wts = torch.randn(T, k, generator=g).softmax(-1)
+    outbuf = bf16_filled(T + 2, H, 0x7F7F)
+    st = status_word()
+    cdl.combine(y.to(DEV), m.to(DEV), wts.to(DEV), out=outbuf[:T], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    got = bits16(outbuf)
+    want = oracle.combine(W.bf16_bits(y), m.numpy(), wts.numpy(), T, k)
+    assert np.array_equal(got[:T], want)
+    assert np.all(got[T:] == 0x7F7F)
+
+
 def test_permute_rejects_unsupported_shapes():
     ids = torch.zeros(2, 1, dtype=torch.int32, device=DEV)
     with pytest.raises(cdl.CdlError):
