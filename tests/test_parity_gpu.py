@@ -689,14 +689,14 @@ def test_permute_fp8_parity(w):
     assert np.all(gq[R:] == 0xA5) and np.all(gs[R:] == -7.0)
 
 
-@pytest.mark.parametrize("T,L,fp8", [(1, 32, False), (5, 8, False), (100, 8, False), (128, 32, False),
-                                    (129, 32, False), (100, 8, True), (128, 32, True), (129, 32, True)])
+@pytest.mark.parametrize("T,L,fp8", [(1, 32, False), (5, 8, False), (100, 8, False), (512, 32, False),
+                                    (513, 32, False), (100, 8, True), (512, 32, True), (513, 32, True)])
 def test_permute_small_batches_all_rows(T, L, fp8):
-    """Batches of up to 128 tokens that count themselves load every token's
-    row whether or not it has a local slot.  With few local experts most
-    tokens have none: their rows must not be stored anywhere (canary rows
-    past R stay untouched), and the rows of the others match the oracle; 129
-    tokens take the path that checks each token first."""
+    """Batches of up to 512 tokens that count themselves (T*k <= 4096) load
+    every token's row whether or not it has a local slot.  With few local
+    experts most tokens have none: their rows must not be stored anywhere
+    (canary rows past R stay untouched), and the rows of the others match the
+    oracle; 513 tokens take the path that checks each token first."""
     w = W.WORKLOADS["dsv3_prefill"].scaled(T=T, L=L, H=1024, expert_begin=256 - L)
     announce("permute small batch T=%d L=%d fp8=%d" % (T, L, fp8))
     x, ids, wts = W.make_inputs(w)
@@ -725,12 +725,12 @@ def test_permute_small_batches_all_rows(T, L, fp8):
     check_layout(lay, ids, w.expert_begin, w.L)
 
 
-@pytest.mark.parametrize("T,k,H", [(1, 8, 7168), (256, 8, 7168), (257, 8, 7168), (200, 9, 512),
+@pytest.mark.parametrize("T,k,H", [(1, 8, 7168), (512, 8, 7168), (513, 8, 7168), (200, 9, 512),
                                    (100, 8, 9000), (64, 8, 8), (40, 1, 200), (3, 8, 8192)])
 def test_combine_small_batch_kernel(T, k, H):
-    """Batches of up to 256 tokens with k <= 8 use the combine kernel that
+    """Batches of up to 512 tokens with k <= 8 use the combine kernel that
     loads all of a token's slots at once (one chunk per thread, a second pass
-    past 1024 chunks); 257 tokens and k = 9 take the other one.  Both give
+    past 1024 chunks); 513 tokens and k = 9 take the other one.  Both give
     the oracle's bits and write nothing past the T output rows."""
     announce("combine small batch T=%d k=%d H=%d" % (T, k, H))
     g = torch.Generator().manual_seed(T * 131 + k * 7 + H)
