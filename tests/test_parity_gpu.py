@@ -689,6 +689,28 @@ def test_permute_fp8_parity(w):
     assert np.all(gq[R:] == 0xA5) and np.all(gs[R:] == -7.0)
 
 
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 128])
+@pytest.mark.parametrize("T", [100, 1500])
+@pytest.mark.parametrize("A", [1, 16])
+def test_layout_expert_scan_paths(L, T, A):
+    """Small batches with up to 64 local experts scan them inside one wave
+    (DPP), other batches across the workgroup: the layout (counts, padded
+    seg_indptr, src2dst, reorder) at both sides of 64, for a batch that counts
+    itself (T = 100, k = 8) and one that uses the count kernel (T = 1500),
+    with and without padding."""
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=T, L=L, H=64, expert_begin=0, E=max(L, 256))
+    announce("expert scan L=%d T=%d A=%d" % (L, T, A))
+    x, ids, wts = W.make_inputs(w)
+    c, s_, d, r = oracle.layout_aligned(ids.numpy(), 0, L, A)
+    lay = cdl.dispatch_layout(ids.to(DEV), 0, L, alignment=A)
+    lay2, _ = cdl.permute(x.to(DEV), ids.to(DEV), 0, L, alignment=A)
+    torch.cuda.synchronize()
+    for g in (lay, lay2):
+        assert np.array_equal(npy(g.counts), c) and np.array_equal(npy(g.seg_indptr), s_)
+        assert np.array_equal(npy(g.src2dst), d)
+        assert np.array_equal(npy(g.reorder_topk_ids), r)
+
+
 @pytest.mark.parametrize("T,L,fp8", [(1, 32, False), (5, 8, False), (100, 8, False), (512, 32, False),
                                     (513, 32, False), (100, 8, True), (512, 32, True), (513, 32, True)])
 def test_permute_small_batches_all_rows(T, L, fp8):
