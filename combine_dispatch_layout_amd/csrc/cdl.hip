@@ -291,15 +291,17 @@ struct Plan {
 };
 
 // Tokens per workgroup: enough workgroups to fill the chip (about 512) for
-// small batches, 8 tokens (512 threads) for large ones.  Superblock size: the
-// power of two that balances the superblock counts every workgroup reads
-// (S * L) against the slots it may recount (sbb * tpb * k).
-inline Plan make_plan(int64_t T, int32_t k, int32_t L)
+// small batches, max_tpb tokens for large ones (8, 512 threads, for bf16
+// rows; 4 for fp8 rows, measured 23.1 -> 22.1 us at T = 4096, H = 7168,
+// where 8 is best for bf16, 39.6 against 43.4 us per step).  Superblock
+// size: the power of two that balances the superblock counts every workgroup
+// reads (S * L) against the slots it may recount (sbb * tpb * k).
+inline Plan make_plan(int64_t T, int32_t k, int32_t L, int max_tpb)
 {
     Plan p;
     p.n = T * k;
     int tpb = 1;
-    while (tpb < 8 && (T + tpb - 1) / tpb > 512) tpb *= 2;
+    while (tpb < max_tpb && (T + tpb - 1) / tpb > 512) tpb *= 2;
     // a batch small enough for every workgroup to count all of its slots:
     // enough tokens per workgroup that the ids fit the one batch of loads
     // issued before the rows (kSelfCountIds per thread)
@@ -1216,10 +1218,15 @@ inline int check_tk(int64_t T, int32_t k)
     return CDL_OK;
 }
 
+constexpr int kMaxTpbBf16 = 8;
+constexpr int kMaxTpbFp8 = 4;
+
 inline size_t layout_ws_bytes(int64_t T, int32_t k, int32_t L)
 {
-    const Plan p = make_plan(T, k, L);
-    const size_t bytes = (size_t)p.S * (size_t)L * sizeof(int32_t);
+    // one workspace serves every mode: the larger of the two plans
+    const int64_t S8 = make_plan(T, k, L, kMaxTpbBf16).S;
+    const int64_t S4 = make_plan(T, k, L, kMaxTpbFp8).S;
+    const size_t bytes = (size_t)(S8 > S4 ? S8 : S4) * (size_t)L * sizeof(int32_t);
     return ((bytes + 255) & ~(size_t)255) + 256;
 }
 
@@ -1309,7 +1316,8 @@ int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
 template <int MODE>
 int run_layout(PermuteArgs a, void *ws, hipStream_t s)
 {
-    const Plan p = make_plan(a.T, a.k, a.L);
+    constexpr bool kFp8Rows = MODE == kRowsFp8 || MODE == kRowsLLFp8;
+    const Plan p = make_plan(a.T, a.k, a.L, kFp8Rows ? kMaxTpbFp8 : kMaxTpbBf16);
     a.sb_counts = (const int32_t *)ws;
     a.S = p.S;
     a.sbb = p.sbb;

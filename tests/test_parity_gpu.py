@@ -252,11 +252,14 @@ def test_graph_replay_low_latency_step():
         check_layout(lay_g, ids, w.expert_begin, w.L)
 
 
-@pytest.mark.parametrize("flags,cap", [(0, 1024), (UE_ | CM_ | PK_, 1024), (UE_ | CM_, 5)])
-def test_permute_ll_fp8_parity(flags, cap):
+@pytest.mark.parametrize("flags,cap,T", [(0, 1024, 128), (UE_ | CM_ | PK_, 1024, 128), (UE_ | CM_, 5, 100),
+                                         (0, 256, 2500)])
+def test_permute_ll_fp8_parity(flags, cap, T):
+    """One-call LL fp8 dispatch; T = 2500 takes the count kernel and 4 tokens
+    per permute workgroup (the fp8 plan)."""
     w = W.WORKLOADS["ll_decode"]
-    if cap < 100:
-        w = w.scaled(T=100, H=512)
+    if T != w.T:
+        w = w.scaled(T=T, H=512)
     announce("permute_ll fp8 flags=%d cap=%d" % (flags, cap))
     x, ids, wts = W.make_inputs(w)
     Q, S, mm, ll, ovf = oracle.dispatch_ll_fp8(W.bf16_bits(x), ids.numpy(), w.expert_begin, w.L,
@@ -666,7 +669,8 @@ def test_permute_edge_cases(case):
 
 
 @pytest.mark.parametrize("w", [W.WORKLOADS["fp8_dispatch"],
-                               W.WORKLOADS["fp8_dispatch"].scaled(T=333, H=1152, expert_begin=96)],
+                               W.WORKLOADS["fp8_dispatch"].scaled(T=333, H=1152, expert_begin=96),
+                               W.WORKLOADS["fp8_dispatch"].scaled(T=2501, H=1024, expert_begin=32)],
                          ids=lambda w: "T%d_H%d" % (w.T, w.H))
 def test_permute_fp8_parity(w):
     announce("permute fp8 T=%d H=%d" % (w.T, w.H))
