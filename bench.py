@@ -66,8 +66,8 @@ def parse():
                    help="rotating input/output sets (defeats the 256 MB Infinity Cache)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-modes", action="store_true",
-                   help="skip the fp8 / low-latency / Zipf side measurements")
-    p.add_argument("--only", choices=["fp8_dispatch", "ll_decode", "zipf_prefill"],
+                   help="skip the side measurements (fp8, low-latency, Zipf, next rows)")
+    p.add_argument("--only", choices=["fp8_dispatch", "ll_decode", "zipf_prefill", "next_rows"],
                    help="run just this side measurement and print its JSON (for profiling)")
     p.add_argument("--calibration-copy", type=int, default=0, metavar="MB",
                    help="first run 5 plain device copies of MB MiB (torch copy_), the "
@@ -305,6 +305,83 @@ def measure_fp8(torch, cdl, sets, steps):
             "scatter_fp8_us": ms_s * 1e3, "scatter_fp8_gbps": scat_bytes / (ms_s * 1e-3) / 1e9}
 
 
+def measure_next_rows(torch, cdl, sets, E, steps):
+    """The rows built beyond the hot path, at the same shape and on the same
+    rotating sets: the rank layout that precedes an exchange (8 ranks on one
+    node), the layout + bf16 scatter with expert segments padded to 128 rows,
+    and the fused fp8 permute in the DeepGEMM format (segments padded to 128,
+    UE8M0 exponents packed four to a word, column-major, TMA-aligned)."""
+    lib = cdl.library()
+    P = ctypes.c_void_p
+    i32, u8 = torch.int32, torch.uint8
+    A, R_RANKS, RPN = 128, 8, 8
+    flags = cdl.FP8_SCALE_UE8M0 | cdl.FP8_SCALE_COLMAJOR | cdl.FP8_SCALE_PACKED
+    bufs = []
+    for s in sets:
+        T, k, L, H, dev = s.T, s.k, s.L, s.H, s.x.device
+        ntr = torch.empty(R_RANKS, dtype=i32, device=dev)
+        ntn = torch.empty(R_RANKS // RPN, dtype=i32, device=dev)
+        nte = torch.empty(E, dtype=i32, device=dev)
+        itr = torch.empty(T, R_RANKS, dtype=u8, device=dev)
+        rwsb = lib.cdl_rank_layout_workspace_size(T, k, E, R_RANKS, RPN)
+        rws = torch.empty(max(rwsb, 1), dtype=u8, device=dev)
+        a_rank = (P(s.ids.data_ptr()), T, k, E, R_RANKS, RPN, P(ntr.data_ptr()), P(ntn.data_ptr()),
+                  P(nte.data_ptr()), P(itr.data_ptr()), P(rws.data_ptr()), rwsb, s.stream)
+        reo_cap = T * k + L * (A - 1)
+        cnt = torch.empty(L, dtype=i32, device=dev)
+        seg = torch.empty(L + 1, dtype=torch.int64, device=dev)
+        s2d = torch.empty(T * k, dtype=i32, device=dev)
+        reo = torch.empty(reo_cap, dtype=i32, device=dev)
+        lay = (P(s.ids.data_ptr()), T, k, 0, L, A, P(cnt.data_ptr()), P(seg.data_ptr()),
+               P(s2d.data_ptr()), P(reo.data_ptr()), reo_cap, None, P(s.ws.data_ptr()),
+               s.ws.numel(), s.stream)
+        if lib.cdl_dispatch_layout_aligned(*lay):
+            raise RuntimeError("cdl_dispatch_layout_aligned failed")
+        torch.cuda.synchronize()
+        Rp = int(seg[L].item())                       # padded rows, sized exactly
+        out = torch.empty(max(Rp, 1), H, dtype=torch.bfloat16, device=dev)
+        a_al = (P(s.x.data_ptr()), T, H, k, P(s.ids.data_ptr()), 0, L, A, P(cnt.data_ptr()),
+                P(seg.data_ptr()), P(s2d.data_ptr()), P(reo.data_ptr()), reo_cap,
+                P(out.data_ptr()), Rp, P(s.status.data_ptr()), P(s.ws.data_ptr()), s.ws.numel(),
+                s.stream)
+        q = torch.empty(max(Rp, 1), H, dtype=u8, device=dev)
+        sb = torch.empty(max(cdl.fp8_scale_bytes(Rp, H, flags, Rp), 1), dtype=u8, device=dev)
+        a_f8 = (P(s.x.data_ptr()), T, H, k, P(s.ids.data_ptr()), 0, L, A, P(cnt.data_ptr()),
+                P(seg.data_ptr()), P(s2d.data_ptr()), P(reo.data_ptr()), reo_cap, P(q.data_ptr()),
+                P(sb.data_ptr()), flags, Rp, P(s.status.data_ptr()), P(s.ws.data_ptr()),
+                s.ws.numel(), s.stream)
+        bufs.append((s, a_rank, a_al, a_f8, Rp, (ntr, ntn, nte, itr, rws, cnt, seg, s2d, reo, out, q, sb)))
+
+    def call(name, fn):
+        def f(b):
+            if fn(*b):
+                raise RuntimeError(name + " failed")
+        return f
+
+    ms_rank, _ = time_steps(torch, bufs, lambda b: call("cdl_rank_layout", lib.cdl_rank_layout)(b[1]), steps, 5)
+    ms_al, _ = time_steps(torch, bufs, lambda b: call("cdl_permute", lib.cdl_permute)(b[2]), steps, 5)
+    ms_f8, _ = time_steps(torch, bufs, lambda b: call("cdl_permute_fp8", lib.cdl_permute_fp8)(b[3]), steps, 5)
+    if sum(int(b[0].status.item()) for b in bufs):
+        raise SystemExit("device status word set in the next-row measurements")
+    G = sets[0].H // 128
+    al_bytes = statistics.mean(b[0].bytes_layout() + 4 * (b[4] - b[0].R) + 2 * b[0].U * b[0].H
+                               + 2 * b[0].R * b[0].H for b in bufs)
+    f8_bytes = statistics.mean(b[0].bytes_layout() + 4 * (b[4] - b[0].R) + 2 * b[0].U * b[0].H
+                               + b[0].R * (b[0].H + 4 * ((G + 3) // 4)) for b in bufs)
+    s0 = sets[0]
+    rank_bytes = 4 * s0.T * s0.k + s0.T * R_RANKS + 4 * (R_RANKS + R_RANKS // RPN + E)
+    return {"workload": "dsv3_prefill shape (T=4096, H=7168, 32 of 256 experts, top-8)",
+            "rank_layout_us": ms_rank * 1e3,
+            "rank_layout_gbps": rank_bytes / (ms_rank * 1e-3) / 1e9,
+            "rank_layout_config": "8 ranks, 1 node, 256 experts",
+            "permute_aligned128_us": ms_al * 1e3,
+            "permute_aligned128_gbps": al_bytes / (ms_al * 1e-3) / 1e9,
+            "permute_fp8_deepgemm_us": ms_f8 * 1e3,
+            "permute_fp8_deepgemm_gbps": f8_bytes / (ms_f8 * 1e-3) / 1e9,
+            "fp8_deepgemm_format": "segments padded to 128, UE8M0 exponents packed 4 per int32, "
+                                   "column-major, TMA-aligned"}
+
+
 def measure_ll(torch, cdl, W, dev, steps):
     w = W.WORKLOADS["ll_decode"]
     lib = cdl.library()
@@ -326,7 +403,19 @@ def measure_ll(torch, cdl, W, dev, steps):
                  P(base.reorder.data_ptr()), base.reorder.numel(), w.cap, P(B.data_ptr()),
                  P(mm.data_ptr()), P(llm.data_ptr()), P(base.status.data_ptr()),
                  P(base.ws.data_ptr()), base.ws.numel(), base.stream)
-        runs.append((base, a_ll, a_cb, B, mm, llm, a_pll))
+        # the same dispatch with fp8 rows, UE8M0 exponents packed four to a
+        # word, column-major per expert (the DeepGEMM masked-GEMM format)
+        f8 = cdl.FP8_SCALE_UE8M0 | cdl.FP8_SCALE_COLMAJOR | cdl.FP8_SCALE_PACKED
+        Bq = torch.empty(w.L, w.cap, w.H, dtype=torch.uint8, device=dev)
+        Bs = torch.empty(cdl.fp8_scale_bytes(w.L * w.cap, w.H, f8, w.cap), dtype=torch.uint8,
+                         device=dev)
+        a_pll8 = (P(base.x.data_ptr()), w.T, w.H, w.k, P(base.ids.data_ptr()), w.expert_begin,
+                  w.L, P(base.counts.data_ptr()), P(base.seg.data_ptr()),
+                  P(base.src2dst.data_ptr()), P(base.reorder.data_ptr()), base.reorder.numel(),
+                  w.cap, P(Bq.data_ptr()), P(Bs.data_ptr()), f8, P(mm.data_ptr()),
+                  P(llm.data_ptr()), P(base.status.data_ptr()), P(base.ws.data_ptr()),
+                  base.ws.numel(), base.stream)
+        runs.append((base, a_ll, a_cb, B, mm, llm, a_pll, a_pll8, Bq, Bs))
 
     def fn(r):
         if lib.cdl_permute_ll(*r[6]) or lib.cdl_combine(*r[2]):
@@ -337,6 +426,16 @@ def measure_ll(torch, cdl, W, dev, steps):
         if lib.cdl_dispatch_ll(*r[1]) or lib.cdl_combine(*r[2]):
             raise RuntimeError("low-latency step failed")
 
+    def dispatch_bf16(r):
+        if lib.cdl_permute_ll(*r[6]):
+            raise RuntimeError("cdl_permute_ll failed")
+
+    def dispatch_fp8(r):
+        if lib.cdl_permute_ll_fp8(*r[7]):
+            raise RuntimeError("cdl_permute_ll_fp8 failed")
+
+    ms_d16, _ = time_steps(torch, runs, dispatch_bf16, steps, 5)
+    ms_d8, _ = time_steps(torch, runs, dispatch_fp8, steps, 5)
     ms, _ = time_steps(torch, runs, fn, steps, 5)
     ms_sep, _ = time_steps(torch, runs, fn_separate, steps, 5)
     ms_graph = ll_graph_step(torch, lib, runs, steps)
@@ -348,6 +447,9 @@ def measure_ll(torch, cdl, W, dev, steps):
             "us_per_step": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9,
             "us_per_step_separate_calls": ms_sep * 1e3,
             "us_per_step_hip_graph": ms_graph * 1e3,
+            "us_dispatch_one_call": ms_d16 * 1e3,
+            "us_dispatch_fp8_one_call": ms_d8 * 1e3,
+            "fp8_format": "UE8M0 exponents packed 4 per int32, column-major per expert",
             "expected_m": cdl.ll_expected_m(w.T, w.num_ranks, w.k, w.E)}
 
 
@@ -502,6 +604,11 @@ def main():
             r = measure_fp8(torch, cdl, fsets, args.steps)
         elif args.only == "ll_decode":
             r = measure_ll(torch, cdl, W, dev, args.steps)
+        elif args.only == "next_rows":
+            wn = W.WORKLOADS["dsv3_prefill"]
+            nsets = [NormalSet(torch, cdl, W, wn.scaled(seed_base=wn.seed_base + 7919 * i), dev)
+                     for i in range(args.sets)]
+            r = measure_next_rows(torch, cdl, nsets, wn.E, args.steps)
         else:
             r = measure_zipf(torch, cdl, W, dev, args.steps)
         print(json.dumps({"only": args.only, **r}), flush=True)
@@ -570,6 +677,7 @@ def main():
             "fp8_dispatch": measure_fp8(torch, cdl, sets, args.steps),
             "ll_decode": measure_ll(torch, cdl, W, dev, args.steps),
             "zipf_prefill": measure_zipf(torch, cdl, W, dev, max(args.steps // 4, 10)),
+            "next_rows": measure_next_rows(torch, cdl, sets, w.E, args.steps),
         }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")

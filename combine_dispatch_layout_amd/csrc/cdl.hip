@@ -899,7 +899,80 @@ __global__ __launch_bounds__(128) void scatter_rows_u16(
 // rank layout (before the exchange)
 // ---------------------------------------------------------------------------
 
-constexpr int kRankThreads = 256;        // tokens per workgroup, one per thread
+constexpr int kRankThreads = 64;         // tokens per workgroup (one wave), one per thread
+constexpr int kRankMaskMax = 64;         // ranks a token's bitmask holds (the fast kernel)
+
+// Per-workgroup partial counts for num_ranks <= 64, one wave per workgroup:
+// the token's ids arrive in batches of 8 loads, its ranks and nodes are bit
+// masks (a rank or node is counted once per token however many of the
+// token's slots it hosts), the per-rank and per-node counts of the wave are
+// ballots, and the expert counts an LDS histogram.  Same partial layout as
+// below.
+__global__ __launch_bounds__(kRankThreads) void rank_layout_mask_kernel(
+    const int32_t *__restrict__ ids, int64_t T, int32_t k, int32_t E, int32_t R, int32_t rpn,
+    uint8_t *__restrict__ in_rank, int32_t *__restrict__ partial)
+{
+    extern __shared__ int32_t h[];
+    const int N = R / rpn;
+    const int W = E + R + N;
+    const int lane = threadIdx.x;
+    for (int i = lane; i < E; i += kRankThreads) h[i] = 0;
+    __syncthreads();
+    const int64_t t0 = (int64_t)blockIdx.x * kRankThreads;
+    const int64_t t = t0 + lane;
+    const bool real = t < T;
+    const int32_t epr = E / R;
+    // one descriptor for the workgroup's ids (a per-lane one would make the
+    // compiler loop over the lanes' descriptors); lane offsets select tokens
+    const int64_t ntok = T - t0 < kRankThreads ? T - t0 : kRankThreads;
+    const rsrc_t r_ids = make_rsrc(ids + t0 * k, (uint32_t)(ntok * k * 4));
+    const uint32_t my_off = (uint32_t)(lane * k) * 4u;
+    uint64_t rmask = 0, nmask = 0;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        int32_t idv[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) idv[q] = buf_ld4(r_ids, my_off + (uint32_t)(j0 + q) * 4u, 0);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int32_t id = idv[q];
+            if (!real || j0 + q >= k || id < 0 || id >= E) continue;
+            atomicAdd(&h[id], 1);
+            const int32_t r = id / epr;
+            rmask |= 1ull << r;
+            nmask |= 1ull << (r / rpn);
+        }
+    }
+    if (real) {
+        uint8_t *row = in_rank + t * R;
+        if (R % 8 == 0 && ((uintptr_t)in_rank & 7) == 0) {
+            // eight flags per 8-byte store
+            for (int r0 = 0; r0 < R; r0 += 8) {
+                const uint32_t b = (uint32_t)(rmask >> r0) & 0xFFu;
+                uint64_t wv = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wv |= (uint64_t)((b >> i) & 1u) << (8 * i);
+                *reinterpret_cast<uint64_t *>(row + r0) = wv;
+            }
+        } else {
+            for (int r = 0; r < R; ++r) row[r] = (uint8_t)((rmask >> r) & 1u);
+        }
+    }
+    // lane r < R ends up with rank r's count, lane n < N with node n's
+    int32_t rc = 0, nc = 0;
+    for (int r = 0; r < R; ++r) {
+        const int32_t c = __popcll(__ballot((rmask >> r) & 1u));
+        if (lane == r) rc = c;
+    }
+    for (int n = 0; n < N; ++n) {
+        const int32_t c = __popcll(__ballot((nmask >> n) & 1u));
+        if (lane == n) nc = c;
+    }
+    int32_t *out = partial + (int64_t)blockIdx.x * W;
+    if (lane < R) out[E + lane] = rc;
+    if (lane < N) out[E + R + lane] = nc;
+    __syncthreads();
+    for (int i = lane; i < E; i += kRankThreads) out[i] = h[i];
+}
 
 // Per-workgroup partial counts: partial[blk][0, E) slots per expert,
 // [E, E+R) tokens per rank, [E+R, E+R+N) tokens per node; each token also
@@ -954,7 +1027,15 @@ __global__ __launch_bounds__(256) void rank_layout_reduce_kernel(
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= W) return;
     int32_t sum = 0;
-    for (int64_t b = 0; b < nblocks; ++b) sum += partial[b * W + i];
+    int64_t b = 0;
+    for (; b + 8 <= nblocks; b += 8) {      // eight independent loads in flight
+        int32_t v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = partial[(b + q) * W + i];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) sum += v[q];
+    }
+    for (; b < nblocks; ++b) sum += partial[b * W + i];
     if (i < E) per_expert[i] = sum;
     else if (i < E + R) per_rank[i - E] = sum;
     else if (per_node) per_node[i - E - R] = sum;
@@ -1483,8 +1564,12 @@ int cdl_rank_layout(const int32_t *topk_ids, int64_t T, int32_t k, int32_t E, in
     const int32_t N = num_ranks / ranks_per_node;
     const int32_t W = E + num_ranks + N;
     if (nblocks > 0) {
-        rank_layout_kernel<<<dim3((unsigned)nblocks), dim3(kRankThreads), (size_t)W * 4, s>>>(
-            topk_ids, T, k, E, num_ranks, ranks_per_node, is_token_in_rank, (int32_t *)ws);
+        if (num_ranks <= kRankMaskMax)
+            rank_layout_mask_kernel<<<dim3((unsigned)nblocks), dim3(kRankThreads), (size_t)E * 4, s>>>(
+                topk_ids, T, k, E, num_ranks, ranks_per_node, is_token_in_rank, (int32_t *)ws);
+        else
+            rank_layout_kernel<<<dim3((unsigned)nblocks), dim3(kRankThreads), (size_t)W * 4, s>>>(
+                topk_ids, T, k, E, num_ranks, ranks_per_node, is_token_in_rank, (int32_t *)ws);
         if ((rc = launch_status()) != CDL_OK) return rc;
     }
     rank_layout_reduce_kernel<<<dim3((unsigned)((W + 255) / 256)), dim3(256), 0, s>>>(

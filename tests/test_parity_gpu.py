@@ -915,8 +915,11 @@ def test_layout_aligned_reorder_capacity_flag():
 
 @pytest.mark.parametrize("name,R,rpn", [("dsv3_prefill", 8, 8), ("dsv3_prefill", 32, 8),
                                         ("ll_decode", 8, 1), ("zipf_prefill", 16, 4),
-                                        ("tiny", 1, 1)])
+                                        ("tiny", 1, 1), ("dsv3_prefill", 64, 16),
+                                        ("dsv3_prefill", 128, 8), ("dsv3_prefill", 4, 2)])
 def test_rank_layout_parity(name, R, rpn):
+    """Up to 64 ranks take the bit-mask kernel (8-byte flag stores when R is a
+    multiple of 8, byte stores otherwise), more ranks the general one."""
     w = W.WORKLOADS[name]
     announce("rank layout %s R=%d rpn=%d" % (name, R, rpn))
     ids = W.make_topk_ids(w).clone()
