@@ -346,11 +346,15 @@ def measure_next_rows(torch, cdl, sets, E, steps):
                 s.stream)
         q = torch.empty(max(Rp, 1), H, dtype=u8, device=dev)
         sb = torch.empty(max(cdl.fp8_scale_bytes(Rp, H, flags, Rp), 1), dtype=u8, device=dev)
+        # workspace with room to stage the column-major scales
+        fws = torch.empty(cdl.permute_fp8_workspace_size(T, k, L, H, flags, Rp), dtype=u8,
+                          device=dev)
         a_f8 = (P(s.x.data_ptr()), T, H, k, P(s.ids.data_ptr()), 0, L, A, P(cnt.data_ptr()),
                 P(seg.data_ptr()), P(s2d.data_ptr()), P(reo.data_ptr()), reo_cap, P(q.data_ptr()),
-                P(sb.data_ptr()), flags, Rp, P(s.status.data_ptr()), P(s.ws.data_ptr()),
-                s.ws.numel(), s.stream)
-        bufs.append((s, a_rank, a_al, a_f8, Rp, (ntr, ntn, nte, itr, rws, cnt, seg, s2d, reo, out, q, sb)))
+                P(sb.data_ptr()), flags, Rp, P(s.status.data_ptr()), P(fws.data_ptr()),
+                fws.numel(), s.stream)
+        bufs.append((s, a_rank, a_al, a_f8, Rp,
+                     (ntr, ntn, nte, itr, rws, cnt, seg, s2d, reo, out, q, sb, fws)))
 
     def call(name, fn):
         def f(b):
@@ -409,13 +413,15 @@ def measure_ll(torch, cdl, W, dev, steps):
         Bq = torch.empty(w.L, w.cap, w.H, dtype=torch.uint8, device=dev)
         Bs = torch.empty(cdl.fp8_scale_bytes(w.L * w.cap, w.H, f8, w.cap), dtype=torch.uint8,
                          device=dev)
+        fws = torch.empty(cdl.permute_fp8_workspace_size(w.T, w.k, w.L, w.H, f8, w.L * w.cap),
+                          dtype=torch.uint8, device=dev)
         a_pll8 = (P(base.x.data_ptr()), w.T, w.H, w.k, P(base.ids.data_ptr()), w.expert_begin,
                   w.L, P(base.counts.data_ptr()), P(base.seg.data_ptr()),
                   P(base.src2dst.data_ptr()), P(base.reorder.data_ptr()), base.reorder.numel(),
                   w.cap, P(Bq.data_ptr()), P(Bs.data_ptr()), f8, P(mm.data_ptr()),
-                  P(llm.data_ptr()), P(base.status.data_ptr()), P(base.ws.data_ptr()),
-                  base.ws.numel(), base.stream)
-        runs.append((base, a_ll, a_cb, B, mm, llm, a_pll, a_pll8, Bq, Bs))
+                  P(llm.data_ptr()), P(base.status.data_ptr()), P(fws.data_ptr()), fws.numel(),
+                  base.stream)
+        runs.append((base, a_ll, a_cb, B, mm, llm, a_pll, a_pll8, Bq, Bs, fws))
 
     def fn(r):
         if lib.cdl_permute_ll(*r[6]) or lib.cdl_combine(*r[2]):

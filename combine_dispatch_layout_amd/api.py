@@ -83,6 +83,8 @@ def library():
         L.cdl_permute_fp8.restype = ctypes.c_int
         L.cdl_rank_layout_workspace_size.argtypes = [i64, i32, i32, i32, i32]
         L.cdl_rank_layout_workspace_size.restype = sz
+        L.cdl_permute_fp8_workspace_size.argtypes = [i64, i32, i32, i64, i32, i64]
+        L.cdl_permute_fp8_workspace_size.restype = sz
         L.cdl_rank_layout.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.cdl_rank_layout.restype = ctypes.c_int
         L.cdl_dispatch.argtypes = [vp, i64, i64, i32, vp, vp, i64, vp, vp]
@@ -274,6 +276,10 @@ def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
     _check_scale_buffer(out_scales, out_q.shape[0], H, scale_flags, out_q.shape[0])
     if status is not None:
         _need(status, "status", torch.int32)
+    if workspace is None and scale_flags & FP8_SCALE_COLMAJOR:
+        # room for the row-major staging of column-major scales
+        ws = torch.empty(permute_fp8_workspace_size(T, k, L, H, scale_flags, out_q.shape[0]),
+                         dtype=torch.uint8, device=x.device)
     rc = library().cdl_permute_fp8(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
                                    lay.alignment, _ptr(lay.counts), _ptr(lay.seg_indptr),
                                    _ptr(lay.src2dst), _ptr(lay.reorder_buf),
@@ -319,6 +325,18 @@ def rank_layout(topk_ids: torch.Tensor, num_experts: int, num_ranks: int,
                                    _ptr(ws), wsb, _stream(dev))
     _check(rc, "cdl_rank_layout")
     return out
+
+
+def permute_fp8_workspace_size(T: int, k: int, L: int, H: int, scale_flags: int,
+                               rows: int) -> int:
+    """Workspace bytes with which permute_fp8 (rows = output rows) and
+    permute_ll_fp8 (rows = L * cap) stage column-major scales row-major and
+    turn them around in a second kernel; the layout workspace size for
+    row-major formats."""
+    n = library().cdl_permute_fp8_workspace_size(T, k, L, H, scale_flags, rows)
+    if n == 0:
+        raise CdlError(-3, "cdl_permute_fp8_workspace_size")
+    return int(n)
 
 
 def fp8_scale_bytes(rows: int, H: int, scale_flags: int = 0, rows_per_mat: int = 0) -> int:
@@ -527,6 +545,9 @@ def permute_ll_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
     ll_map = torch.empty(T * k, dtype=torch.int32, device=x.device)
     if status is not None:
         _need(status, "status", torch.int32)
+    if workspace is None and scale_flags & FP8_SCALE_COLMAJOR:
+        ws = torch.empty(permute_fp8_workspace_size(T, k, L, H, scale_flags, L * int(cap)),
+                         dtype=torch.uint8, device=x.device)
     rc = library().cdl_permute_ll_fp8(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
                                       _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
                                       _ptr(lay.reorder_buf), lay.reorder_buf.numel(), int(cap),

@@ -1282,6 +1282,105 @@ __global__ __launch_bounds__(128) void combine_rows_u16(
 }
 
 // ---------------------------------------------------------------------------
+// column-major scales from a row-major staging copy
+// ---------------------------------------------------------------------------
+
+// Written directly, a column-major scale matrix takes one 4-byte store per
+// row and scale word, each in a different 128-byte line, and a line's 32 rows
+// come from workgroups on every XCD: at the end of the kernel the L2s write
+// back tens of thousands of partial lines (about 9 us at 4096 tokens of
+// H = 7168 top-8).  The fused fp8 permutes therefore stage row-major words
+// (`words` 32-bit words per row: fp32 scales, or four packed exponent bytes)
+// and this kernel turns 64 x 64 tiles of them around through LDS, so that
+// both its reads and its writes are whole lines.  Only rows the dispatch
+// wrote are copied: in normal mode the rows [seg_indptr[e], seg_indptr[e] +
+// counts[e]) of each expert (not the alignment padding), in low-latency mode
+// the slots below masked_m; other
+// entries of the output keep their contents, and so do the unused bytes of a
+// last packed word (tail_bytes = groups % 4 used bytes, 0 when full).
+constexpr int kTileRows = 64, kTileWords = 64;
+
+__global__ __launch_bounds__(256) void scales_colmajor_kernel(
+    const uint32_t *__restrict__ stage, int64_t rows, int64_t words, int64_t rows_per_mat,
+    int64_t ld, uint32_t *__restrict__ out, const int64_t *__restrict__ seg_indptr,
+    const int32_t *__restrict__ counts, int32_t L, int32_t alignment,
+    const int32_t *__restrict__ masked_m, int32_t tail_bytes)
+{
+    __shared__ uint32_t tile[kTileWords][kTileRows + 1];
+    __shared__ int32_t use[kTileRows];
+    extern __shared__ int64_t seg_lds[];          // [L + 1] when padded
+    const int64_t r0 = (int64_t)blockIdx.x * kTileRows;
+    const int64_t w0 = (int64_t)blockIdx.y * kTileWords;
+    const int tid = threadIdx.x;
+    const bool padded = !masked_m && alignment > 1;
+    if (padded) {
+        for (int i = tid; i <= L; i += 256) seg_lds[i] = seg_indptr[i];
+        __syncthreads();
+    }
+    if (tid < kTileRows) {
+        const int64_t r = r0 + tid;
+        bool ok = r < rows;
+        if (ok && masked_m) {
+            const int64_t e = r / rows_per_mat;
+            ok = r - e * rows_per_mat < (int64_t)masked_m[e];
+        } else if (ok && !padded) {
+            ok = r < seg_indptr[L];
+        } else if (ok) {
+            // the expert whose padded segment holds r: the last e with
+            // seg_indptr[e] <= r (nondecreasing from 0), searched in LDS
+            ok = r < seg_lds[L];
+            if (ok) {
+                int lo = 0, hi = L - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) / 2;
+                    if (seg_lds[mid] <= r) lo = mid; else hi = mid - 1;
+                }
+                ok = r < seg_lds[lo] + counts[lo];
+            }
+        }
+        use[tid] = ok ? 1 : 0;
+    }
+    const int any = __syncthreads_or(tid < kTileRows ? use[tid] : 0);
+    if (!any) return;
+    // rows in, words along the threads: all 16 loads of a thread issued
+    // before the first is used, through one descriptor for the tile's rows
+    // (an unused entry reads past its range: 0, no memory touched)
+    constexpr int kPer = kTileRows * kTileWords / 256;
+    const int64_t nr = rows - r0 < kTileRows ? rows - r0 : kTileRows;
+    const rsrc_t rs = make_rsrc(stage + r0 * words, (uint32_t)(nr * words * 4));
+    uint32_t vals[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * 256;
+        const int rr = i / kTileWords, ww = i % kTileWords;
+        const bool ok = use[rr] && w0 + ww < words;
+        vals[j] = (uint32_t)buf_ld4(rs, ok ? (uint32_t)((rr * words + w0 + ww) * 4) : 0xFFFFFFFFu, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int i = tid + j * 256;
+        tile[i % kTileWords][i / kTileWords] = vals[j];
+    }
+    __syncthreads();
+    // words out, rows along the threads (consecutive rows of one matrix are
+    // consecutive in a column)
+    for (int i = tid; i < kTileRows * kTileWords; i += 256) {
+        const int ww = i / kTileRows, rr = i % kTileRows;
+        const int64_t w = w0 + ww;
+        if (!use[rr] || w >= words) continue;
+        const int64_t r = r0 + rr;
+        const int64_t mat = (int32_t)r / (int32_t)rows_per_mat;
+        const int64_t o = (mat * words + w) * ld + (r - mat * rows_per_mat);
+        if (tail_bytes && w == words - 1) {
+            uint8_t *ob = reinterpret_cast<uint8_t *>(out + o);
+            for (int b = 0; b < tail_bytes; ++b) ob[b] = (uint8_t)(tile[ww][rr] >> (8 * b));
+        } else {
+            out[o] = tile[ww][rr];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------
 
@@ -1504,6 +1603,43 @@ size_t cdl_fp8_scale_bytes(int64_t rows, int64_t H, int32_t scale_flags, int64_t
     return (size_t)scale_bytes(rows, H, scale_flags, rows_per_mat);
 }
 
+static int64_t scale_words(int64_t H, int32_t flags)
+{
+    const int64_t G = H / CDL_FP8_GROUP;
+    return (flags & CDL_FP8_SCALE_PACKED) ? (G + 3) / 4 : G;
+}
+
+size_t cdl_permute_fp8_workspace_size(int64_t T, int32_t k, int32_t L, int64_t H,
+                                      int32_t scale_flags, int64_t rows)
+{
+    if (check_tk(T, k) != CDL_OK || L < 1 || L > CDL_MAX_LOCAL_EXPERTS) return 0;
+    if (H < CDL_FP8_GROUP || H > CDL_MAX_HIDDEN || H % CDL_FP8_GROUP != 0 || rows < 0) return 0;
+    if (!valid_scale_flags(scale_flags)) return 0;
+    const size_t base = layout_ws_bytes(T, k, L);
+    if (!(scale_flags & CDL_FP8_SCALE_COLMAJOR)) return base;
+    const size_t stage = (size_t)rows * (size_t)scale_words(H, scale_flags) * 4;
+    return base + ((stage + 255) & ~(size_t)255);
+}
+
+// The column-major scales of a staged dispatch (scales_colmajor_kernel).
+static int launch_scales_colmajor(const void *stage, int64_t rows, int64_t H, int32_t flags,
+                                  int64_t rows_per_mat, void *out, const int64_t *seg_indptr,
+                                  const int32_t *counts, int32_t L, int32_t alignment,
+                                  const int32_t *masked_m, hipStream_t s)
+{
+    if (rows <= 0) return CDL_OK;
+    const int64_t words = scale_words(H, flags);
+    const int64_t G = H / CDL_FP8_GROUP;
+    const int32_t tail = (flags & CDL_FP8_SCALE_PACKED) ? (int32_t)(G % 4) : 0;
+    const dim3 grid((unsigned)((rows + kTileRows - 1) / kTileRows),
+                    (unsigned)((words + kTileWords - 1) / kTileWords));
+    const size_t lds = (!masked_m && alignment > 1) ? (size_t)(L + 1) * sizeof(int64_t) : 0;
+    scales_colmajor_kernel<<<grid, dim3(256), lds, s>>>(
+        (const uint32_t *)stage, rows, words, rows_per_mat, (rows_per_mat + 3) / 4 * 4,
+        (uint32_t *)out, seg_indptr, counts, L, alignment, masked_m, tail);
+    return launch_status();
+}
+
 int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
                     int32_t expert_begin, int32_t L, int32_t alignment, int32_t *counts,
                     int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
@@ -1524,9 +1660,21 @@ int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
                                 src2dst, reorder_topk_ids, reorder_cap, status);
     a.x = (const u32x4 *)x;
     a.chunks = H / 8;
-    a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap_rows);
     a.cap_rows = cap_rows;
-    return run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
+    const bool staged = (scale_flags & CDL_FP8_SCALE_COLMAJOR) && cap_rows > 0 &&
+                        ws_bytes >= cdl_permute_fp8_workspace_size(T, k, L, H, scale_flags, cap_rows);
+    if (!staged) {
+        a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap_rows);
+        return run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
+    }
+    // row-major staging after the layout's part of the workspace, then the
+    // column-major matrix (one matrix of cap_rows rows)
+    void *stage = (uint8_t *)ws + layout_ws_bytes(T, k, L);
+    a.fp8 = make_fp8_out(out_q, stage, scale_flags & ~CDL_FP8_SCALE_COLMAJOR, H, cap_rows);
+    rc = run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
+    if (rc != CDL_OK) return rc;
+    return launch_scales_colmajor(stage, cap_rows, H, scale_flags, cap_rows, out_scales, seg_indptr,
+                                  counts, L, alignment, nullptr, (hipStream_t)stream);
 }
 
 static int check_rank_layout_sizes(int64_t T, int32_t k, int32_t E, int32_t R, int32_t rpn)
@@ -1704,8 +1852,21 @@ int cdl_permute_ll_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
     if (H % CDL_FP8_GROUP != 0 || !valid_scale_flags(scale_flags)) return CDL_ERR_UNSUPPORTED;
     if (cap > 0 && !out_scales) return CDL_ERR_NULL_POINTER;
     if (cap > 0 && (!aligned(out_q, 8) || !aligned(out_scales, 4))) return CDL_ERR_UNSUPPORTED;
-    a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap);
-    return run_layout<kRowsLLFp8>(a, ws, (hipStream_t)stream);
+    const int64_t rows = (int64_t)L * cap;
+    const bool staged = (scale_flags & CDL_FP8_SCALE_COLMAJOR) && rows > 0 &&
+                        ws_bytes >= cdl_permute_fp8_workspace_size(T, k, L, H, scale_flags, rows);
+    if (!staged) {
+        a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap);
+        return run_layout<kRowsLLFp8>(a, ws, (hipStream_t)stream);
+    }
+    // row-major staging of the L * cap padded rows, then one column-major
+    // matrix per expert
+    void *stage = (uint8_t *)ws + layout_ws_bytes(T, k, L);
+    a.fp8 = make_fp8_out(out_q, stage, scale_flags & ~CDL_FP8_SCALE_COLMAJOR, H, cap);
+    rc = run_layout<kRowsLLFp8>(a, ws, (hipStream_t)stream);
+    if (rc != CDL_OK) return rc;
+    return launch_scales_colmajor(stage, rows, H, scale_flags, cap, out_scales, nullptr, nullptr, L,
+                                  1, masked_m, (hipStream_t)stream);
 }
 
 

@@ -252,11 +252,15 @@ def test_graph_replay_low_latency_step():
         check_layout(lay_g, ids, w.expert_begin, w.L)
 
 
-@pytest.mark.parametrize("flags,cap,T", [(0, 1024, 128), (UE_ | CM_ | PK_, 1024, 128), (UE_ | CM_, 5, 100),
-                                         (0, 256, 2500)])
-def test_permute_ll_fp8_parity(flags, cap, T):
+@pytest.mark.parametrize("flags,cap,T,staged", [(0, 1024, 128, True), (UE_ | CM_ | PK_, 1024, 128, True),
+                                                (UE_ | CM_ | PK_, 1024, 128, False),
+                                                (UE_ | CM_, 5, 100, True), (UE_ | CM_, 5, 100, False),
+                                                (CM_, 256, 2500, True), (0, 256, 2500, True)])
+def test_permute_ll_fp8_parity(flags, cap, T, staged):
     """One-call LL fp8 dispatch; T = 2500 takes the count kernel and 4 tokens
-    per permute workgroup (the fp8 plan)."""
+    per permute workgroup (the fp8 plan).  Column-major scales are staged in
+    the workspace and turned around by a second kernel, or (staged = False,
+    only the layout's workspace) written in place."""
     w = W.WORKLOADS["ll_decode"]
     if T != w.T:
         w = w.scaled(T=T, H=512)
@@ -267,8 +271,11 @@ def test_permute_ll_fp8_parity(flags, cap, T):
     q = torch.zeros(w.L, cap, w.H, dtype=torch.uint8, device=DEV)
     sb = torch.full((max(S.size, 1),), 0xEE, dtype=torch.uint8, device=DEV)
     st = status_word()
+    ws = None if staged else torch.empty(cdl.layout_workspace_size(w.T, w.k, w.L),
+                                         dtype=torch.uint8, device=DEV)
     lay, q, sb, gmm, gll = cdl.permute_ll_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, cap,
-                                              scale_flags=flags, out_q=q, out_scales=sb, status=st)
+                                              scale_flags=flags, out_q=q, out_scales=sb, status=st,
+                                              workspace=ws)
     torch.cuda.synchronize()
     check_layout(lay, ids, w.expert_begin, w.L)
     assert np.array_equal(npy(gmm), mm) and np.array_equal(npy(gll), ll)
@@ -988,15 +995,48 @@ def test_fp8_scale_formats_parity(flags):
     sb = filled_scales(nbytes)
     st = status_word()
     cdl.dispatch_fp8(x.to(DEV), lay, out_q=q, out_scales=sb, status=st, scale_flags=flags)
-    # fused permute
+    # fused permute (column-major formats: staged row-major, then turned
+    # around by a second kernel) ...
     q2 = torch.zeros(cap, w.H, dtype=torch.uint8, device=DEV)
     sb2 = filled_scales(nbytes)
     cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q2, out_scales=sb2,
                     status=st, scale_flags=flags)
+    # ... and with only the layout's workspace: written in place
+    q3 = torch.zeros(cap, w.H, dtype=torch.uint8, device=DEV)
+    sb3 = filled_scales(nbytes)
+    ws = torch.empty(cdl.layout_workspace_size(w.T, w.k, w.L), dtype=torch.uint8, device=DEV)
+    cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q3, out_scales=sb3,
+                    status=st, scale_flags=flags, workspace=ws)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    assert np.array_equal(u8(q), Q) and np.array_equal(u8(q2), Q)
+    assert np.array_equal(u8(q), Q) and np.array_equal(u8(q2), Q) and np.array_equal(u8(q3), Q)
     assert np.array_equal(raw_bytes(sb), S) and np.array_equal(raw_bytes(sb2), S)
+    assert np.array_equal(raw_bytes(sb3), S)
+
+
+@pytest.mark.parametrize("flags", [CM, UE | CM | PK])
+@pytest.mark.parametrize("A", [1, 128])
+def test_permute_fp8_colmajor_staged(flags, A):
+    """Column-major scales staged in the workspace at the fp8 dispatch shape
+    (4096 tokens, count kernel) and with segments padded to 128 rows: every
+    real row's scales land in its column, padding rows, rows past R and the
+    TMA padding of each column keep the fill."""
+    w = W.WORKLOADS["fp8_dispatch"].scaled(H=1152)                   # 9 groups: ragged packing
+    announce("fp8 colmajor staged flags=%d A=%d" % (flags, A))
+    x, ids, wts = W.make_inputs(w)
+    _, s_, d, _ = oracle.layout_aligned(ids.numpy(), w.expert_begin, w.L, A)
+    cap = int(s_[-1]) + 5
+    Q, S = oracle.dispatch_fp8_fmt(W.bf16_bits(x), d, w.k, cap, flags, rows_per_mat=cap, fill=0xEE)
+    q = torch.zeros(cap, w.H, dtype=torch.uint8, device=DEV)
+    sb = filled_scales(cdl.fp8_scale_bytes(cap, w.H, flags, cap))
+    st = status_word()
+    cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q, out_scales=sb,
+                    status=st, scale_flags=flags, alignment=A)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    gq = u8(q)
+    assert np.array_equal(gq[d[d >= 0]], Q[d[d >= 0]])
+    assert np.array_equal(raw_bytes(sb), S)
 
 
 def test_fp8_ue8m0_group_magnitudes():
