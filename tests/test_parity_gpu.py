@@ -563,6 +563,60 @@ def test_permute_parity(w):
     assert np.all(got[R:] == 0x7F7F)
 
 
+def test_full_size_zipf_prefill_permute_sampled():
+    """The Zipf workload at full size through the fused permute and the
+    combine, as timed: exact layout, sampled rows, and the all-local softmax
+    round trip combine(permute(x)) == x for every token."""
+    w = W.WORKLOADS["zipf_prefill"]
+    announce("full zipf_prefill permute")
+    x, ids, wts = W.make_inputs(w)
+    st = status_word()
+    lay, rows = cdl.permute(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, status=st)
+    out = cdl.combine(rows, lay.src2dst, wts.to(DEV), status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    _, s_, d, _ = check_layout(lay, ids, w.expert_begin, w.L)
+    assert int(s_[-1]) == w.T * w.k
+    xb = W.bf16_bits(x)
+    slots = np.random.default_rng(2).choice(w.T * w.k, 4096, replace=False)
+    got = bits16(rows[torch.from_numpy(d[slots].astype(np.int64)).to(DEV)])
+    assert np.array_equal(got, xb[slots // w.k])
+    assert np.array_equal(bits16(out), xb)
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_permute_many_superblocks(fp8):
+    """2^19 tokens of top-8 over 32 of 256 experts: hundreds of superblocks,
+    so every permute workgroup reads its superblock counts and recounts its
+    superblock's earlier slots in several rounds; layout, rows (and for bf16
+    the combine) against the oracle."""
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=1 << 19, H=128 if fp8 else 64)
+    announce("permute many superblocks T=%d fp8=%d" % (w.T, fp8))
+    x, ids, wts = W.make_inputs(w)
+    c, s_, d, r = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s_[-1])
+    st = status_word()
+    xb = W.bf16_bits(x)
+    if fp8:
+        lay, q, sc = cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, rows=R,
+                                     status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        check_layout(lay, ids, w.expert_begin, w.L)
+        Q, S = oracle.dispatch_fp8(xb, d, w.k, R)
+        assert np.array_equal(u8(q), Q)
+        assert np.array_equal(npy(sc).view(np.uint32), S.view(np.uint32))
+        return
+    lay, rows = cdl.permute(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, rows=R, status=st)
+    out = cdl.combine(rows, lay.src2dst, wts.to(DEV), status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    check_layout(lay, ids, w.expert_begin, w.L)
+    P = oracle.dispatch(xb, d, w.k, R)
+    assert np.array_equal(bits16(rows), P)
+    assert np.array_equal(bits16(out), oracle.combine(P, d, wts.numpy(), w.T, w.k))
+
+
 def test_permute_default_capacity_and_repeat():
     """rows defaults to T*k (no host sync); two calls give identical bits."""
     w = W.WORKLOADS["zipf_prefill"].scaled(T=3000, H=512)
