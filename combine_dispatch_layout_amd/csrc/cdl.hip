@@ -280,6 +280,8 @@ constexpr int kMaxChunksFp8 = 14;       // the same for rows quantised on the wa
                                         // H = 7168; quantised kFp8Part chunks at a time)
 constexpr int kCountThreads = 256;
 constexpr int kSelfCountIds = 8;        // ids per thread when workgroups count every slot
+constexpr int kFp8WavesSmall = 7;       // waves per token for fp8 rows of small self-counted
+                                        // batches (2 chunks per lane each)
 
 struct Plan {
     int64_t n;            // slots, T * k
@@ -534,7 +536,8 @@ struct PermuteArgs {
     int32_t *ll_src2dst;
 };
 
-// One workgroup per TPB tokens, one wave per token.
+// One workgroup per TPB tokens, WPT waves per token (wave h of a token moves
+// the chunks [h * NC * 64, (h + 1) * NC * 64) of each pass of its row).
 //  0. every thread loads its first batch of layout operands, then the wave
 //     of token t loads its row (all NC chunks per lane; the first part in
 //     fp8 modes) if the token has a valid slot;
@@ -554,19 +557,21 @@ struct PermuteArgs {
 // ALL_ROWS (small self-counted batches): every token's row is loaded at once,
 // without first reading the token's ids to see whether it has a local slot,
 // so the row and the ids arrive together instead of one after the other.
-template <int TPB, int MODE, bool ALL_ROWS>
-__global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
+template <int TPB, int MODE, bool ALL_ROWS, int WPT>
+__global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
 {
-    constexpr int NT = TPB * kWave;
+    constexpr int NW = TPB * WPT;         // waves
+    constexpr int NT = NW * kWave;
     constexpr bool kFp8Mode = MODE == kRowsFp8 || MODE == kRowsLLFp8;
     constexpr bool kLLMode = MODE == kRowsLL || MODE == kRowsLLFp8;
-    constexpr int NC = kFp8Mode ? kMaxChunksFp8 : kMaxChunks;
+    static_assert((kFp8Mode ? kMaxChunksFp8 : kMaxChunks) % WPT == 0, "chunks split over waves");
+    constexpr int NC = (kFp8Mode ? kMaxChunksFp8 : kMaxChunks) / WPT;
     extern __shared__ int32_t lds[];
     const int L = a.L;
     int32_t *tot = lds;
     int32_t *cur = lds + L;
     int32_t *dsts = lds + 2 * L;          // [TPB * k]
-    __shared__ int32_t scan_tmp[TPB];
+    __shared__ int32_t scan_tmp[NW];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -604,7 +609,12 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     const int my_rel = wave * kWave + lane;
     const int32_t my_id = buf_ld4(r_my, (uint32_t)my_rel * 4u, 0);
 
-    const int64_t t = t_begin + wave;
+    // WPT waves per token: wave h of token t moves the row chunks
+    // [h * NC * 64, (h + 1) * NC * 64) of each pass of WPT * NC * 64 chunks
+    const int64_t t = t_begin + wave / WPT;
+    const int h = wave % WPT;
+    const int64_t c_first = (int64_t)h * NC * kWave;
+    const uint32_t hoff = (uint32_t)(c_first * 16);
     // low latency: lane j < k holds the local expert of this wave's slot j
     // (loaded ahead of the row, so that reading it does not wait for the row)
     int32_t ll_e = -1;
@@ -630,12 +640,12 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
     const rsrc_t xr = make_rsrc(a.x + (tok_valid ? t * a.chunks : 0), tok_valid ? row_bytes : 0u);
     if (MODE != kLayoutOnly && (ALL_ROWS || tok_valid)) {
         if (kFp8Mode) {
-            load_fp8_first_parts(v, xr, voff, 0);
+            load_fp8_first_parts(v, xr, voff, hoff);
         } else {
             // source rows are read once: streaming loads leave the Infinity
             // Cache to the permuted rows, which the combine reads back
 #pragma unroll
-            for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, u * kWave * 16);
+            for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, hoff + u * kWave * 16);
         }
     }
 
@@ -703,7 +713,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
                 R = __builtin_amdgcn_readlane(incl, kWave - 1);
             }
         } else {
-            excl = block_exclusive_scan<TPB>(run, scan_tmp, &R);
+            excl = block_exclusive_scan<NW>(run, scan_tmp, &R);
         }
         for (int q = 0; q < per && e0 + q < L; ++q) {
             const int e = e0 + q;
@@ -764,7 +774,7 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
         // expert's capacity are dropped
         bool ovf = false;
         if (t < a.T && lane < k) {
-            const int32_t d = dsts[wave * k + lane];
+            const int32_t d = dsts[(wave / WPT) * k + lane];
             if (d >= 0) {
                 const int64_t slot = (int64_t)d - tot[ll_e];
                 if (slot < a.ll_cap)
@@ -772,17 +782,17 @@ __global__ __launch_bounds__(TPB *kWave) void permute_kernel(PermuteArgs a)
                 else
                     ovf = true;
             }
-            a.ll_src2dst[t * k + lane] = dlane;
+            if (h == 0) a.ll_src2dst[t * k + lane] = dlane;
         }
         if (__ballot(ovf) != 0 && lane == 0) set_status(a.status, CDL_STATUS_LL_OVERFLOW);
     }
     if (!tok_valid) return;
-    if (!kLLMode) dlane = lane < k ? dsts[wave * k + lane] : -1;
-    for (int64_t c0 = 0; c0 < a.chunks; c0 += (int64_t)NC * kWave) {
+    if (!kLLMode) dlane = lane < k ? dsts[(wave / WPT) * k + lane] : -1;
+    for (int64_t c0 = c_first; c0 < a.chunks; c0 += (int64_t)WPT * NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
-        if (c0 > 0 && kFp8Mode) {
+        if (c0 > c_first && kFp8Mode) {
             load_fp8_first_parts(v, xr, voff, pass);
-        } else if (c0 > 0) {
+        } else if (c0 > c_first) {
 #pragma unroll
             for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, pass + u * kWave * 16);
         }
@@ -1460,16 +1470,39 @@ inline int64_t scale_bytes(int64_t rows, int64_t H, int32_t flags, int64_t rows_
     return rows * words * 4;
 }
 
+// Waves per token.  One, except for fp8 rows of small self-counted batches:
+// a row quantised on the way is split over 7 waves of 2 chunks per lane (one
+// 7168-wide row in one part), which shortens each wave's load -> quantise ->
+// store chain while the GPU has SIMDs to spare (low-latency fp8 dispatch of
+// 128 tokens, H = 7168, top-8: 17.0 -> 12.2 us).  Full batches keep one wave
+// per token: at 4096 tokens two waves of 7 chunks took the fused fp8 permute
+// from 22.9 to 28.6 us (twice the waves, not all of them resident).
+template <int MODE, bool ALL_ROWS, int TPB>
+constexpr int waves_per_token()
+{
+    if constexpr ((MODE == kRowsFp8 || MODE == kRowsLLFp8) && ALL_ROWS && TPB <= 2)
+        return kFp8WavesSmall;
+    else
+        return 1;
+}
+
+template <int MODE, bool ALL_ROWS, int TPB>
+void launch_permute_wpt(const PermuteArgs &a, dim3 grid, size_t lds, hipStream_t s)
+{
+    constexpr int WPT = waves_per_token<MODE, ALL_ROWS, TPB>();
+    permute_kernel<TPB, MODE, ALL_ROWS, WPT><<<grid, dim3(TPB * WPT * kWave), lds, s>>>(a);
+}
+
 template <int MODE, bool ALL_ROWS>
 void launch_permute_tpb(const PermuteArgs &a, const Plan &p, hipStream_t s)
 {
     const size_t lds = (size_t)(2 * a.L + p.tpb * a.k) * sizeof(int32_t);
     const dim3 grid((unsigned)(p.nblocks > 0 ? p.nblocks : 1));
     switch (p.tpb) {
-    case 1: permute_kernel<1, MODE, ALL_ROWS><<<grid, dim3(1 * kWave), lds, s>>>(a); break;
-    case 2: permute_kernel<2, MODE, ALL_ROWS><<<grid, dim3(2 * kWave), lds, s>>>(a); break;
-    case 4: permute_kernel<4, MODE, ALL_ROWS><<<grid, dim3(4 * kWave), lds, s>>>(a); break;
-    default: permute_kernel<8, MODE, ALL_ROWS><<<grid, dim3(8 * kWave), lds, s>>>(a); break;
+    case 1: launch_permute_wpt<MODE, ALL_ROWS, 1>(a, grid, lds, s); break;
+    case 2: launch_permute_wpt<MODE, ALL_ROWS, 2>(a, grid, lds, s); break;
+    case 4: launch_permute_wpt<MODE, ALL_ROWS, 4>(a, grid, lds, s); break;
+    default: launch_permute_wpt<MODE, ALL_ROWS, 8>(a, grid, lds, s); break;
     }
 }
 

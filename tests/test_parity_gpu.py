@@ -812,6 +812,48 @@ def test_permute_small_batches_all_rows(T, L, fp8):
     check_layout(lay, ids, w.expert_begin, w.L)
 
 
+@pytest.mark.parametrize("H", [128, 1152, 7168, 8320])
+@pytest.mark.parametrize("T", [1, 64])
+def test_permute_fp8_small_batch_rows_over_waves(T, H):
+    """Small self-counted fp8 batches split each row over 7 waves of 2
+    chunks per lane: one group (only wave 0 has chunks), ragged packing
+    (9 groups), one full 7168-wide pass, and two passes (65 groups).  Normal
+    permute (fp32 scales, canary rows) and low-latency permute (packed
+    column-major UE8M0 scales staged in the workspace) against the oracle."""
+    w = W.WORKLOADS["ll_decode"].scaled(T=T, H=H)
+    announce("fp8 small batch over waves T=%d H=%d" % (T, H))
+    x, ids, wts = W.make_inputs(w)
+    xb = W.bf16_bits(x)
+    _, s_, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s_[-1])
+    st = status_word()
+    q = torch.full((R + 2, H), 0xA5, dtype=torch.uint8, device=DEV)
+    sc = torch.full((R + 2, H // 128), -7.0, dtype=torch.float32, device=DEV)
+    lay, _, _ = cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q[:R],
+                                out_scales=sc[:R], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    check_layout(lay, ids, w.expert_begin, w.L)
+    Q, S = oracle.dispatch_fp8(xb, d, w.k, R)
+    gq, gs = u8(q), npy(sc)
+    assert np.array_equal(gq[:R], Q) and np.array_equal(gs[:R].view(np.uint32), S.view(np.uint32))
+    assert np.all(gq[R:] == 0xA5) and np.all(gs[R:] == -7.0)
+    flags = UE_ | CM_ | PK_
+    cap = 64
+    Q2, S2, mm, ll, ovf = oracle.dispatch_ll_fp8(xb, ids.numpy(), w.expert_begin, w.L, cap, flags,
+                                                 fill=0xEE)
+    q2 = torch.zeros(w.L, cap, H, dtype=torch.uint8, device=DEV)
+    sb = torch.full((max(S2.size, 1),), 0xEE, dtype=torch.uint8, device=DEV)
+    lay2, q2, sb, gmm, gll = cdl.permute_ll_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, cap,
+                                                scale_flags=flags, out_q=q2, out_scales=sb,
+                                                status=st)
+    torch.cuda.synchronize()
+    assert not ovf and int(st.item()) == 0
+    assert np.array_equal(npy(gmm), mm) and np.array_equal(npy(gll), ll)
+    assert np.array_equal(u8(q2).reshape(-1), Q2.reshape(-1))
+    assert np.array_equal(sb.cpu().numpy().reshape(-1)[:S2.size], S2)
+
+
 @pytest.mark.parametrize("T,k,H", [(1, 8, 7168), (512, 8, 7168), (513, 8, 7168), (200, 9, 512),
                                    (100, 8, 9000), (64, 8, 8), (40, 1, 200), (3, 8, 8192)])
 def test_combine_small_batch_kernel(T, k, H):
