@@ -198,7 +198,8 @@ int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
  * different line per scale word and the lines are shared by rows from every
  * XCD).  A workspace of only cdl_dispatch_layout_workspace_size bytes is
  * still accepted and the scales are then written in place; the results are
- * the same.  Equal to cdl_dispatch_layout_workspace_size for row-major
+ * the same.  Small batches (at most 512 tokens and T*k <= 1024) always write
+ * in place: their few scale rows cost less than the second launch.  Equal to cdl_dispatch_layout_workspace_size for row-major
  * formats; 0 for invalid arguments (H not a multiple of 128, bad flags).
  */
 size_t cdl_permute_fp8_workspace_size(int64_t T, int32_t k, int32_t L, int64_t H,
