@@ -513,7 +513,10 @@ def cpu_model():
     return "unknown"
 
 
-def cpu_baseline(W, s, budget_s=12.0, max_reps=8):
+def cpu_baseline(W, s, budget_s=12.0, max_reps=64):
+    """The oracle as it stands, single-threaded, on full steps of the timed
+    workload until about budget_s seconds of CPU work are done (a bounded
+    sample: at least one step, at most max_reps)."""
     import numpy as np  # noqa: F401
     import oracle
 
@@ -539,7 +542,8 @@ def cpu_baseline(W, s, budget_s=12.0, max_reps=8):
                                            for i in range(3)],
             "cpu_model": cpu_model(),
             "sample": "%d full steps (layout+dispatch+combine) of the same T=%d workload, "
-                      "single-threaded C oracle, median" % (len(times), s.T)}
+                      "%.1f s of single-threaded C oracle work, median step" % (
+                          len(times), s.T, sum(times))}
 
 
 def step_spread(torch, sets, fn, steps, warmup, loops=10):
