@@ -961,6 +961,42 @@ def test_permute_aligned_parity(w, A):
     assert np.array_equal(bits16(out), want)
 
 
+def test_full_size_dsv3_aligned_and_deepgemm_fp8():
+    """The bench's NEXT-row configurations at full size (4096 tokens,
+    H = 7168, 32 of 256 experts, top-8, segments padded to 128 rows, output
+    sized to the padded row count): the bf16 permute (padding rows untouched)
+    and the fp8 permute in the DeepGEMM format (packed column-major UE8M0
+    scales staged in the workspace), bit for bit against the oracle."""
+    w = W.WORKLOADS["dsv3_prefill"]
+    A = 128
+    announce("full dsv3_prefill aligned 128 + DeepGEMM fp8")
+    x, ids, wts = W.make_inputs(w)
+    xb = W.bf16_bits(x)
+    c, s_, d, r = oracle.layout_aligned(ids.numpy(), w.expert_begin, w.L, A)
+    Rp = int(s_[-1])
+    buf = bf16_filled(Rp + 2, w.H, 0x7F7F)
+    st = status_word()
+    lay, _ = cdl.permute(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out=buf[:Rp], status=st,
+                         alignment=A)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(npy(lay.seg_indptr), s_) and np.array_equal(npy(lay.src2dst), d)
+    assert np.array_equal(npy(lay.reorder_topk_ids), r)
+    assert np.array_equal(bits16(buf[:Rp]), oracle.dispatch(xb, d, w.k, Rp, fill=0x7F7F))
+    assert np.all(bits16(buf[Rp:]) == 0x7F7F)
+    flags = UE_ | CM_ | PK_
+    Q, S = oracle.dispatch_fp8_fmt(xb, d, w.k, Rp, flags, rows_per_mat=Rp, fill=0xEE)
+    q = torch.zeros(Rp, w.H, dtype=torch.uint8, device=DEV)
+    sb = filled_scales(cdl.fp8_scale_bytes(Rp, w.H, flags, Rp))
+    cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q, out_scales=sb,
+                    status=st, scale_flags=flags, alignment=A)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    real = d[d >= 0]
+    assert np.array_equal(u8(q)[real], Q[real])
+    assert np.array_equal(raw_bytes(sb), S)
+
+
 def test_permute_fp8_aligned_parity():
     w = W.WORKLOADS["fp8_dispatch"].scaled(T=600, H=1024)
     A = 128
