@@ -144,6 +144,30 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None) -> None:
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
+_ROW_DTYPES_2 = (torch.bfloat16, torch.float16, torch.int16)
+_ROW_DTYPES_1 = (torch.uint8, torch.int8, torch.float8_e4m3fn, torch.float8_e5m2)
+
+
+def _rows16(t: torch.Tensor, name: str) -> torch.Tensor:
+    """[n, H] rows of 1- or 2-byte elements viewed as 16-bit words.  The
+    scatter moves bits, so any such dtype is dispatched exactly: bf16 hidden
+    states, or rows already quantised to fp8 per tensor, whose permuted
+    buffer stays fp8."""
+    _need_gpu(t, name)
+    if t.dim() != 2:
+        raise ValueError("%s must be [rows, H]" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if t.dtype in _ROW_DTYPES_2:
+        return t.view(torch.int16)
+    if t.dtype in _ROW_DTYPES_1:
+        if t.shape[1] % 2:
+            raise ValueError("%s: rows of 1-byte elements need an even width" % name)
+        return t.view(torch.int16)
+    raise TypeError("%s must have 1- or 2-byte elements (bf16, fp16, fp8, int8), got %s"
+                    % (name, t.dtype))
+
+
 @dataclasses.dataclass
 class Layout:
     """Caller-owned routing layout: the explicit form of the pages' dispatch
@@ -228,25 +252,26 @@ def permute(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int, num_loca
     """Layout + normal-mode scatter in one call (two kernels, one for T*k <= 4096).  `out` holds
     `rows` rows (default T*k + L*(alignment-1), an upper bound on R); the
     first R rows receive the dispatched rows (padding rows are not written).
-    Returns (layout, out)."""
-    _need(x, "x", torch.bfloat16)
+    Returns (layout, out).  x holds bf16 rows, or any 1- or 2-byte element
+    type (rows are copied bit for bit; `out` has x's dtype)."""
+    xw = _rows16(x, "x")
     lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace, alignment)
     T, k, L = lay.T, lay.k, lay.num_local_experts
-    if x.dim() != 2 or x.shape[0] != T:
+    if x.shape[0] != T:
         raise ValueError("x must be [T, H] with T = %d" % T)
-    H = x.shape[1]
     if out is None:
-        out = torch.empty(lay.reorder_buf.numel() if rows is None else int(rows), H,
-                          dtype=torch.bfloat16, device=x.device)
-    _need(out, "out", torch.bfloat16)
-    if out.dim() != 2 or out.shape[1] != H:
-        raise ValueError("out must be [rows, H]")
+        out = torch.empty(lay.reorder_buf.numel() if rows is None else int(rows), x.shape[1],
+                          dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or out.dim() != 2 or out.shape[1] != x.shape[1]:
+        raise ValueError("out must be [rows, H] of x's dtype")
+    ow = _rows16(out, "out")
+    H = xw.shape[1]
     if status is not None:
         _need(status, "status", torch.int32)
-    rc = library().cdl_permute(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
+    rc = library().cdl_permute(_ptr(xw), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
                                lay.alignment, _ptr(lay.counts), _ptr(lay.seg_indptr),
                                _ptr(lay.src2dst), _ptr(lay.reorder_buf), lay.reorder_buf.numel(),
-                               _ptr(out), out.shape[0], _ptr(status), _ptr(ws),
+                               _ptr(ow), ow.shape[0], _ptr(status), _ptr(ws),
                                ws.numel() * ws.element_size(), _stream(x.device))
     _check(rc, "cdl_permute")
     return lay, out
@@ -368,21 +393,23 @@ def new_scale_tensor(rows: int, H: int, scale_flags: int, device, rows_per_mat: 
 def dispatch(x: torch.Tensor, layout: Layout, out: Optional[torch.Tensor] = None,
              rows: Optional[int] = None, status: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Normal-mode scatter: out[src2dst[t*k+j]] = x[t].  Allocates [R, H]
-    (reading R from the device) unless `out` or `rows` is given."""
+    (reading R from the device) unless `out` or `rows` is given.  x holds bf16
+    rows, or any 1- or 2-byte element type (e.g. fp8 rows quantised per
+    tensor): rows are copied bit for bit and `out` has x's dtype."""
     T, k = layout.T, layout.k
-    _need(x, "x", torch.bfloat16)
-    if x.dim() != 2 or x.shape[0] != T:
+    xw = _rows16(x, "x")
+    if x.shape[0] != T:
         raise ValueError("x must be [T, H] with T = %d" % T)
-    H = x.shape[1]
     if out is None:
         n = layout.num_rows() if rows is None else int(rows)
-        out = torch.empty(n, H, dtype=torch.bfloat16, device=x.device)
-    _need(out, "out", torch.bfloat16)
-    if out.dim() != 2 or out.shape[1] != H:
-        raise ValueError("out must be [rows, H]")
+        out = torch.empty(n, x.shape[1], dtype=x.dtype, device=x.device)
+    if out.dtype != x.dtype or out.dim() != 2 or out.shape[1] != x.shape[1]:
+        raise ValueError("out must be [rows, H] of x's dtype")
+    ow = _rows16(out, "out")
+    H = xw.shape[1]
     if status is not None:
         _need(status, "status", torch.int32)
-    rc = library().cdl_dispatch(_ptr(x), T, H, k, _ptr(layout.src2dst), _ptr(out), out.shape[0],
+    rc = library().cdl_dispatch(_ptr(xw), T, H, k, _ptr(layout.src2dst), _ptr(ow), ow.shape[0],
                                 _ptr(status), _stream(x.device))
     _check(rc, "cdl_dispatch")
     return out

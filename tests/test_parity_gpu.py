@@ -617,6 +617,32 @@ def test_permute_many_superblocks(fp8):
     assert np.array_equal(bits16(out), oracle.combine(P, d, wts.numpy(), w.T, w.k))
 
 
+@pytest.mark.parametrize("dtype", [torch.float8_e4m3fn, torch.uint8, torch.float16])
+def test_dispatch_rows_of_other_dtypes(dtype):
+    """Rows already quantised per tensor (the pages keep the permuted buffer
+    in fp8 then) or of any 1- or 2-byte type are dispatched bit for bit, by
+    the fused permute and by the scatter from a layout."""
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=1000, H=512)
+    announce("rows of dtype %s" % dtype)
+    x, ids, wts = W.make_inputs(w)
+    g = torch.Generator().manual_seed(77)
+    raw = torch.randint(0, 256, (w.T, w.H), generator=g, dtype=torch.uint8)
+    xd = raw.view(dtype) if dtype != torch.float16 else W.make_hidden(w).to(torch.float16)
+    words = xd.view(torch.int16).numpy().view(np.uint16)       # the rows as 16-bit words
+    _, s_, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s_[-1])
+    want = oracle.dispatch(words, d, w.k, R)
+    st = status_word()
+    lay, rows = cdl.permute(xd.to(DEV), ids.to(DEV), w.expert_begin, w.L, rows=R, status=st)
+    rows2 = cdl.dispatch(xd.to(DEV), lay, rows=R, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert rows.dtype == dtype and rows2.dtype == dtype and rows.shape == (R, w.H)
+    for r in (rows, rows2):
+        got = r.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, want)
+
+
 def test_permute_default_capacity_and_repeat():
     """rows defaults to T*k (no host sync); two calls give identical bits."""
     w = W.WORKLOADS["zipf_prefill"].scaled(T=3000, H=512)
