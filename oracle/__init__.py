@@ -87,6 +87,8 @@ def lib():
         L.oracle_dispatch_ll.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _i32,
                                          _i32, _i64, _u16p, _i32p, _i32p]
         L.oracle_dispatch_ll.restype = _i32
+        L.oracle_cast_fp8_tensor.argtypes = [_u16p, _i64, ctypes.c_float, _u8p]
+        L.oracle_cast_fp8_tensor.restype = None
         L.oracle_quant_group_fp8.argtypes = [_u16p, _i64, _u8p,
                                              ctypes.POINTER(ctypes.c_float)]
         L.oracle_quant_group_fp8.restype = None
@@ -256,6 +258,29 @@ def quant_group_fp8(x_bits: np.ndarray) -> Tuple[np.ndarray, float]:
     s = ctypes.c_float(0.0)
     lib().oracle_quant_group_fp8(x, x.size, q, ctypes.byref(s))
     return q, s.value
+
+
+def cast_fp8_tensor(x_bits: np.ndarray, scale: float = 1.0) -> np.ndarray:
+    """Per-tensor fp8 cast: e4m3fn_rne(clamp(fl(x / scale), +-448)) of
+    every bf16 value, same shape, uint8."""
+    x = _c(x_bits, np.uint16)
+    q = np.zeros(x.shape, np.uint8)
+    lib().oracle_cast_fp8_tensor(x.reshape(-1), x.size, float(scale), q.reshape(-1))
+    return q
+
+
+def dispatch_fp8_tensor(x_bits: np.ndarray, src2dst: np.ndarray, k: int, rows: int,
+                        scale: float = 1.0, fill: int = 0) -> np.ndarray:
+    """Normal dispatch of per-tensor fp8 rows: Q [rows, H] u8 with
+    Q[src2dst[i]] = cast_fp8_tensor(x[i // k], scale); other rows hold
+    `fill`."""
+    q = cast_fp8_tensor(x_bits, scale)
+    T, H = q.shape
+    Q = np.full((rows, H), fill, np.uint8)
+    d = np.asarray(src2dst).reshape(-1)
+    for i in np.nonzero(d >= 0)[0]:
+        Q[d[i]] = q[i // k]
+    return Q
 
 
 def dispatch_fp8(x_bits: np.ndarray, src2dst: np.ndarray, k: int, rows: int,

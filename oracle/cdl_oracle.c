@@ -370,6 +370,27 @@ int32_t oracle_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k,
     return overflow;
 }
 
+/* Per-tensor fp8 cast of n bf16 values: the permuted buffer of the older
+ * permute is fp8 when the weights are w8a8 per tensor ([0.4.4 diff],
+ * _DeepEPDispatcherImplNormal._deepep_permute: gateup_input is allocated in
+ * the fp8 dtype unless the quantisation is block-wise, and the permute kernel
+ * receives no scale, None, in the place of an input scale).  Reading: the
+ * per-tensor scale s divides every element (s = 1 when none is given), the
+ * quotient is clamped to [-448, 448] (saturation to the largest finite
+ * e4m3fn) and rounded to e4m3fn, ties to even:
+ *   q = e4m3fn_rne(clamp(fl(x / s), -448, 448)),  s > 0 finite. */
+void oracle_cast_fp8_tensor(const uint16_t *x, int64_t n, float s, uint8_t *q)
+{
+    for (int64_t c = 0; c < n; ++c) {
+        float v = oracle_bf16_to_f32(x[c]) / s;
+        if (v > 448.0f)
+            v = 448.0f;
+        if (v < -448.0f)
+            v = -448.0f;
+        q[c] = oracle_e4m3fn_rne(v);
+    }
+}
+
 /* Per-token, per-group fp8 quantisation of one group of n bf16 values
  * ([deepep.py], _DeepEPDispatcherImplNormal.dispatch_a: per-token group quant
  * with a hard-coded group of 128 before a normal fp8 dispatch).  Reading of

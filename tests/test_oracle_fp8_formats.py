@@ -114,3 +114,48 @@ def test_ll_fp8_rows_match_normal_rows(flags):
     assert np.array_equal(mm, mm0) and np.array_equal(ll, ll0) and ovf == ovf0 == 1
     Qn, Sn = oracle.dispatch_fp8_fmt(x, ll, 2, 5 * cap, flags, rows_per_mat=cap, fill=0xEE)
     assert np.array_equal(Q.reshape(5 * cap, -1), Qn) and np.array_equal(S, Sn)
+
+
+# --------------------------------------------------------------------------
+# per-tensor fp8 cast (the w8a8 permuted buffer)
+# --------------------------------------------------------------------------
+
+def test_tensor_cast_golden(golden):
+    rows = golden("fp8_tensor_cast.txt")
+    assert len(rows) >= 15
+    for xb, s, q in rows:
+        got = oracle.cast_fp8_tensor(np.array([int(xb, 16)], np.uint16), float(s))
+        assert int(got[0]) == int(q, 16), (xb, s)
+
+
+def _all_finite_bf16():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    exp = (b >> 7) & 0xFF
+    return b[exp != 0xFF]                                    # no inf / NaN
+
+
+@pytest.mark.parametrize("s", [1.0, 2.0, 0.25, 0.37, 3.0, 1e-3, 2.0 ** -10, 1e4, 0.0123])
+def test_tensor_cast_matches_torch_on_every_bf16(s):
+    """Every finite bf16 value against torch's CPU float32 division, clamp and
+    float8_e4m3fn cast (round to nearest even, sign kept on zero)."""
+    b = _all_finite_bf16()
+    x = torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).float()
+    want = (x / torch.tensor(s, dtype=torch.float32)).clamp(-448.0, 448.0) \
+        .to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.cast_fp8_tensor(b, s), want)
+
+
+def test_tensor_dispatch_rows():
+    """Every destination row of a token carries the token's cast row; other
+    rows keep the fill."""
+    w = W.WORKLOADS["tiny"]
+    x, ids, _ = W.make_inputs(w)
+    xb = W.bf16_bits(x)
+    _, seg, d, _ = oracle.layout(ids.numpy(), 0, w.L)
+    R = int(seg[-1])
+    Q = oracle.dispatch_fp8_tensor(xb, d, w.k, R + 2, scale=0.5, fill=0xEE)
+    q = oracle.cast_fp8_tensor(xb, 0.5)
+    for i in range(w.T * w.k):
+        if d[i] >= 0:
+            assert np.array_equal(Q[d[i]], q[i // w.k])
+    assert np.all(Q[R:] == 0xEE)
