@@ -283,7 +283,12 @@ def measure_fp8(torch, cdl, sets, steps):
                   P(s.counts.data_ptr()), P(s.seg.data_ptr()), P(s.src2dst.data_ptr()),
                   P(s.reorder.data_ptr()), s.T * s.k, P(q.data_ptr()), P(sc.data_ptr()), 0, s.R,
                   P(s.status.data_ptr()), P(s.ws.data_ptr()), s.ws.numel(), s.stream)
-        bufs.append((s, a_scatter, a_perm, q, sc))
+        # per-tensor cast (the w8a8 buffer), no scale given
+        a_tens = (P(s.x.data_ptr()), s.T, s.H, s.k, P(s.ids.data_ptr()), 0, s.L, 1,
+                  P(s.counts.data_ptr()), P(s.seg.data_ptr()), P(s.src2dst.data_ptr()),
+                  P(s.reorder.data_ptr()), s.T * s.k, P(q.data_ptr()), None, s.R,
+                  P(s.status.data_ptr()), P(s.ws.data_ptr()), s.ws.numel(), s.stream)
+        bufs.append((s, a_scatter, a_perm, q, sc, a_tens))
 
     def scatter(b):
         if lib.cdl_dispatch_fp8(*b[1]):
@@ -293,8 +298,14 @@ def measure_fp8(torch, cdl, sets, steps):
         if lib.cdl_permute_fp8(*b[2]):
             raise RuntimeError("cdl_permute_fp8 failed")
 
+    def perm_tensor(b):
+        if lib.cdl_permute_fp8_tensor(*b[5]):
+            raise RuntimeError("cdl_permute_fp8_tensor failed")
+
     ms_s, _ = time_steps(torch, bufs, scatter, steps, 5)
     ms_p, _ = time_steps(torch, bufs, perm, steps, 5)
+    ms_t, _ = time_steps(torch, bufs, perm_tensor, steps, 5)
+    tens_bytes = statistics.mean(x.bytes_layout() + 2 * x.U * x.H + x.R * x.H for x in sets)
     scat_bytes = statistics.mean(4 * x.T * x.k + 2 * x.U * x.H + x.R * (x.H + 4 * x.H // 128)
                                  for x in sets)
     perm_bytes = statistics.mean(x.bytes_layout() + 2 * x.U * x.H + x.R * (x.H + 4 * x.H // 128)
@@ -302,7 +313,10 @@ def measure_fp8(torch, cdl, sets, steps):
     return {"workload": "fp8_dispatch (T=4096, H=7168, 32 of 256 experts, top-8, e4m3fn "
                         "groups of 128)",
             "permute_fp8_us": ms_p * 1e3, "permute_fp8_gbps": perm_bytes / (ms_p * 1e-3) / 1e9,
-            "scatter_fp8_us": ms_s * 1e3, "scatter_fp8_gbps": scat_bytes / (ms_s * 1e-3) / 1e9}
+            "scatter_fp8_us": ms_s * 1e3, "scatter_fp8_gbps": scat_bytes / (ms_s * 1e-3) / 1e9,
+            "permute_fp8_tensor_us": ms_t * 1e3,
+            "permute_fp8_tensor_gbps": tens_bytes / (ms_t * 1e-3) / 1e9,
+            "fp8_tensor_format": "per-tensor cast, no scale (w8a8 permuted buffer)"}
 
 
 def measure_next_rows(torch, cdl, sets, E, steps):

@@ -31,6 +31,7 @@ from .api import (  # noqa: F401
     permute_ll,
     permute_ll_fp8,
     permute_fp8,
+    permute_fp8_tensor,
     permute_fp8_workspace_size,
     rank_layout,
     RankLayout,

@@ -83,6 +83,9 @@ def library():
         L.cdl_permute_fp8.restype = ctypes.c_int
         L.cdl_rank_layout_workspace_size.argtypes = [i64, i32, i32, i32, i32]
         L.cdl_rank_layout_workspace_size.restype = sz
+        L.cdl_permute_fp8_tensor.argtypes = [vp, i64, i64, i32, vp, i32, i32, i32, vp, vp, vp,
+                                             vp, i64, vp, vp, i64, vp, vp, sz, vp]
+        L.cdl_permute_fp8_tensor.restype = ctypes.c_int
         L.cdl_permute_fp8_workspace_size.argtypes = [i64, i32, i32, i64, i32, i64]
         L.cdl_permute_fp8_workspace_size.restype = sz
         L.cdl_rank_layout.argtypes = [vp, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -313,6 +316,44 @@ def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
                                    ws.numel() * ws.element_size(), _stream(x.device))
     _check(rc, "cdl_permute_fp8")
     return lay, out_q, out_scales
+
+
+def permute_fp8_tensor(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
+                       num_local_experts: int, scale: Optional[torch.Tensor] = None,
+                       rows: Optional[int] = None, out_q: Optional[torch.Tensor] = None,
+                       status: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None, alignment: int = 1):
+    """Layout + scatter with every row cast to fp8 per tensor:
+    e4m3fn(clamp(x / scale, +-448)), scale a device fp32 scalar or None for 1
+    (the w8a8 per-tensor permuted buffer).  Returns (layout, q [rows, H] uint8
+    holding e4m3fn bytes)."""
+    _need(x, "x", torch.bfloat16)
+    lay, ws = _new_layout(topk_ids, expert_begin, num_local_experts, workspace, alignment)
+    T, k, L = lay.T, lay.k, lay.num_local_experts
+    if x.dim() != 2 or x.shape[0] != T:
+        raise ValueError("x must be [T, H] with T = %d" % T)
+    H = x.shape[1]
+    n = lay.reorder_buf.numel() if rows is None else int(rows)
+    if out_q is None:
+        out_q = torch.empty(n, H, dtype=torch.uint8, device=x.device)
+    _need(out_q, "out_q", torch.uint8)
+    if out_q.dim() != 2 or out_q.shape[1] != H:
+        raise ValueError("out_q must be [rows, H]")
+    if scale is not None:
+        _need(scale, "scale", torch.float32)
+        if scale.numel() != 1:
+            raise ValueError("scale must hold one value")
+    if status is not None:
+        _need(status, "status", torch.int32)
+    rc = library().cdl_permute_fp8_tensor(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin,
+                                          L, lay.alignment, _ptr(lay.counts),
+                                          _ptr(lay.seg_indptr), _ptr(lay.src2dst),
+                                          _ptr(lay.reorder_buf), lay.reorder_buf.numel(),
+                                          _ptr(out_q), _ptr(scale), out_q.shape[0],
+                                          _ptr(status), _ptr(ws),
+                                          ws.numel() * ws.element_size(), _stream(x.device))
+    _check(rc, "cdl_permute_fp8_tensor")
+    return lay, out_q
 
 
 @dataclasses.dataclass

@@ -239,6 +239,25 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, bool ue8m0, float *scale, 
     return u32x2{lo, hi};
 }
 
+// Per-tensor cast of one 16-byte chunk (8 bf16) to 8 e4m3fn bytes:
+// e4m3_rne(clamp(fl(x / s), +-448)).  POW2: s is a power of two whose inverse
+// inv is a normal float, so x * inv is the exact quotient; otherwise the
+// quotient is a correctly rounded division.
+template <bool POW2>
+__device__ __forceinline__ u32x2 cast_chunk_fp8(u32x4 v, float s, float inv)
+{
+    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float q = POW2 ? f[e] * inv : f[e] / s;
+        f[e] = fminf(fmaxf(q, -448.0f), 448.0f);
+    }
+    const uint32_t lo = pack2_e4m3(f[0], f[1]) | (pack2_e4m3(f[2], f[3]) << 16);
+    const uint32_t hi = pack2_e4m3(f[4], f[5]) | (pack2_e4m3(f[6], f[7]) << 16);
+    return u32x2{lo, hi};
+}
+
 // Where fp8 rows and their scales go.  Scale layouts (CDL_FP8_SCALE_*):
 // row-major fp32 [rows][groups]; column-major: every rows_per_mat rows form a
 // matrix stored [groups][ld], ld = rows_per_mat rounded up to 4; packed: the
@@ -461,7 +480,11 @@ __device__ __forceinline__ void store_fp8_parts(u32x4 (&v)[NCH], int k, int lane
 // layout kernel B (+ fused row scatter): the permute
 // ---------------------------------------------------------------------------
 
-enum PermuteMode { kLayoutOnly = 0, kRowsBf16 = 1, kRowsFp8 = 2, kRowsLL = 3, kRowsLLFp8 = 4 };
+enum PermuteMode {
+    kLayoutOnly = 0, kRowsBf16 = 1, kRowsFp8 = 2, kRowsLL = 3, kRowsLLFp8 = 4,
+    kRowsFp8Tensor = 5,   // per-tensor fp8 cast (no per-row scales), scale from the device
+    kRowsFp8Cast1 = 6     // the same with no scale given (s = 1): no division
+};
 
 // Block-wide exclusive scan of one int32 per thread (NW waves).
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves only: shifts
@@ -526,6 +549,7 @@ struct PermuteArgs {
     int64_t chunks;       // H / 8
     u32x4 *out;           // bf16 rows
     Fp8Out fp8;           // fp8 rows and scales
+    const float *tensor_scale;   // per-tensor fp8 cast: device scalar, NULL = 1
     int64_t cap_rows;
     int32_t *status;
     // small batches: every workgroup counts all slots itself (no count kernel)
@@ -788,6 +812,15 @@ __global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
     }
     if (!tok_valid) return;
     if (!kLLMode) dlane = lane < k ? dsts[(wave / WPT) * k + lane] : -1;
+    // per-tensor cast: a power-of-two scale is applied by its exact inverse
+    // (cast_inv != 0), any other by a correctly rounded division
+    float cast_s = 1.0f, cast_inv = 1.0f;      // kRowsFp8Cast1: s = 1
+    if constexpr (MODE == kRowsFp8Tensor) {
+        cast_s = a.tensor_scale ? *a.tensor_scale : 1.0f;
+        const uint32_t sb = __float_as_uint(cast_s);
+        const uint32_t ef = (sb >> 23) & 0xFFu;
+        cast_inv = ((sb & 0x807FFFFFu) == 0 && ef >= 1 && ef <= 253) ? __uint_as_float((254u - ef) << 23) : 0.0f;
+    }
     for (int64_t c0 = c_first; c0 < a.chunks; c0 += (int64_t)WPT * NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
         if (c0 > c_first && kFp8Mode) {
@@ -796,7 +829,50 @@ __global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
 #pragma unroll
             for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, pass + u * kWave * 16);
         }
-        if (!kFp8Mode) {
+        if constexpr (MODE == kRowsFp8Tensor || MODE == kRowsFp8Cast1) {
+            const uint32_t q_bytes = (uint32_t)(a.chunks * 8);
+            auto row_dst = [&](int j, int u) -> int32_t {
+                const int32_t dst = __builtin_amdgcn_readlane(dlane, j);
+                if (dst >= 0 && (int64_t)dst >= a.cap_rows) {
+                    if (u == 0 && c0 == 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
+                    return -1;
+                }
+                return dst;
+            };
+            if (MODE == kRowsFp8Cast1 || cast_inv != 0.0f) {
+                // exact scaling: the whole row is cast in place (the bytes
+                // replace the first half of each chunk's registers), then
+                // stored to every destination
+#pragma unroll
+                for (int u = 0; u < NC; ++u) {
+                    const u32x2 c = cast_chunk_fp8<true>(v[u], cast_s, cast_inv);
+                    v[u].x = c.x;
+                    v[u].y = c.y;
+                }
+                for (int j = 0; j < k; ++j) {
+                    const int32_t dst = row_dst(j, 0);
+                    if (dst < 0) continue;
+                    const rsrc_t o = make_rsrc(a.fp8.q + (int64_t)dst * a.chunks, q_bytes);
+#pragma unroll
+                    for (int u = 0; u < NC; ++u)
+                        buf_st8_stream(o, u32x2{v[u].x, v[u].y}, (uint32_t)lane * 8u,
+                                       (uint32_t)(c0 * 8) + u * kWave * 8);
+                }
+            } else {
+                // a division per element: one chunk at a time, so that only
+                // one chunk's division temporaries are live
+#pragma unroll
+                for (int u = 0; u < NC; ++u) {
+                    const u32x2 c = cast_chunk_fp8<false>(v[u], cast_s, cast_inv);
+                    for (int j = 0; j < k; ++j) {
+                        const int32_t dst = row_dst(j, u);
+                        if (dst < 0) continue;
+                        const rsrc_t o = make_rsrc(a.fp8.q + (int64_t)dst * a.chunks, q_bytes);
+                        buf_st8_stream(o, c, (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + u * kWave * 8);
+                    }
+                }
+            }
+        } else if constexpr (!kFp8Mode) {
             for (int j = 0; j < k; ++j) {
                 const int32_t dst = __builtin_amdgcn_readlane(dlane, j);
                 if (dst < 0) continue;
@@ -1638,6 +1714,34 @@ int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_
     a.out = (u32x4 *)out;
     a.cap_rows = cap_rows;
     return run_layout<kRowsBf16>(a, ws, (hipStream_t)stream);
+}
+
+int cdl_permute_fp8_tensor(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                           const int32_t *topk_ids, int32_t expert_begin, int32_t L,
+                           int32_t alignment, int32_t *counts, int64_t *seg_indptr,
+                           int32_t *src2dst, int32_t *reorder_topk_ids, int64_t reorder_cap,
+                           uint8_t *out_q, const float *scale, int64_t cap_rows, int32_t *status,
+                           void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_layout_args(topk_ids, T, k, L, alignment, counts, seg_indptr, src2dst,
+                               reorder_topk_ids, reorder_cap, ws, ws_bytes);
+    if (rc != CDL_OK) return rc;
+    if (H < 1 || cap_rows < 0) return CDL_ERR_BAD_SIZE;
+    if (H > CDL_MAX_HIDDEN) return CDL_ERR_TOO_LARGE;
+    if (cap_rows > INT32_MAX) return CDL_ERR_TOO_LARGE;
+    if (T > 0 && !x) return CDL_ERR_NULL_POINTER;
+    if (cap_rows > 0 && !out_q) return CDL_ERR_NULL_POINTER;
+    if (H % 8 != 0 || !aligned(x, 16) || !aligned(out_q, 8) || !aligned(scale, 4))
+        return CDL_ERR_UNSUPPORTED;
+    PermuteArgs a = layout_args(topk_ids, T, k, expert_begin, L, alignment, counts, seg_indptr,
+                                src2dst, reorder_topk_ids, reorder_cap, status);
+    a.x = (const u32x4 *)x;
+    a.chunks = H / 8;
+    a.cap_rows = cap_rows;
+    a.fp8.q = (u32x2 *)out_q;
+    a.tensor_scale = scale;
+    if (!scale) return run_layout<kRowsFp8Cast1>(a, ws, (hipStream_t)stream);
+    return run_layout<kRowsFp8Tensor>(a, ws, (hipStream_t)stream);
 }
 
 size_t cdl_fp8_scale_bytes(int64_t rows, int64_t H, int32_t scale_flags, int64_t rows_per_mat)

@@ -190,6 +190,31 @@ int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
                     int64_t cap_rows, int32_t *status, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * cdl_permute_fp8_tensor -- cdl_permute with the permuted rows cast to fp8
+ * per tensor: the older permute allocates its buffer in the fp8 dtype for
+ * per-tensor w8a8 weights (not block-quantised) and passes its permute kernel
+ * no input scale ([0.4.4 diff], _DeepEPDispatcherImplNormal._deepep_permute:
+ * gateup_input's dtype).  Every element of a dispatched row becomes
+ *     e4m3fn_rne(clamp(fl32(x / s), -448, 448)),
+ * s the per-tensor scale, with no per-row scales written.
+ *
+ *   out_q  out [cap_rows, H] E4M3FN bytes (8-byte aligned); rows at or beyond
+ *          cap_rows are dropped with CDL_STATUS_ROWS_OVERFLOW, padding rows
+ *          are not written
+ *   scale  in  device pointer to one fp32 s > 0 (finite), or NULL for s = 1
+ *          (the pages' None); a power of two is applied exactly through its
+ *          inverse, any other value by a correctly rounded division
+ * Layout arguments, workspace, x, cap_rows and status as for cdl_permute.
+ * Requires H % 8 == 0 and 16-byte aligned x (CDL_ERR_UNSUPPORTED otherwise).
+ */
+int cdl_permute_fp8_tensor(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                           const int32_t *topk_ids, int32_t expert_begin, int32_t L,
+                           int32_t alignment, int32_t *counts, int64_t *seg_indptr,
+                           int32_t *src2dst, int32_t *reorder_topk_ids, int64_t reorder_cap,
+                           uint8_t *out_q, const float *scale, int64_t cap_rows, int32_t *status,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
  * cdl_permute_fp8_workspace_size -- workspace bytes with which
  * cdl_permute_fp8 (rows = cap_rows) and cdl_permute_ll_fp8 (rows = L * cap)
  * write column-major scales through a row-major staging copy in the

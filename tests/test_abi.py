@@ -336,3 +336,24 @@ def test_rank_layout_rejects():
     assert f(FAKE, 16, 2, 256, 8, 1, FAKE, FAKE, NULL, FAKE, FAKE, 1 << 20, NULL) == ENULL
     assert f(FAKE, 16, 2, 256, 8, 1, FAKE, FAKE, FAKE, NULL, FAKE, 1 << 20, NULL) == ENULL
     assert f(FAKE, 16, 2, 256, 8, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 8, NULL) == EWS
+
+
+def test_permute_fp8_tensor_rejects():
+    lib = cdl.library()
+    P = ctypes.c_void_p
+    cnt, seg, s2d, reo, q = FAKE, FAKE, FAKE, FAKE, FAKE
+    ws_b = lib.cdl_dispatch_layout_workspace_size(64, 2, 8)
+
+    def call(x=FAKE, T=64, H=256, k=2, ids=FAKE, L=8, A=1, out=FAKE, scale=None, cap=128,
+             ws=FAKE, wsb=ws_b):
+        return lib.cdl_permute_fp8_tensor(x, T, H, k, ids, 0, L, A, cnt, seg, s2d, reo, 128, out,
+                                          scale, cap, None, ws, wsb, None)
+    assert call(x=NULL) == ENULL
+    assert call(out=NULL) == ENULL
+    assert call(H=12) == EUNSUP                               # H % 8
+    assert call(x=P(0x1008)) == EUNSUP                        # x not 16-byte aligned
+    assert call(out=P(0x1004)) == EUNSUP                      # out_q not 8-byte aligned
+    assert call(scale=P(0x1002)) == EUNSUP                    # scale not 4-byte aligned
+    assert call(cap=-1) == ESIZE
+    assert call(H=(1 << 24) + 8) == EBIG
+    assert call(wsb=16) == EWS

@@ -643,6 +643,54 @@ def test_dispatch_rows_of_other_dtypes(dtype):
         assert np.array_equal(got, want)
 
 
+@pytest.mark.parametrize("scale", [None, 0.5, 0.37, 3.0])
+@pytest.mark.parametrize("w", [W.WORKLOADS["dsv3_prefill"].scaled(T=1000, H=512),
+                               W.WORKLOADS["tiny"],
+                               W.WORKLOADS["ll_decode"].scaled(mode="normal", T=100, H=1024),
+                               W.WORKLOADS["dsv3_prefill"]],
+                         ids=lambda w: "%s_T%d_H%d" % (w.name, w.T, w.H))
+def test_permute_fp8_tensor_parity(w, scale):
+    """Per-tensor fp8 cast on the permute (the w8a8 buffer): no scale (1),
+    a power of two, and two scales that need the division; hidden states
+    scaled by 300 s so that some quotients saturate at +-448.  Rows
+    bit-exact, canary rows untouched."""
+    announce("permute fp8 tensor %s T=%d scale=%s" % (w.name, w.T, scale))
+    x, ids, wts = W.make_inputs(w)
+    x = (x.float() * (300.0 * (1.0 if scale is None else scale))).to(torch.bfloat16)
+    xb = W.bf16_bits(x)
+    _, s_, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s_[-1])
+    want = oracle.dispatch_fp8_tensor(xb, d, w.k, R + 2, 1.0 if scale is None else scale,
+                                      fill=0xA5)
+    assert np.any(want[:R] == 0x7E) and np.any(want[:R] == 0xFE)        # saturated
+    q = torch.full((R + 2, w.H), 0xA5, dtype=torch.uint8, device=DEV)
+    sd = None if scale is None else torch.tensor([scale], dtype=torch.float32, device=DEV)
+    st = status_word()
+    lay, _ = cdl.permute_fp8_tensor(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, scale=sd,
+                                    out_q=q[:R], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    check_layout(lay, ids, w.expert_begin, w.L)
+    assert np.array_equal(u8(q), want)
+
+
+def test_permute_fp8_tensor_rows_overflow():
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=300, H=256)
+    announce("permute fp8 tensor cap < R")
+    x, ids, _ = W.make_inputs(w)
+    _, s_, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s_[-1])
+    cap = R - 7
+    want = oracle.dispatch_fp8_tensor(W.bf16_bits(x), d, w.k, R, fill=0xA5)
+    q = torch.full((R, w.H), 0xA5, dtype=torch.uint8, device=DEV)
+    st = status_word()
+    cdl.permute_fp8_tensor(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q[:cap], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == cdl.CDL_STATUS_ROWS_OVERFLOW
+    got = u8(q)
+    assert np.array_equal(got[:cap], want[:cap]) and np.all(got[cap:] == 0xA5)
+
+
 def test_permute_default_capacity_and_repeat():
     """rows defaults to T*k (no host sync); two calls give identical bits."""
     w = W.WORKLOADS["zipf_prefill"].scaled(T=3000, H=512)
