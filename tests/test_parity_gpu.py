@@ -801,6 +801,12 @@ def test_permute_edge_cases(case):
     got = bits16(buf)
     assert np.array_equal(got[:R], oracle.dispatch(W.bf16_bits(x), d, k, R))
     assert np.all(got[R:] == 0x7F7F)
+    # the same case through the per-tensor fp8 permute (rows cast, canaries kept)
+    q = torch.full((R + 2, H), 0xA5, dtype=torch.uint8, device=DEV)
+    lay2, _ = cdl.permute_fp8_tensor(x.to(DEV), ids.to(DEV), b, L, out_q=q[:R])
+    torch.cuda.synchronize()
+    check_layout(lay2, ids, b, L)
+    assert np.array_equal(u8(q), oracle.dispatch_fp8_tensor(W.bf16_bits(x), d, k, R + 2, fill=0xA5))
 
 
 @pytest.mark.parametrize("w", [W.WORKLOADS["fp8_dispatch"],
