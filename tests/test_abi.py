@@ -357,3 +357,25 @@ def test_permute_fp8_tensor_rejects():
     assert call(cap=-1) == ESIZE
     assert call(H=(1 << 24) + 8) == EBIG
     assert call(wsb=16) == EWS
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/cdl.h compiles as C99 with no HIP or torch header, and a C
+    program links against libcdl.so and calls its pure host functions."""
+    import subprocess
+    src = tmp_path / "use_cdl.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "cdl.h"\n'
+        "int main(void) {\n"
+        "    if (cdl_ll_expected_m(128, 8, 8, 256) != 33) return 1;\n"
+        "    if (cdl_dispatch_layout_workspace_size(4096, 8, 32) == 0) return 2;\n"
+        "    if (cdl_status_string(CDL_OK) == 0) return 3;\n"
+        "    if (cdl_dispatch_layout(0, -1, 8, 0, 32, 0, 0, 0, 0, 0, 0, 0) != CDL_ERR_BAD_SIZE) return 4;\n"
+        '    printf("ok\\n");\n    return 0;\n}\n')
+    exe = tmp_path / "use_cdl"
+    lib_dir = os.path.dirname(cdl.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", lib_dir, "-lcdl",
+                    "-Wl,-rpath," + lib_dir], check=True, capture_output=True, timeout=120)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
