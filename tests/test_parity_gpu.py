@@ -1303,3 +1303,28 @@ def test_ll_fp8_parity(flags, cap):
     assert (int(st.item()) != 0) == bool(ovf)
     assert np.array_equal(u8(q).reshape(-1), Q.reshape(-1))
     assert np.array_equal(raw_bytes(sb), S)
+
+
+def test_calls_on_a_side_stream():
+    """Every call enqueues on torch's current stream: the permute, the
+    combine and the low-latency dispatch issued on a side stream (inputs
+    copied there, nothing synchronised in between) give the oracle's
+    results once that stream is synchronised."""
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=700, H=1024)
+    announce("side stream T=%d" % w.T)
+    x, ids, wts = W.make_inputs(w)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        xd, idd, wd = x.to(DEV, non_blocking=False), ids.to(DEV), wts.to(DEV)
+        lay, rows = cdl.permute(xd, idd, w.expert_begin, w.L)
+        out = cdl.combine(rows, lay.src2dst, wd)
+        lay2, buf, mm, llmap = cdl.permute_ll(xd, idd, w.expert_begin, w.L, 64)
+        out2 = cdl.combine(buf, llmap, wd)
+    side.synchronize()
+    _, s_, d, _ = check_layout(lay, ids, w.expert_begin, w.L)
+    R = int(s_[-1])
+    P = oracle.dispatch(W.bf16_bits(x), d, w.k, R)
+    assert np.array_equal(bits16(rows[:R]), P)
+    want = oracle.combine(P, d, wts.numpy(), w.T, w.k)
+    assert np.array_equal(bits16(out), want)
+    assert np.array_equal(bits16(out2), want)                # LL combine = normal combine
