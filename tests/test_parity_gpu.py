@@ -1328,3 +1328,25 @@ def test_calls_on_a_side_stream():
     want = oracle.combine(P, d, wts.numpy(), w.T, w.k)
     assert np.array_equal(bits16(out), want)
     assert np.array_equal(bits16(out2), want)                # LL combine = normal combine
+
+
+@pytest.mark.parametrize("A", [16, 128])
+def test_permute_fp8_tensor_aligned(A):
+    """Per-tensor fp8 permute with expert segments padded to A rows: the
+    padded layout, real rows bit-exact, padding rows and rows past the
+    padded count untouched."""
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=900, H=256)
+    announce("permute fp8 tensor aligned A=%d" % A)
+    x, ids, _ = W.make_inputs(w)
+    c, s_, d, r = oracle.layout_aligned(ids.numpy(), w.expert_begin, w.L, A)
+    Rp = int(s_[-1])
+    want = oracle.dispatch_fp8_tensor(W.bf16_bits(x), d, w.k, Rp + 3, fill=0xA5)
+    q = torch.full((Rp + 3, w.H), 0xA5, dtype=torch.uint8, device=DEV)
+    st = status_word()
+    lay, _ = cdl.permute_fp8_tensor(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q[:Rp],
+                                    status=st, alignment=A)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(npy(lay.seg_indptr), s_) and np.array_equal(npy(lay.src2dst), d)
+    assert np.array_equal(npy(lay.reorder_topk_ids), r)
+    assert np.array_equal(u8(q), want)
