@@ -147,6 +147,23 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None) -> None:
         raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
 
 
+def _same_device(dev: torch.device, **tensors) -> None:
+    """Every given tensor (None skipped) lives on `dev`: the kernels of one
+    call run on one device and take every pointer as that device's memory."""
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError("%s is on %s, the call's inputs on %s" % (name, t.device, dev))
+
+
+def _need_q_rows(t: torch.Tensor, H: int) -> None:
+    """out_q of the normal-mode fp8 calls: [rows, H] bytes.  The kernels
+    write H bytes per destination row at row * H, up to rows rows, so a
+    narrower buffer would be written past its end."""
+    _need(t, "out_q", torch.uint8)
+    if t.dim() != 2 or t.shape[1] != H:
+        raise ValueError("out_q must be [rows, H] with H = %d, got %s" % (H, tuple(t.shape)))
+
+
 _ROW_DTYPES_2 = (torch.bfloat16, torch.float16, torch.int16)
 _ROW_DTYPES_1 = (torch.uint8, torch.int8, torch.float8_e4m3fn, torch.float8_e5m2)
 
@@ -271,6 +288,7 @@ def permute(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int, num_loca
     H = xw.shape[1]
     if status is not None:
         _need(status, "status", torch.int32)
+    _same_device(x.device, topk_ids=lay.topk_ids, out=out, status=status, workspace=ws)
     rc = library().cdl_permute(_ptr(xw), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
                                lay.alignment, _ptr(lay.counts), _ptr(lay.seg_indptr),
                                _ptr(lay.src2dst), _ptr(lay.reorder_buf), lay.reorder_buf.numel(),
@@ -300,10 +318,12 @@ def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
         out_q = torch.empty(n, H, dtype=torch.uint8, device=x.device)
     if out_scales is None:
         out_scales = new_scale_tensor(out_q.shape[0], H, scale_flags, x.device)
-    _need(out_q, "out_q", torch.uint8)
+    _need_q_rows(out_q, H)
     _check_scale_buffer(out_scales, out_q.shape[0], H, scale_flags, out_q.shape[0])
     if status is not None:
         _need(status, "status", torch.int32)
+    _same_device(x.device, topk_ids=lay.topk_ids, out_q=out_q, out_scales=out_scales,
+                 status=status, workspace=ws)
     if workspace is None and scale_flags & FP8_SCALE_COLMAJOR:
         # room for the row-major staging of column-major scales
         ws = torch.empty(permute_fp8_workspace_size(T, k, L, H, scale_flags, out_q.shape[0]),
@@ -336,15 +356,15 @@ def permute_fp8_tensor(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: in
     n = lay.reorder_buf.numel() if rows is None else int(rows)
     if out_q is None:
         out_q = torch.empty(n, H, dtype=torch.uint8, device=x.device)
-    _need(out_q, "out_q", torch.uint8)
-    if out_q.dim() != 2 or out_q.shape[1] != H:
-        raise ValueError("out_q must be [rows, H]")
+    _need_q_rows(out_q, H)
     if scale is not None:
         _need(scale, "scale", torch.float32)
         if scale.numel() != 1:
             raise ValueError("scale must hold one value")
     if status is not None:
         _need(status, "status", torch.int32)
+    _same_device(x.device, topk_ids=lay.topk_ids, out_q=out_q, scale=scale, status=status,
+                 workspace=ws)
     rc = library().cdl_permute_fp8_tensor(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin,
                                           L, lay.alignment, _ptr(lay.counts),
                                           _ptr(lay.seg_indptr), _ptr(lay.src2dst),
@@ -450,6 +470,7 @@ def dispatch(x: torch.Tensor, layout: Layout, out: Optional[torch.Tensor] = None
     H = xw.shape[1]
     if status is not None:
         _need(status, "status", torch.int32)
+    _same_device(x.device, src2dst=layout.src2dst, out=out, status=status)
     rc = library().cdl_dispatch(_ptr(xw), T, H, k, _ptr(layout.src2dst), _ptr(ow), ow.shape[0],
                                 _ptr(status), _stream(x.device))
     _check(rc, "cdl_dispatch")
@@ -476,10 +497,12 @@ def dispatch_fp8(x: torch.Tensor, layout: Layout, out_q: Optional[torch.Tensor] 
         out_q = torch.empty(n, H, dtype=torch.uint8, device=x.device)
     if out_scales is None:
         out_scales = new_scale_tensor(out_q.shape[0], H, scale_flags, x.device)
-    _need(out_q, "out_q", torch.uint8)
+    _need_q_rows(out_q, H)
     _check_scale_buffer(out_scales, out_q.shape[0], H, scale_flags, out_q.shape[0])
     if status is not None:
         _need(status, "status", torch.int32)
+    _same_device(x.device, src2dst=layout.src2dst, out_q=out_q, out_scales=out_scales,
+                 status=status)
     rc = library().cdl_dispatch_fp8_ex(_ptr(x), T, H, k, _ptr(layout.src2dst), _ptr(out_q),
                                        _ptr(out_scales), int(scale_flags), out_q.shape[0],
                                        _ptr(status), _stream(x.device))
@@ -514,6 +537,7 @@ def dispatch_ll(x: torch.Tensor, layout: Layout, cap: int, out: Optional[torch.T
     ll_map = torch.empty(T * k, dtype=torch.int32, device=x.device)
     if status is not None:
         _need(status, "status", torch.int32)
+    _same_device(x.device, topk_ids=layout.topk_ids, out=out, status=status)
     rc = library().cdl_dispatch_ll(_ptr(x), T, H, k, _ptr(layout.topk_ids), layout.expert_begin,
                                    L, _ptr(layout.src2dst), _ptr(layout.seg_indptr),
                                    _ptr(layout.counts), int(cap), _ptr(out), _ptr(masked_m),
@@ -548,6 +572,8 @@ def dispatch_ll_fp8(x: torch.Tensor, layout: Layout, cap: int, scale_flags: int 
     ll_map = torch.empty(T * k, dtype=torch.int32, device=x.device)
     if status is not None:
         _need(status, "status", torch.int32)
+    _same_device(x.device, topk_ids=layout.topk_ids, out_q=out_q, out_scales=out_scales,
+                 status=status)
     rc = library().cdl_dispatch_ll_fp8(_ptr(x), T, H, k, _ptr(layout.topk_ids),
                                        layout.expert_begin, L, _ptr(layout.src2dst),
                                        _ptr(layout.seg_indptr), _ptr(layout.counts), int(cap),
@@ -576,6 +602,7 @@ def permute_ll(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
     ll_map = torch.empty(T * k, dtype=torch.int32, device=x.device)
     if status is not None:
         _need(status, "status", torch.int32)
+    _same_device(x.device, topk_ids=lay.topk_ids, out=out, status=status, workspace=ws)
     rc = library().cdl_permute_ll(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
                                   _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
                                   _ptr(lay.reorder_buf), lay.reorder_buf.numel(), int(cap),
@@ -616,6 +643,8 @@ def permute_ll_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
     if workspace is None and scale_flags & FP8_SCALE_COLMAJOR:
         ws = torch.empty(permute_fp8_workspace_size(T, k, L, H, scale_flags, L * int(cap)),
                          dtype=torch.uint8, device=x.device)
+    _same_device(x.device, topk_ids=lay.topk_ids, out_q=out_q, out_scales=out_scales,
+                 status=status, workspace=ws)
     rc = library().cdl_permute_ll_fp8(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
                                       _ptr(lay.counts), _ptr(lay.seg_indptr), _ptr(lay.src2dst),
                                       _ptr(lay.reorder_buf), lay.reorder_buf.numel(), int(cap),
@@ -647,6 +676,7 @@ def combine(y: torch.Tensor, map_: torch.Tensor, topk_weights: torch.Tensor,
     _need(out, "out", torch.bfloat16, (T, H))
     if status is not None:
         _need(status, "status", torch.int32)
+    _same_device(y.device, map=map_, topk_weights=topk_weights, out=out, status=status)
     rc = library().cdl_combine(_ptr(y), y_rows, H, _ptr(map_), _ptr(topk_weights), T, k,
                                _ptr(out), _ptr(status), _stream(y.device))
     _check(rc, "cdl_combine")

@@ -458,7 +458,28 @@ int cdl_combine_timed(const uint16_t *y, int64_t y_rows, int64_t H, const int32_
  */
 int64_t cdl_ll_expected_m(int64_t T, int32_t num_ranks, int32_t k, int32_t E);
 
-/* cdl_status_string -- static text for a CDL_OK / CDL_ERR_* return code. */
+/*
+ * cdl_status_string -- static text for a CDL_OK / CDL_ERR_* return code.
+ *
+ * The return codes stand in for the exceptions the dispatcher pages raise
+ * before any dispatch work starts: [deepep.py] _DeepEPDispatcherImplBase.__init__
+ * raises ImportError when the communication library is missing (here: the
+ * HIP library is loaded or the binding refuses, and CDL_ERR_HIP reports a
+ * failed launch); _DeepEPDispatcherImplBase._validate_and_adjust_dtype raises
+ * RuntimeError for an output dtype the hardware cannot produce and
+ * _DeepEPDispatcherImplNormal.combine_a raises NotImplementedError for a
+ * runner that is not supported (here: CDL_ERR_UNSUPPORTED for a shape,
+ * alignment or scale format the operation does not support);
+ * DeepEPDispatcher._get_impl raises ValueError for an invalid mode (here:
+ * CDL_ERR_BAD_SIZE / CDL_ERR_TOO_LARGE / CDL_ERR_NULL_POINTER /
+ * CDL_ERR_WORKSPACE for invalid arguments).  Unlike the exceptions, every
+ * code is returned on the host before any work is enqueued (CDL_ERR_HIP
+ * aside), so a failed call leaves every output untouched.
+ *
+ * Returns a pointer to a static NUL-terminated string owned by the library
+ * (never NULL; "unknown cdl status code" for a value that is not a code).
+ * Pure host function, thread-safe.
+ */
 const char *cdl_status_string(int code);
 
 #ifdef __cplusplus

@@ -379,3 +379,55 @@ def test_header_is_plain_c_and_links(tmp_path):
                     "-Wl,-rpath," + lib_dir], check=True, capture_output=True, timeout=120)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+
+
+class _NoLaunch:
+    """The real library for its host-only size queries; any other entry point
+    (one that would enqueue work) fails the test if reached."""
+
+    HOST_ONLY = {"cdl_dispatch_layout_workspace_size", "cdl_permute_fp8_workspace_size",
+                 "cdl_fp8_scale_bytes", "cdl_status_string"}
+
+    def __init__(self, lib):
+        self._lib = lib
+        self.launched = []
+
+    def __getattr__(self, name):
+        if name in self.HOST_ONLY:
+            return getattr(self._lib, name)
+        self.launched.append(name)
+        raise AssertionError("%s reached before the argument checks refused the call" % name)
+
+
+@pytest.fixture
+def no_launch(monkeypatch):
+    """The binding on CPU tensors with the GPU-tensor check lifted, so that
+    the shape checks behind it can be exercised without a GPU."""
+    import combine_dispatch_layout_amd.api as api
+    stub = _NoLaunch(api.library())
+    monkeypatch.setattr(api, "library", lambda: stub)
+    monkeypatch.setattr(api, "_need_gpu", lambda t, name: None)
+    return stub
+
+
+def test_fp8_calls_refuse_a_narrow_out_q_before_any_launch(no_launch):
+    """The fp8 kernels write H bytes per destination row at row * H: an out_q
+    narrower than H is refused by the binding, before any kernel is queued."""
+    import torch
+    T, k, L, H = 8, 2, 4, 256
+    x = torch.zeros(T, H, dtype=torch.bfloat16)
+    ids = torch.zeros(T, k, dtype=torch.int32)
+    narrow = torch.empty(T * k, H - 128, dtype=torch.uint8)
+    flat = torch.empty(T * k * H, dtype=torch.uint8)
+    for bad in (narrow, flat):
+        with pytest.raises(ValueError, match="out_q"):
+            cdl.permute_fp8(x, ids, 0, L, out_q=bad)
+        with pytest.raises(ValueError, match="out_q"):
+            cdl.permute_fp8_tensor(x, ids, 0, L, out_q=bad)
+        lay = cdl.Layout(T, k, 0, L, ids, torch.empty(L, dtype=torch.int32),
+                         torch.empty(L + 1, dtype=torch.int64),
+                         torch.empty(T * k, dtype=torch.int32),
+                         torch.empty(T * k, dtype=torch.int32))
+        with pytest.raises(ValueError, match="out_q"):
+            cdl.dispatch_fp8(x, lay, out_q=bad)
+    assert no_launch.launched == []
