@@ -151,6 +151,9 @@ uint8_t oracle_e4m3fn_rne(float v)
     return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | ((int)q - 8)));
 }
 
+/* The e4m3fn NaN pattern S.1111.111 carrying the sign of the bf16 value x. */
+static uint8_t nan_code_of(uint16_t x) { return (uint8_t)(((x >> 8) & 0x80u) | 0x7Fu); }
+
 /* ------------------------------------------------------------------------ */
 /* Routing layout.                                                           */
 /* ------------------------------------------------------------------------ */
@@ -378,7 +381,11 @@ int32_t oracle_dispatch_ll(const uint16_t *x, int64_t T, int64_t H, int32_t k,
  * per-tensor scale s divides every element (s = 1 when none is given), the
  * quotient is clamped to [-448, 448] (saturation to the largest finite
  * e4m3fn) and rounded to e4m3fn, ties to even:
- *   q = e4m3fn_rne(clamp(fl(x / s), -448, 448)),  s > 0 finite. */
+ *   q = e4m3fn_rne(clamp(fl(x / s), -448, 448)),  s > 0 finite.
+ * Non-finite x (the pages are silent): +-inf saturates to +-448 like any
+ * other quotient beyond the range, and a NaN quotient becomes the e4m3fn NaN
+ * code with the sign of x (stated explicitly: the sign of a NaN produced by
+ * arithmetic is left open by IEEE 754). */
 void oracle_cast_fp8_tensor(const uint16_t *x, int64_t n, float s, uint8_t *q)
 {
     for (int64_t c = 0; c < n; ++c) {
@@ -387,7 +394,7 @@ void oracle_cast_fp8_tensor(const uint16_t *x, int64_t n, float s, uint8_t *q)
             v = 448.0f;
         if (v < -448.0f)
             v = -448.0f;
-        q[c] = oracle_e4m3fn_rne(v);
+        q[c] = isnan(v) ? nan_code_of(x[c]) : oracle_e4m3fn_rne(v);
     }
 }
 
@@ -395,13 +402,17 @@ void oracle_cast_fp8_tensor(const uint16_t *x, int64_t n, float s, uint8_t *q)
  * ([deepep.py], _DeepEPDispatcherImplNormal.dispatch_a: per-token group quant
  * with a hard-coded group of 128 before a normal fp8 dispatch).  Reading of
  * the scale: s = amax / 448 (448 = largest finite e4m3fn), the elements are
- * divided by s, clamped to [-448, 448] and rounded to e4m3fn, ties to even. */
+ * divided by s, clamped to [-448, 448] and rounded to e4m3fn, ties to even.
+ * Non-finite elements (the pages are silent): NaN elements do not enter
+ * amax (an infinity does, and then s = inf, so finite elements quantise to
+ * signed zeros); a NaN quotient (a NaN x, or inf / inf) becomes the e4m3fn
+ * NaN code with the sign of x. */
 void oracle_quant_group_fp8(const uint16_t *x, int64_t n, uint8_t *q, float *s)
 {
     float a = 0.0f;
     for (int64_t c = 0; c < n; ++c) {
         float v = fabsf(oracle_bf16_to_f32(x[c]));
-        if (v > a)
+        if (v > a)                  /* false for NaN: NaN elements are skipped */
             a = v;
     }
     float sc = a / 448.0f;
@@ -414,7 +425,7 @@ void oracle_quant_group_fp8(const uint16_t *x, int64_t n, uint8_t *q, float *s)
             if (v < -448.0f)
                 v = -448.0f;
         }
-        q[c] = oracle_e4m3fn_rne(v);
+        q[c] = isnan(v) ? nan_code_of(x[c]) : oracle_e4m3fn_rne(v);
     }
     *s = sc;
 }
@@ -488,12 +499,17 @@ void oracle_quant_group_fp8_ue8m0(const uint16_t *x, int64_t n, uint8_t *q, floa
         if (v > a)
             a = v;
     }
+    /* the exponent stops at 127, the largest below the E8M0 NaN code: only
+       an infinite amax (no finite bf16 needs more than 2^120) reaches it */
     int e = -127;
-    while (ldexp(448.0, e) < a)
+    while (e < 127 && ldexp(448.0, e) < a)
         ++e;
     float pf = (float)ldexp(1.0, e);
-    for (int64_t c = 0; c < n; ++c)
-        q[c] = oracle_e4m3fn_rne(oracle_bf16_to_f32(x[c]) / pf);
+    for (int64_t c = 0; c < n; ++c) {
+        float v = oracle_bf16_to_f32(x[c]) / pf;
+        /* no clamp (exact scaling): +-inf x gives the NaN code with its sign */
+        q[c] = isnan(v) ? nan_code_of(x[c]) : oracle_e4m3fn_rne(v);
+    }
     *p = pf;
     *p_exp = e;
 }

@@ -159,3 +159,43 @@ def test_tensor_dispatch_rows():
         if d[i] >= 0:
             assert np.array_equal(Q[d[i]], q[i // w.k])
     assert np.all(Q[R:] == 0xEE)
+
+
+def test_nonfinite_golden(golden):
+    """The oracle's reading of NaN and infinity in the three fp8
+    quantisations (amax skips NaN, an infinite amax gives an infinite or
+    capped scale, a NaN quotient is the NaN code with x's sign), against a
+    hand-worked table."""
+    rows = golden("fp8_nonfinite.txt")
+    assert len(rows) == 7
+    for mode, xs, scale, codes in rows:
+        x = np.array([int(v, 16) for v in xs.split(",")], np.uint16)
+        want = np.array([int(v, 16) for v in codes.split(",")], np.uint8)
+        if mode == "group":
+            q, s = oracle.quant_group_fp8(x)
+            assert np.float32(s).view(np.uint32) == int(scale, 16), (xs, np.float32(s).view(np.uint32))
+        elif mode == "ue8m0":
+            q, p, e = oracle.quant_group_fp8_ue8m0(x)
+            assert e == int(scale), (xs, e)
+            assert p == 2.0 ** int(scale)
+        else:
+            q = oracle.cast_fp8_tensor(x, float(mode.split(":")[1]))
+        assert np.array_equal(q, want), (mode, xs, [hex(v) for v in q])
+
+
+def test_nonfinite_elements_leave_finite_groups_alone():
+    """A NaN or infinity changes only its own group: the other groups of the
+    row quantise exactly as they do without it (the definition is per group)."""
+    g = torch.Generator().manual_seed(7)
+    x = W.bf16_bits(torch.randn(4 * 128, generator=g).to(torch.bfloat16))
+    base_q, base_s = [], []
+    for g in range(4):
+        q, s = oracle.quant_group_fp8(x[g * 128:(g + 1) * 128])
+        base_q.append(q)
+        base_s.append(s)
+    for bad in (0x7FC0, 0xFF80, 0x7F80):
+        y = x.copy()
+        y[128 + 5] = bad
+        for g in (0, 2, 3):
+            q, s = oracle.quant_group_fp8(y[g * 128:(g + 1) * 128])
+            assert np.array_equal(q, base_q[g]) and s == base_s[g]
