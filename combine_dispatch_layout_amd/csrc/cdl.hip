@@ -84,10 +84,6 @@ __device__ __forceinline__ void buf_st8_stream(rsrc_t r, u32x2 v, uint32_t voff,
 {
     __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, kPolicyNT);
 }
-__device__ __forceinline__ void buf_st4_stream(rsrc_t r, float v, uint32_t voff, uint32_t soff)
-{
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff, soff, kPolicyNT);
-}
 __device__ __forceinline__ int32_t buf_ld4(rsrc_t r, uint32_t voff, uint32_t soff)
 {
     return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
@@ -126,6 +122,36 @@ __device__ __forceinline__ uint32_t pack2_e4m3(float a, float b)
     return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
+// Four such values to one 32-bit word (bytes a, b, c, d from low to high):
+// each v_cvt_pk_fp8_f32 writes one 16-bit half of its destination and keeps
+// the other, so no masking or shifting is needed.  The first conversion's
+// "kept" half is a don't-care (it is overwritten by the second).
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d)
+{
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __float_as_int(a), false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
+// Non-finite bf16 patterns: exponent field all ones (Inf: mantissa 0, NaN:
+// mantissa != 0), as the magnitude bits of a 16-bit half.
+constexpr uint32_t kBf16ExpMask = 0x7F80u;
+
+// The e4m3fn NaN code (S.1111.111) with the sign of the bf16 element x.
+__device__ __forceinline__ uint32_t e4m3_nan_of(uint32_t x_bf16) { return ((x_bf16 >> 8) & 0x80u) | 0x7Fu; }
+
+// Non-finite values among the 8 bf16 of a chunk: the exponent bits of every
+// half masked and maximised as integers reach kBf16ExpMask iff one is Inf or
+// NaN.
+__device__ __forceinline__ bool chunk_has_nonfinite(u32x4 v)
+{
+    using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+    const uint32_t m = 0x7F807F80u;
+    const u16x2 e = __builtin_elementwise_max(
+        __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.x & m), __builtin_bit_cast(u16x2, v.y & m)),
+        __builtin_elementwise_max(__builtin_bit_cast(u16x2, v.z & m), __builtin_bit_cast(u16x2, v.w & m)));
+    return (e.x > e.y ? e.x : e.y) == kBf16ExpMask;
+}
+
 __device__ __forceinline__ int32_t local_expert(int32_t id, int32_t expert_begin, int32_t L)
 {
     // id - expert_begin in 64 bits: no overflow for any int32 pair
@@ -156,7 +182,19 @@ __device__ __forceinline__ uint32_t dpp_umax_step(uint32_t a)
     const uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, 0xF, 0xF, false);
     return a > b ? a : b;
 }
-__device__ __forceinline__ float group_amax(u32x4 v)
+// The maximum over the 16 lanes of a DPP row of one 32-bit value per lane.
+__device__ __forceinline__ uint32_t row_umax(uint32_t a)
+{
+    a = dpp_umax_step<0xB1>(a);    // quad_perm [1,0,3,2]
+    a = dpp_umax_step<0x4E>(a);    // quad_perm [2,3,0,1]
+    a = dpp_umax_step<0x141>(a);   // row_half_mirror
+    a = dpp_umax_step<0x140>(a);   // row_mirror
+    return a;
+}
+
+// Bit pattern of the group's largest magnitude (a NaN pattern orders above
+// every other): its bf16 magnitude in the upper half of a binary32.
+__device__ __forceinline__ uint32_t group_amax_bits(u32x4 v)
 {
     using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
     const u16x2 m0 = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
@@ -165,23 +203,78 @@ __device__ __forceinline__ float group_amax(u32x4 v)
     const u16x2 m3 = __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu);
     const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
                                               __builtin_elementwise_max(m2, m3));
-    uint32_t a = (uint32_t)(m.x > m.y ? m.x : m.y) << 16;
-    a = dpp_umax_step<0xB1>(a);    // quad_perm [1,0,3,2]
-    a = dpp_umax_step<0x4E>(a);    // quad_perm [2,3,0,1]
-    a = dpp_umax_step<0x141>(a);   // row_half_mirror
-    a = dpp_umax_step<0x140>(a);   // row_mirror
-    return __uint_as_float(a);
+    return row_umax((uint32_t)(m.x > m.y ? m.x : m.y) << 16);
 }
 
 // Groups with amax >= kFastQuotientMinAmax divide by the scale with one
 // correctly rounded reciprocal y = 1/s per group and Markstein's correction
-// step per element: q0 = x*y, r = fma(-q0, s, x) (exact), q = fma(r, y, q0).
-// An exhaustive check over every bf16 amax and every bf16 x with |x| <= amax
-// (about 1.06e9 pairs, tests/fast_quotient_check.c) finds the e4m3fn code of
-// this quotient equal to that of the correctly rounded x / s whenever
-// amax >= 3.3e-32; below 2^-96 the element-wise division is kept.  copysign
-// keeps the sign of x = +-0 (the correction step would return +0).
-constexpr float kFastQuotientMinAmax = 0x1p-96f;
+// step per element: q0 = x*y, the exact residual r = q0*s - x, q = q0 - r*y
+// (the negation is a source modifier of the second fma).  For x = +-0 the
+// residual is +0 and q keeps the sign of x, so the clamp to [-448, 448] is
+// one v_med3_f32.  An exhaustive check over every bf16 amax and every bf16 x
+// with |x| <= amax (about 1.06e9 pairs, tests/fast_quotient_check.c) finds
+// the e4m3fn code of this quotient equal to that of the correctly rounded
+// x / s whenever amax >= 3.3e-32; below 2^-96 the exact path divides.
+constexpr uint32_t kFastQuotientMinBits = 0x0F800000u;   // bits of 2^-96
+static_assert(__builtin_bit_cast(float, kFastQuotientMinBits) == 0x1p-96f, "fast-path threshold");
+
+// Exact path of one chunk, taken by the whole wave when any of its groups is
+// tiny (amax < 2^-96) or holds a non-finite value; it gives the same bytes as
+// the fast paths for every other group.  Non-finite values (the pages say
+// nothing of them; the oracle states the same reading):
+//   * amax is taken over the group's non-NaN elements (an infinity counts);
+//   * fp32 scales: s = fl(amax / 448) (infinite for an infinite amax), the
+//     quotient x / s of a correctly rounded division (x / inf = +-0), clamped
+//     to [-448, 448] with NaN passing through;
+//   * power-of-two scales: the exponent is capped at 127, the largest below
+//     the E8M0 NaN code;
+//   * an element whose quotient is NaN (or infinite, with unclamped
+//     power-of-two scaling) becomes the e4m3fn NaN code with x's sign.
+__device__ __forceinline__ u32x2 quant_chunk_exact(u32x4 v, bool ue8m0, float *scale, int *scale_exp)
+{
+    const uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                           v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t mag = h[e] & 0x7FFFu;
+        if (mag <= kBf16ExpMask && mag > m) m = mag;
+    }
+    const float a = __uint_as_float(row_umax(m << 16));
+    float q[8];
+    if (ue8m0) {
+        int e = -127;
+        if (a > 0.0f) {
+            int ex = 0;
+            const float mt = frexpf(a, &ex);
+            e = a == __builtin_huge_valf() ? 127 : ex - 9 + (mt > 0.875f ? 1 : 0);
+            e = e < -127 ? -127 : e;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[i] = ldexpf(__uint_as_float(h[i] << 16), -e);
+        *scale = ldexpf(1.0f, e);
+        *scale_exp = e;
+    } else {
+        const float s = a / 448.0f;                     // correctly rounded
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x = __uint_as_float(h[i] << 16);
+            const float d = a > 0.0f ? x / s : x;
+            q[i] = d > 448.0f ? 448.0f : (d < -448.0f ? -448.0f : d);
+        }
+        *scale = s;
+        *scale_exp = 0;
+    }
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+        const uint32_t p = pack2_e4m3(__builtin_isfinite(q[i]) ? q[i] : 0.0f,
+                                      __builtin_isfinite(q[i + 1]) ? q[i + 1] : 0.0f);
+        b[i] = __builtin_isfinite(q[i]) ? (p & 0xFFu) : e4m3_nan_of(h[i]);
+        b[i + 1] = __builtin_isfinite(q[i + 1]) ? (p >> 8) : e4m3_nan_of(h[i + 1]);
+    }
+    return u32x2{b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24};
+}
 
 // Returns the 8 e4m3fn bytes of the chunk; *scale receives the group scale
 // and *scale_exp its exponent (power-of-two scales only).
@@ -192,70 +285,78 @@ constexpr float kFastQuotientMinAmax = 0x1p-96f;
 // x / p is then an exact power-of-two scaling and needs no clamp.
 __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, bool ue8m0, float *scale, int *scale_exp)
 {
-    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    const float a = group_amax(v);
+    const uint32_t ab = group_amax_bits(v);
+    // one exact path for the whole wave when any group needs it (a uniform
+    // branch: the fast path below carries no exec-mask bookkeeping)
+    const bool special = ab >= (kBf16ExpMask << 16) || (!ue8m0 && ab < kFastQuotientMinBits);
+    if (__builtin_expect(__ballot(special) != 0, 0)) return quant_chunk_exact(v, ue8m0, scale, scale_exp);
+    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    const float a = __uint_as_float(ab);
+    float q[8];
     if (ue8m0) {
         int ex = 0;
         const float m = frexpf(a, &ex);
         int e = a > 0.0f ? ex - 9 + (m > 0.875f ? 1 : 0) : -127;
         e = e < -127 ? -127 : e;
-        float q[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) q[i] = ldexpf(f[i], -e);
         *scale = ldexpf(1.0f, e);
         *scale_exp = e;
-        const uint32_t lo = pack2_e4m3(q[0], q[1]) | (pack2_e4m3(q[2], q[3]) << 16);
-        const uint32_t hi = pack2_e4m3(q[4], q[5]) | (pack2_e4m3(q[6], q[7]) << 16);
-        return u32x2{lo, hi};
-    }
-    *scale_exp = 0;
-    float s;
-    float q[8];
-    if (a >= kFastQuotientMinAmax) {
+    } else {
         // s = fl(a / 448) = fl((a * 2^-6) / 7) by one correction step with
         // fl(1/7); y = fl(1 / s) by one correction step from v_rcp_f32 (within
         // 1 ulp); both exact for every bf16 a >= 2^-96 (exhaustive CPU check)
         const float c7 = 1.0f / 7.0f;
         const float t = a * 0x1p-6f;
         const float s0 = t * c7;
-        s = fmaf(fmaf(-s0, 7.0f, t), c7, s0);
+        const float s = fmaf(fmaf(-s0, 7.0f, t), c7, s0);
         const float r0 = __builtin_amdgcn_rcpf(s);
         const float y = fmaf(fmaf(-s, r0, 1.0f), r0, r0);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float q0 = f[e] * y;
-            // clamp the magnitude, then take the sign of x
-            q[e] = copysignf(fminf(fabsf(fmaf(fmaf(-q0, s, f[e]), y, q0)), 448.0f), f[e]);
+            q[e] = __builtin_amdgcn_fmed3f(fmaf(-fmaf(q0, s, -f[e]), y, q0), -448.0f, 448.0f);
         }
-    } else {
-        s = a / 448.0f;                         // correctly rounded binary32 division
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = fminf(fmaxf(a > 0.0f ? f[e] / s : f[e], -448.0f), 448.0f);
+        *scale = s;
+        *scale_exp = 0;
     }
-    const uint32_t lo = pack2_e4m3(q[0], q[1]) | (pack2_e4m3(q[2], q[3]) << 16);
-    const uint32_t hi = pack2_e4m3(q[4], q[5]) | (pack2_e4m3(q[6], q[7]) << 16);
-    *scale = s;
-    return u32x2{lo, hi};
+    return u32x2{pack4_e4m3(q[0], q[1], q[2], q[3]), pack4_e4m3(q[4], q[5], q[6], q[7])};
 }
 
 // Per-tensor cast of one 16-byte chunk (8 bf16) to 8 e4m3fn bytes:
 // e4m3_rne(clamp(fl(x / s), +-448)).  POW2: s is a power of two whose inverse
 // inv is a normal float, so x * inv is the exact quotient; otherwise the
-// quotient is a correctly rounded division.
+// quotient is a correctly rounded division.  A NaN quotient (x NaN) becomes
+// the e4m3fn NaN code with x's sign, an infinite one saturates; POW2 leaves
+// those to a wave-uniform branch taken only when the chunks of the wave hold
+// a non-finite value.
 template <bool POW2>
 __device__ __forceinline__ u32x2 cast_chunk_fp8(u32x4 v, float s, float inv)
 {
-    float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                  bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+    float q[8];
+    if (!POW2 || __builtin_expect(__ballot(chunk_has_nonfinite(v)) != 0, 0)) {
+        const uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
+                               v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+        uint32_t b[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float q = POW2 ? f[e] * inv : f[e] / s;
-        f[e] = fminf(fmaxf(q, -448.0f), 448.0f);
+        for (int e = 0; e < 8; ++e) {
+            const float d = POW2 ? f[e] * inv : f[e] / s;
+            q[e] = d > 448.0f ? 448.0f : (d < -448.0f ? -448.0f : d);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const uint32_t p = pack2_e4m3(q[e] == q[e] ? q[e] : 0.0f, q[e + 1] == q[e + 1] ? q[e + 1] : 0.0f);
+            b[e] = q[e] == q[e] ? (p & 0xFFu) : e4m3_nan_of(h[e]);
+            b[e + 1] = q[e + 1] == q[e + 1] ? (p >> 8) : e4m3_nan_of(h[e + 1]);
+        }
+        return u32x2{b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24};
     }
-    const uint32_t lo = pack2_e4m3(f[0], f[1]) | (pack2_e4m3(f[2], f[3]) << 16);
-    const uint32_t hi = pack2_e4m3(f[4], f[5]) | (pack2_e4m3(f[6], f[7]) << 16);
-    return u32x2{lo, hi};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[e] = __builtin_amdgcn_fmed3f(f[e] * inv, -448.0f, 448.0f);
+    return u32x2{pack4_e4m3(q[0], q[1], q[2], q[3]), pack4_e4m3(q[4], q[5], q[6], q[7])};
 }
 
 // Where fp8 rows and their scales go.  Scale layouts (CDL_FP8_SCALE_*):
@@ -272,22 +373,49 @@ struct Fp8Out {
     int64_t ld;            // column stride of a column-major matrix
 };
 
-__device__ __forceinline__ void put_scale(const Fp8Out &o, int64_t row, int64_t g, float p, int e)
+// The scales of one row pass reach memory with one store per destination
+// row: lane 16r + i (i < the pass's chunks per lane) collects the scale of
+// its wave's chunk u = i in DPP row r, which is group c0/16 + 4i + r of the
+// pass starting at chunk c0, as the 32-bit word to store (the fp32 scale, or
+// the exponent byte log2(p) + 127 of a packed format).  A destination row's
+// pass scales are then written by one instruction of up to 56 lanes (dword
+// stores, byte stores when packed), instead of one 4-lane store per chunk.
+__device__ __forceinline__ uint32_t scale_word(const Fp8Out &o, float p, int e)
 {
+    return (o.flags & CDL_FP8_SCALE_PACKED) ? (uint32_t)(e + 127) : __float_as_uint(p);
+}
+
+template <int NCH, typename DstFn>
+__device__ __forceinline__ void store_pass_scales(uint32_t sw, int k, int lane, int64_t c0,
+                                                  int64_t chunks, const Fp8Out &o, DstFn dst_of)
+{
+    const int i = lane & 15;
+    const int64_t g = c0 / 16 + 4 * i + (lane >> 4);      // this lane's group
+    const bool active = i < NCH && g < chunks / 16;
     const bool packed = (o.flags & CDL_FP8_SCALE_PACKED) != 0;
+    const bool colmajor = (o.flags & CDL_FP8_SCALE_COLMAJOR) != 0;
     const int64_t words = packed ? (o.groups + 3) / 4 : o.groups;
     const int64_t col = packed ? g / 4 : g;
-    int64_t word;
-    if (o.flags & CDL_FP8_SCALE_COLMAJOR) {
-        const int64_t mat = row / o.rows_per_mat;
-        word = mat * words * o.ld + col * o.ld + (row - mat * o.rows_per_mat);
-    } else {
-        word = row * words + col;
+    // byte offset of this lane's scale inside a destination row's scales
+    const int64_t lane_off = colmajor ? col * o.ld * 4 + (packed ? (g & 3) : 0) : (packed ? g : g * 4);
+    for (int j = 0; j < k; ++j) {
+        const int32_t dst = uniform((int32_t)dst_of(j, false));
+        if (dst < 0) continue;
+        int64_t base;                 // first byte of the destination row's scales
+        if (colmajor) {
+            const int32_t rpm = (int32_t)o.rows_per_mat;
+            const int32_t mat = dst / rpm;
+            base = ((int64_t)mat * words * o.ld + (dst - mat * rpm)) * 4;
+        } else {
+            base = (int64_t)dst * words * 4;
+        }
+        if (!active) continue;
+        uint8_t *p = o.s + base + lane_off;
+        if (packed)
+            __builtin_nontemporal_store((uint8_t)sw, p);
+        else
+            __builtin_nontemporal_store(sw, reinterpret_cast<uint32_t *>(p));
     }
-    if (packed)
-        o.s[word * 4 + (g & 3)] = (uint8_t)(e + 127);
-    else
-        reinterpret_cast<float *>(o.s)[word] = p;
 }
 
 // ---------------------------------------------------------------------------
@@ -403,17 +531,19 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
 template <int U0, int NQ, int NCH, typename DstFn>
 __device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], int k, int lane, int64_t c0,
                                                int64_t chunks, const Fp8Out &o, bool ue8m0,
-                                               DstFn dst_of)
+                                               DstFn dst_of, uint32_t &sw)
 {
     u32x2 q[NQ];
-    float sc[NQ];
-    int ex[NQ];
 #pragma unroll
-    for (int u = 0; u < NQ; ++u) q[u] = quant_chunk(v[U0 + u], ue8m0, &sc[u], &ex[u]);
+    for (int u = 0; u < NQ; ++u) {
+        float sc;
+        int ex;
+        q[u] = quant_chunk(v[U0 + u], ue8m0, &sc, &ex);
+        // lane 16r + i keeps the scale of chunk i (see store_pass_scales)
+        const uint32_t w = scale_word(o, sc, ex);
+        sw = (lane & 15) == U0 + u ? w : sw;
+    }
     const uint32_t q_bytes = (uint32_t)(chunks * 8);
-    const uint32_t s_bytes = (uint32_t)(chunks / 16 * 4);
-    const bool group_head = (lane & 15) == 0;       // one scale per 16-lane group
-    const bool row_major_f32 = (o.flags & (CDL_FP8_SCALE_COLMAJOR | CDL_FP8_SCALE_PACKED)) == 0;
     for (int j = 0; j < k; ++j) {
         // readfirstlane: the row is wave-uniform, but a status report inside
         // dst_of hides that from the compiler (the descriptors must be scalar)
@@ -423,19 +553,6 @@ __device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], int k, int
 #pragma unroll
         for (int u = 0; u < NQ; ++u)
             buf_st8_stream(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + (U0 + u) * kWave * 8);
-        if (row_major_f32) {
-            const rsrc_t os = make_rsrc(reinterpret_cast<float *>(o.s) + dst * (chunks / 16), s_bytes);
-#pragma unroll
-            for (int u = 0; u < NQ; ++u)
-                if (group_head)
-                    buf_st4_stream(os, sc[u], (uint32_t)(lane >> 4) * 4u, (uint32_t)(c0 / 16 * 4) + (U0 + u) * 16);
-        } else if (group_head) {
-#pragma unroll
-            for (int u = 0; u < NQ; ++u) {
-                const int64_t c = c0 + (U0 + u) * kWave + lane;
-                if (c < chunks) put_scale(o, dst, c >> 4, sc[u], ex[u]);
-            }
-        }
     }
 }
 
@@ -465,14 +582,17 @@ __device__ __forceinline__ void load_fp8_first_parts(u32x4 (&v)[NCH], rsrc_t xr,
 template <int U0, int NCH, typename DstFn>
 __device__ __forceinline__ void store_fp8_parts(u32x4 (&v)[NCH], int k, int lane, int64_t c0,
                                                 int64_t chunks, const Fp8Out &o, bool ue8m0,
-                                                DstFn dst_of, rsrc_t xr, uint32_t voff, uint32_t pass)
+                                                DstFn dst_of, rsrc_t xr, uint32_t voff, uint32_t pass,
+                                                uint32_t sw = 0)
 {
     if constexpr (U0 < NCH) {
         constexpr int NQ = NCH - U0 < kFp8Part ? NCH - U0 : kFp8Part;
-        store_fp8_part<U0, NQ>(v, k, lane, c0, chunks, o, ue8m0, dst_of);
+        store_fp8_part<U0, NQ>(v, k, lane, c0, chunks, o, ue8m0, dst_of, sw);
         constexpr int next = U0 / kFp8Part + kFp8Ahead;
         if constexpr (next * kFp8Part < NCH) load_fp8_part(v, next, xr, voff, pass);
-        store_fp8_parts<U0 + NQ>(v, k, lane, c0, chunks, o, ue8m0, dst_of, xr, voff, pass);
+        store_fp8_parts<U0 + NQ>(v, k, lane, c0, chunks, o, ue8m0, dst_of, xr, voff, pass, sw);
+    } else {
+        store_pass_scales<NCH>(sw, k, lane, c0, chunks, o, dst_of);
     }
 }
 
@@ -536,7 +656,7 @@ struct PermuteArgs {
     int32_t L;
     const int32_t *sb_counts;
     int64_t S;
-    int64_t sbb;
+    int32_t sbb_shift;    // log2 of the permute workgroups per superblock
     int64_t sb_slots;
     int32_t alignment;    // expert segments padded to multiples of this
     int32_t *counts;
@@ -559,6 +679,107 @@ struct PermuteArgs {
     int32_t *masked_m;
     int32_t *ll_src2dst;
 };
+
+// Step 4 of the permutes: the wave's token row (its first pass already
+// loaded into v; fp8 modes: the first part) goes to the destinations held
+// in lanes (lane j < k: slot j's row, -1 for none), pass by pass; wave h of a
+// token's WPT waves moves the chunks [h * NC * 64, (h + 1) * NC * 64) of
+// each pass of WPT * NC * 64 chunks, starting at chunk c_first.
+template <int MODE, int NC, int WPT>
+__device__ __forceinline__ void store_token_rows(const PermuteArgs &a, u32x4 (&v)[NC], rsrc_t xr,
+                                                 uint32_t voff, int64_t c_first, int32_t dlane,
+                                                 int lane)
+{
+    constexpr bool kFp8Mode = MODE == kRowsFp8 || MODE == kRowsLLFp8;
+    const int k = a.k;
+    const uint32_t row_bytes = (uint32_t)(a.chunks * 16);
+    // per-tensor cast: a power-of-two scale is applied by its exact inverse
+    // (cast_inv != 0), any other by a correctly rounded division
+    float cast_s = 1.0f, cast_inv = 1.0f;      // kRowsFp8Cast1: s = 1
+    if constexpr (MODE == kRowsFp8Tensor) {
+        cast_s = a.tensor_scale ? *a.tensor_scale : 1.0f;
+        const uint32_t sb = __float_as_uint(cast_s);
+        const uint32_t ef = (sb >> 23) & 0xFFu;
+        cast_inv = ((sb & 0x807FFFFFu) == 0 && ef >= 1 && ef <= 253) ? __uint_as_float((254u - ef) << 23) : 0.0f;
+    }
+    for (int64_t c0 = c_first; c0 < a.chunks; c0 += (int64_t)WPT * NC * kWave) {
+        const uint32_t pass = (uint32_t)(c0 * 16);
+        if (c0 > c_first && kFp8Mode) {
+            load_fp8_first_parts(v, xr, voff, pass);
+        } else if (c0 > c_first) {
+#pragma unroll
+            for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, pass + u * kWave * 16);
+        }
+        if constexpr (MODE == kRowsFp8Tensor || MODE == kRowsFp8Cast1) {
+            const uint32_t q_bytes = (uint32_t)(a.chunks * 8);
+            auto row_dst = [&](int j, int u) -> int32_t {
+                const int32_t dst = __builtin_amdgcn_readlane(dlane, j);
+                if (dst >= 0 && (int64_t)dst >= a.cap_rows) {
+                    if (u == 0 && c0 == 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
+                    return -1;
+                }
+                return dst;
+            };
+            if (MODE == kRowsFp8Cast1 || cast_inv != 0.0f) {
+                // exact scaling: the whole row is cast in place (the bytes
+                // replace the first half of each chunk's registers), then
+                // stored to every destination
+#pragma unroll
+                for (int u = 0; u < NC; ++u) {
+                    const u32x2 c = cast_chunk_fp8<true>(v[u], cast_s, cast_inv);
+                    v[u].x = c.x;
+                    v[u].y = c.y;
+                }
+                for (int j = 0; j < k; ++j) {
+                    const int32_t dst = row_dst(j, 0);
+                    if (dst < 0) continue;
+                    const rsrc_t o = make_rsrc(a.fp8.q + (int64_t)dst * a.chunks, q_bytes);
+#pragma unroll
+                    for (int u = 0; u < NC; ++u)
+                        buf_st8_stream(o, u32x2{v[u].x, v[u].y}, (uint32_t)lane * 8u,
+                                       (uint32_t)(c0 * 8) + u * kWave * 8);
+                }
+            } else {
+                // a division per element: one chunk at a time, so that only
+                // one chunk's division temporaries are live
+#pragma unroll
+                for (int u = 0; u < NC; ++u) {
+                    const u32x2 c = cast_chunk_fp8<false>(v[u], cast_s, cast_inv);
+                    for (int j = 0; j < k; ++j) {
+                        const int32_t dst = row_dst(j, u);
+                        if (dst < 0) continue;
+                        const rsrc_t o = make_rsrc(a.fp8.q + (int64_t)dst * a.chunks, q_bytes);
+                        buf_st8_stream(o, c, (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + u * kWave * 8);
+                    }
+                }
+            }
+        } else if constexpr (!kFp8Mode) {
+            for (int j = 0; j < k; ++j) {
+                const int32_t dst = __builtin_amdgcn_readlane(dlane, j);
+                if (dst < 0) continue;
+                if ((int64_t)dst >= a.cap_rows) {
+                    if (c0 == 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
+                    continue;
+                }
+                const rsrc_t o = make_rsrc(a.out + (int64_t)dst * a.chunks, row_bytes);
+#pragma unroll
+                for (int u = 0; u < NC; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
+            }
+        } else {
+            auto dst_of = [&](int j, bool report) -> int64_t {
+                const int32_t d = __builtin_amdgcn_readlane(dlane, j);
+                if (d < 0) return -1;
+                if ((int64_t)d >= a.cap_rows) {
+                    if (report && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
+                    return -1;
+                }
+                return d;
+            };
+            const bool ue8m0 = (a.fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
+            store_fp8_parts<0>(v, k, lane, c0, a.chunks, a.fp8, ue8m0, dst_of, xr, voff, pass);
+        }
+    }
+}
 
 // One workgroup per TPB tokens, WPT waves per token (wave h of a token moves
 // the chunks [h * NC * 64, (h + 1) * NC * 64) of each pass of its row).
@@ -617,10 +838,34 @@ __global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
     // counts, and nothing is recounted
     const bool self = a.self_count != 0;
     const int64_t n_all = a.T * k;
-    const int64_t s_me = blk / a.sbb;
+    const int64_t s_me = blk >> a.sbb_shift;
     const int64_t nsc = self ? n_all : a.S * L;
     const int64_t rc_begin = s_me * a.sb_slots;
     const int64_t nrc = self ? 0 : slot_begin - rc_begin;
+    // WPT waves per token: wave h of token t moves the row chunks
+    // [h * NC * 64, (h + 1) * NC * 64) of each pass of WPT * NC * 64 chunks
+    const int64_t t = t_begin + wave / WPT;
+    const int h = wave % WPT;
+    const int64_t c_first = (int64_t)h * NC * kWave;
+    const uint32_t hoff = (uint32_t)(c_first * 16);
+    const bool real = t < a.T;
+    // lane j < k holds the local expert of the wave's slot j: one vector load,
+    // issued before the layout operands so that the wait for it (the row
+    // loads below depend on it) waits for no other load.  It replaced k
+    // dependent scalar loads, which took up to 5 us under the row traffic of
+    // the other waves (T = 4096, H = 7168: 38.9 -> 38.2 us per step).  A wave
+    // past the last token reads an empty range, whose zeros are not ids.
+    int32_t e_lane = -1;
+    if (MODE != kLayoutOnly && (kLLMode || !ALL_ROWS)) {
+        const rsrc_t r_tok = make_rsrc(a.ids + (real ? t * k : 0), real ? (uint32_t)k * 4u : 0u);
+        const int32_t id_lane = buf_ld4(r_tok, (uint32_t)lane * 4u, 0);
+        // keep it first: scheduled after the layout loads, the wait for it
+        // waited for them too (38.5 against 38.2 us per step)
+        __builtin_amdgcn_sched_barrier(0);
+        // a select, not a branch: the load must not sink into a branch
+        const int32_t le = local_expert(id_lane, a.expert_begin, L);
+        e_lane = ((lane < k) & real) ? le : -1;
+    }
     const rsrc_t r_sc = self ? make_rsrc(a.ids, (uint32_t)(n_all * 4)) : make_rsrc(a.sb_counts, (uint32_t)(nsc * 4));
     const rsrc_t r_rc = make_rsrc(a.ids + rc_begin, (uint32_t)(nrc * 4));
     const rsrc_t r_my = make_rsrc(a.ids + slot_begin, (uint32_t)(nslots * 4));
@@ -633,36 +878,22 @@ __global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
     const int my_rel = wave * kWave + lane;
     const int32_t my_id = buf_ld4(r_my, (uint32_t)my_rel * 4u, 0);
 
-    // WPT waves per token: wave h of token t moves the row chunks
-    // [h * NC * 64, (h + 1) * NC * 64) of each pass of WPT * NC * 64 chunks
-    const int64_t t = t_begin + wave / WPT;
-    const int h = wave % WPT;
-    const int64_t c_first = (int64_t)h * NC * kWave;
-    const uint32_t hoff = (uint32_t)(c_first * 16);
-    // low latency: lane j < k holds the local expert of this wave's slot j
-    // (loaded ahead of the row, so that reading it does not wait for the row)
-    int32_t ll_e = -1;
-    if (kLLMode) {
-        const bool real = t < a.T;
-        const rsrc_t r_tok = make_rsrc(a.ids + (real ? t * k : 0), real ? (uint32_t)k * 4u : 0u);
-        ll_e = lane < k ? local_expert(buf_ld4(r_tok, (uint32_t)lane * 4u, 0), a.expert_begin, L) : -1;
-    }
+    // low latency: the local experts of the slots, for the padded rows
+    const int32_t ll_e = e_lane;
     // tok_valid: the token's row is loaded and stored to its destinations
     bool tok_valid = false;
-    if (MODE != kLayoutOnly && t < a.T) {
-        if (ALL_ROWS)
-            tok_valid = true;
-        else
-            for (int j = 0; j < k; ++j) tok_valid |= local_expert(a.ids[t * k + j], a.expert_begin, L) >= 0;
-    }
+    if (MODE != kLayoutOnly && real) tok_valid = ALL_ROWS ? true : __ballot(e_lane >= 0) != 0;
     u32x4 v[NC];
     const uint32_t row_bytes = (uint32_t)(a.chunks * 16);
     const uint32_t voff = (uint32_t)lane * 16u;
-    // ALL_ROWS: the loads are issued by every wave (a wave past the last
-    // token gets an empty range: its loads return 0 and touch no memory), so
-    // the compiler's wait counts for the layout operands above are exact
+    // The row loads are issued on every path: a wave whose token has no
+    // local slot (or lies past the last token) gets an empty range, whose
+    // loads return 0 and touch no memory.  The compiler's wait counts for the
+    // layout operands above are then exact; with the loads behind a branch it
+    // had to assume the path without them, and the layout waited for part of
+    // every row (measured at T = 4096, H = 7168: 39.1 -> 38.9 us per step).
     const rsrc_t xr = make_rsrc(a.x + (tok_valid ? t * a.chunks : 0), tok_valid ? row_bytes : 0u);
-    if (MODE != kLayoutOnly && (ALL_ROWS || tok_valid)) {
+    if (MODE != kLayoutOnly) {
         if (kFp8Mode) {
             load_fp8_first_parts(v, xr, voff, hoff);
         } else {
@@ -679,7 +910,16 @@ __global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
         cur[e] = 0;
     }
     __syncthreads();
-    // superblock counts, kBatch per thread per round
+    // superblock counts, kBatch per thread per round.  Entry idx = b0 +
+    // q * NT + tid is superblock idx / L, expert idx % L: one 32-bit division
+    // per thread, then advanced by NT entries at a time with adds (a 64-bit
+    // division per entry cost about a hundred instructions on this path)
+    uint32_t sb_s = 0, sb_e = 0;
+    const uint32_t step_s = (uint32_t)NT / (uint32_t)L, step_e = (uint32_t)NT % (uint32_t)L;
+    if (!self) {
+        sb_s = (uint32_t)tid / (uint32_t)L;
+        sb_e = (uint32_t)tid - sb_s * (uint32_t)L;
+    }
     for (int64_t b0 = 0; b0 < nsc; b0 += (int64_t)NT * kBatch) {
         if (b0 > 0) {
 #pragma unroll
@@ -695,10 +935,17 @@ __global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
                     atomicAdd(&tot[e], 1);
                     if (idx < slot_begin) atomicAdd(&cur[e], 1);
                 }
-            } else if (idx < nsc && c[q]) {
-                const int e = (int)(idx % L);
-                atomicAdd(&tot[e], c[q]);
-                if (idx / L < s_me) atomicAdd(&cur[e], c[q]);
+            } else {
+                if (idx < nsc && c[q]) {
+                    atomicAdd(&tot[sb_e], c[q]);
+                    if ((int64_t)sb_s < s_me) atomicAdd(&cur[sb_e], c[q]);
+                }
+                sb_s += step_s;
+                sb_e += step_e;
+                if (sb_e >= (uint32_t)L) {
+                    sb_e -= (uint32_t)L;
+                    ++sb_s;
+                }
             }
         }
     }
@@ -812,90 +1059,146 @@ __global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
     }
     if (!tok_valid) return;
     if (!kLLMode) dlane = lane < k ? dsts[(wave / WPT) * k + lane] : -1;
-    // per-tensor cast: a power-of-two scale is applied by its exact inverse
-    // (cast_inv != 0), any other by a correctly rounded division
-    float cast_s = 1.0f, cast_inv = 1.0f;      // kRowsFp8Cast1: s = 1
-    if constexpr (MODE == kRowsFp8Tensor) {
-        cast_s = a.tensor_scale ? *a.tensor_scale : 1.0f;
-        const uint32_t sb = __float_as_uint(cast_s);
-        const uint32_t ef = (sb >> 23) & 0xFFu;
-        cast_inv = ((sb & 0x807FFFFFu) == 0 && ef >= 1 && ef <= 253) ? __uint_as_float((254u - ef) << 23) : 0.0f;
-    }
-    for (int64_t c0 = c_first; c0 < a.chunks; c0 += (int64_t)WPT * NC * kWave) {
-        const uint32_t pass = (uint32_t)(c0 * 16);
-        if (c0 > c_first && kFp8Mode) {
-            load_fp8_first_parts(v, xr, voff, pass);
-        } else if (c0 > c_first) {
+    store_token_rows<MODE, NC, WPT>(a, v, xr, voff, c_first, dlane, lane);
+}
+
+// The layout alone (cdl_dispatch_layout) for batches with superblock counts
+// (the count kernel ran first): one wave per workgroup derives the
+// destinations of its TPB tokens with wave-level operations only.  It loads
+// the superblock counts, this superblock's slots before the workgroup
+// (recount) and the workgroup's own slots in one batch, accumulates tot[e] /
+// cur[e] with LDS atomics, scans the experts with DPP adds, and ranks the
+// slots 64 at a time with ballots: no barrier, and every wait is for the
+// layout's own operands.  (The all-waves kernel below spends its barriers
+// waiting for its slowest wave; measured at T = 4096, top-8 over 32 of 256
+// experts, the unfused layout + scatter + combine went 48.9 -> 48.5 us.
+// Giving the row-moving permutes such a layout wave made them slower: their
+// row stores then began while the other waves were still reading, 38.9 ->
+// 40.7 us per prefill step, and the extra wave per workgroup of fp8 rows no
+// longer fit the GPU at once.)
+template <int TPB>
+__global__ __launch_bounds__(kWave) void layout_wave_kernel(PermuteArgs a)
+{
+    constexpr int kLB = 16;              // layout operands per lane per batch
+    extern __shared__ int32_t lds[];
+    const int L = a.L;
+    int32_t *tot = lds;                  // totals
+    int32_t *cur = lds + L;              // next destination row of each expert
+    const int lane = threadIdx.x & (kWave - 1);
+    const int k = a.k;
+    const int64_t blk = blockIdx.x;
+    const int64_t t_begin = blk * TPB;
+    const int64_t t_end = t_begin + TPB < a.T ? t_begin + TPB : a.T;
+    const int64_t slot_begin = t_begin * k;
+    const int nslots = (int)((t_end > t_begin ? t_end - t_begin : 0) * k);
+
+    {
+        const int64_t s_me = blk >> a.sbb_shift;
+        const int64_t nsc = a.S * L;
+        const int64_t rc_begin = s_me * a.sb_slots;
+        const int64_t nrc = slot_begin - rc_begin;
+        const rsrc_t r_sc = make_rsrc(a.sb_counts, (uint32_t)(nsc * 4));
+        const rsrc_t r_rc = make_rsrc(a.ids + rc_begin, (uint32_t)(nrc * 4));
+        const rsrc_t r_my = make_rsrc(a.ids + slot_begin, (uint32_t)(nslots * 4));
+        // every first batch is issued before any is used: one memory latency
+        int32_t c[kLB], id[kLB], my[TPB];
 #pragma unroll
-            for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, pass + u * kWave * 16);
+        for (int q = 0; q < kLB; ++q) c[q] = buf_ld4(r_sc, (uint32_t)(q * kWave + lane) * 4u, 0);
+#pragma unroll
+        for (int q = 0; q < kLB; ++q) id[q] = buf_ld4(r_rc, (uint32_t)(q * kWave + lane) * 4u, 0);
+        // nslots <= TPB * 64 (k <= 64): round r ranks slots [64 r, 64 r + 64)
+#pragma unroll
+        for (int r = 0; r < TPB; ++r) my[r] = buf_ld4(r_my, (uint32_t)(r * kWave + lane) * 4u, 0);
+        for (int e = lane; e < L; e += kWave) {
+            tot[e] = 0;
+            cur[e] = 0;
         }
-        if constexpr (MODE == kRowsFp8Tensor || MODE == kRowsFp8Cast1) {
-            const uint32_t q_bytes = (uint32_t)(a.chunks * 8);
-            auto row_dst = [&](int j, int u) -> int32_t {
-                const int32_t dst = __builtin_amdgcn_readlane(dlane, j);
-                if (dst >= 0 && (int64_t)dst >= a.cap_rows) {
-                    if (u == 0 && c0 == 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
-                    return -1;
-                }
-                return dst;
-            };
-            if (MODE == kRowsFp8Cast1 || cast_inv != 0.0f) {
-                // exact scaling: the whole row is cast in place (the bytes
-                // replace the first half of each chunk's registers), then
-                // stored to every destination
+        // 1. totals and offsets before this workgroup.  Superblock-count entry
+        //    idx = s * L + e is advanced 64 entries at a time with adds.
+        uint32_t sb_s = (uint32_t)lane / (uint32_t)L, sb_e = (uint32_t)lane % (uint32_t)L;
+        const uint32_t step_s = (uint32_t)kWave / (uint32_t)L, step_e = (uint32_t)kWave % (uint32_t)L;
+        for (int64_t b0 = 0; b0 < nsc; b0 += (int64_t)kWave * kLB) {
+            if (b0 > 0) {
 #pragma unroll
-                for (int u = 0; u < NC; ++u) {
-                    const u32x2 c = cast_chunk_fp8<true>(v[u], cast_s, cast_inv);
-                    v[u].x = c.x;
-                    v[u].y = c.y;
-                }
-                for (int j = 0; j < k; ++j) {
-                    const int32_t dst = row_dst(j, 0);
-                    if (dst < 0) continue;
-                    const rsrc_t o = make_rsrc(a.fp8.q + (int64_t)dst * a.chunks, q_bytes);
+                for (int q = 0; q < kLB; ++q)
+                    c[q] = buf_ld4(r_sc, (uint32_t)(q * kWave + lane) * 4u, (uint32_t)(b0 * 4));
+            }
 #pragma unroll
-                    for (int u = 0; u < NC; ++u)
-                        buf_st8_stream(o, u32x2{v[u].x, v[u].y}, (uint32_t)lane * 8u,
-                                       (uint32_t)(c0 * 8) + u * kWave * 8);
+            for (int q = 0; q < kLB; ++q) {
+                if (b0 + q * kWave + lane < nsc && c[q]) {
+                    atomicAdd(&tot[sb_e], c[q]);
+                    if ((int64_t)sb_s < s_me) atomicAdd(&cur[sb_e], c[q]);
                 }
-            } else {
-                // a division per element: one chunk at a time, so that only
-                // one chunk's division temporaries are live
-#pragma unroll
-                for (int u = 0; u < NC; ++u) {
-                    const u32x2 c = cast_chunk_fp8<false>(v[u], cast_s, cast_inv);
-                    for (int j = 0; j < k; ++j) {
-                        const int32_t dst = row_dst(j, u);
-                        if (dst < 0) continue;
-                        const rsrc_t o = make_rsrc(a.fp8.q + (int64_t)dst * a.chunks, q_bytes);
-                        buf_st8_stream(o, c, (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + u * kWave * 8);
-                    }
+                sb_s += step_s;
+                sb_e += step_e;
+                if (sb_e >= (uint32_t)L) {
+                    sb_e -= (uint32_t)L;
+                    ++sb_s;
                 }
             }
-        } else if constexpr (!kFp8Mode) {
-            for (int j = 0; j < k; ++j) {
-                const int32_t dst = __builtin_amdgcn_readlane(dlane, j);
-                if (dst < 0) continue;
-                if ((int64_t)dst >= a.cap_rows) {
-                    if (c0 == 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
-                    continue;
-                }
-                const rsrc_t o = make_rsrc(a.out + (int64_t)dst * a.chunks, row_bytes);
+        }
+        for (int64_t b0 = 0; b0 < nrc; b0 += (int64_t)kWave * kLB) {
+            if (b0 > 0) {
 #pragma unroll
-                for (int u = 0; u < NC; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
+                for (int q = 0; q < kLB; ++q)
+                    id[q] = buf_ld4(r_rc, (uint32_t)(q * kWave + lane) * 4u, (uint32_t)(b0 * 4));
             }
-        } else {
-            auto dst_of = [&](int j, bool report) -> int64_t {
-                const int32_t d = __builtin_amdgcn_readlane(dlane, j);
-                if (d < 0) return -1;
-                if ((int64_t)d >= a.cap_rows) {
-                    if (report && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
-                    return -1;
+#pragma unroll
+            for (int q = 0; q < kLB; ++q) {
+                const int32_t e = b0 + q * kWave + lane < nrc ? local_expert(id[q], a.expert_begin, L) : -1;
+                if (e >= 0) atomicAdd(&cur[e], 1);
+            }
+        }
+        // 2. exclusive scan over the experts padded to the alignment, 64 at a
+        //    time (DPP adds); workgroup 0 publishes counts and seg_indptr
+        const int A = a.alignment;
+        int32_t base = 0;
+        for (int e0 = 0; e0 < L; e0 += kWave) {
+            const int e = e0 + lane;
+            const int32_t cnt = e < L ? tot[e] : 0;
+            const int32_t padded = (cnt + A - 1) / A * A;
+            const int32_t incl = wave_inclusive_scan(padded);
+            const int32_t excl = base + incl - padded;
+            if (e < L) {
+                if (blk == 0) {
+                    a.counts[e] = cnt;
+                    a.seg_indptr[e] = excl;
                 }
-                return d;
-            };
-            const bool ue8m0 = (a.fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            store_fp8_parts<0>(v, k, lane, c0, a.chunks, a.fp8, ue8m0, dst_of, xr, voff, pass);
+                cur[e] += excl;
+                if (padded > cnt && (int64_t)(e % gridDim.x) == blk) {
+                    for (int64_t r = excl + cnt; r < excl + padded && r < a.reorder_cap; ++r) a.reorder[r] = -1;
+                }
+            }
+            base += __builtin_amdgcn_readlane(incl, kWave - 1);
+        }
+        if (blk == 0 && lane == 0) {
+            a.seg_indptr[L] = base;
+            if ((int64_t)base > a.reorder_cap) set_status(a.status, CDL_STATUS_REORDER_OVERFLOW);
+        }
+        // 3. stable ranks, 64 slots per round in slot order; the leader of
+        //    each expert match advances cur[e]
+        const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+#pragma unroll
+        for (int r = 0; r < TPB; ++r) {
+            const int rel = r * kWave + lane;
+            if (r * kWave >= nslots) break;
+            const int32_t e = rel < nslots ? local_expert(my[r], a.expert_begin, L) : -1;
+            uint64_t pending = __ballot(e >= 0);
+            int32_t dst = -1;
+            while (pending) {
+                const int leader = __builtin_ctzll(pending);
+                const int32_t el = __builtin_amdgcn_readlane(e, leader);
+                const uint64_t m = __ballot(e == el);
+                const int32_t before = cur[el];
+                if (e == el) dst = before + __popcll(m & lt_mask);
+                if (lane == leader) cur[el] = before + __popcll(m);
+                pending &= ~m;
+            }
+            if (rel < nslots) {
+                const int64_t i = slot_begin + rel;
+                a.src2dst[i] = dst;
+                if (dst >= 0 && (int64_t)dst < a.reorder_cap) a.reorder[dst] = e;
+            }
         }
     }
 }
@@ -1589,15 +1892,33 @@ void launch_permute_tpb(const PermuteArgs &a, const Plan &p, hipStream_t s)
 // 256-512).
 constexpr int64_t kAllRowsMaxTokens = 512;
 
+// The layout alone for batches with superblock counts: one wave per
+// workgroup of p.tpb tokens.
+inline void launch_layout_wave(const PermuteArgs &a, const Plan &p, hipStream_t s)
+{
+    const size_t lds = (size_t)(2 * a.L) * sizeof(int32_t);
+    const dim3 grid((unsigned)(p.nblocks > 0 ? p.nblocks : 1));
+    switch (p.tpb) {
+    case 1: layout_wave_kernel<1><<<grid, dim3(kWave), lds, s>>>(a); break;
+    case 2: layout_wave_kernel<2><<<grid, dim3(kWave), lds, s>>>(a); break;
+    case 4: layout_wave_kernel<4><<<grid, dim3(kWave), lds, s>>>(a); break;
+    default: layout_wave_kernel<8><<<grid, dim3(kWave), lds, s>>>(a); break;
+    }
+}
+
 template <int MODE>
 int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
 {
-    if constexpr (MODE == kLayoutOnly)
-        launch_permute_tpb<MODE, false>(a, p, s);
-    else if (a.self_count && a.T > 0 && a.T <= kAllRowsMaxTokens)
+    if constexpr (MODE == kLayoutOnly) {
+        if (a.self_count)
+            launch_permute_tpb<MODE, false>(a, p, s);
+        else
+            launch_layout_wave(a, p, s);
+    } else if (a.self_count && a.T > 0 && a.T <= kAllRowsMaxTokens) {
         launch_permute_tpb<MODE, true>(a, p, s);
-    else
+    } else {
         launch_permute_tpb<MODE, false>(a, p, s);
+    }
     return launch_status();
 }
 
@@ -1609,8 +1930,11 @@ int run_layout(PermuteArgs a, void *ws, hipStream_t s)
     const Plan p = make_plan(a.T, a.k, a.L, kFp8Rows ? kMaxTpbFp8 : kMaxTpbBf16);
     a.sb_counts = (const int32_t *)ws;
     a.S = p.S;
-    a.sbb = p.sbb;
+    a.sbb_shift = 0;
+    while ((int64_t)1 << a.sbb_shift < p.sbb) ++a.sbb_shift;     // sbb is a power of two
     a.sb_slots = p.sb_slots;
+    // the superblock-count entries are indexed in 32 bits
+    if (p.S * (int64_t)a.L > (int64_t)INT32_MAX) return CDL_ERR_TOO_LARGE;
     // a batch of at most kSelfCountIds ids per thread of a permute workgroup
     // is counted by every workgroup itself, without the count kernel
     a.self_count = p.n <= (int64_t)kSelfCountIds * kWave * p.tpb ? 1 : 0;

@@ -10,9 +10,12 @@
  *   reciprocal y = fl(1 / s): from v_rcp_f32's result r0 (within 1 ulp of
  *              1/s, so one of the two binary32 neighbours of 1/s),
  *              e = fma(-s, r0, 1), y = fma(e, r0, r0);
- *   quotient   q = copysign(fma(fma(-q0, s, x), y, q0), x) with q0 = fl(x * y)
- *              (Markstein's correction step; copysign keeps the sign of
- *              x = +-0, for which the correction would return +0).
+ *   quotient   q = fma(-fma(q0, s, -x), y, q0) with q0 = fl(x * y)
+ *              (Markstein's correction step with the residual negated: the
+ *              exact residual q0*s - x is computed, and its negation enters
+ *              the second fma as a source modifier; for x = +-0 the
+ *              residual is +0 and the result keeps the sign of x, so the
+ *              clamp to [-448, 448] is a plain median of three).
  * The definitions are s = fl(amax / 448), y = fl(1 / s) and
  * e4m3fn_rne(clamp(fl(x / s), -448, 448)).
  *
@@ -83,7 +86,11 @@ int main(void)
                 const float xx = sg ? -x : x;
                 const float exact = xx / s;
                 const float q0 = xx * y;
-                const float q = copysignf(fmaf(fmaf(-q0, s, xx), y, q0), xx);
+                /* the residual through a volatile: the compiler must not
+                   fold the negation back into the first fma (which would
+                   change the sign of a zero residual) */
+                volatile float r = fmaf(q0, s, -xx);
+                const float q = fmaf(-r, y, q0);
                 ++pairs;
                 if (oracle_e4m3fn_rne(clampq(exact)) != oracle_e4m3fn_rne(clampq(q))) {
                     if (a >= threshold)
