@@ -23,7 +23,9 @@ Reported (one JSON line on stdout):
                from rocprofv3 FETCH_SIZE + WRITE_SIZE when a summary taken on
                the current kernel source is committed, else null
   cpu_baseline the CPU oracle (single-threaded C) on host copies of the same
-               input, over a bounded number of full steps
+               input, over a bounded number of full steps; all_cores: the
+               oracle's loops on every host core this job may use (OpenMP
+               timing build)
 Input/output sets rotate between steps (default 6 sets, > 1 GB in total) so
 that no step finds its input in the 256 MB Infinity Cache; the warm
 (single-set) rate is reported beside it for context.
@@ -234,13 +236,23 @@ def time_steps(torch, sets, fn, steps, warmup):
     return start.elapsed_time(end) / steps, wall / steps
 
 
-def time_kernels(torch, sets, steps, warmup):
-    """The combine kernel's average duration inside the timed step loop: its
-    launch carries two HIP events that receive the kernel's own begin and end
+def time_kernels(torch, sets, steps, warmup, lag=0):
+    """The combine kernel's average duration inside a step loop: its launch
+    carries two HIP events that receive the kernel's own begin and end
     (cdl_combine_timed), so nothing is added to the stream between the
     kernels.  Also returns the mean step time of that same loop, to show the
-    events do not perturb it."""
+    events do not perturb it.
+
+    lag = 0: each step combines the rows its own permute just wrote, as the
+    timed step does; about 59 MB of the combine's reads then come from the
+    256 MB Infinity Cache.  lag = len(sets) - 1 (cold source): step i
+    permutes set i and combines the set permuted len(sets) - 1 steps earlier,
+    whose rows the later permutes' (4 x 59 MB at 6 sets) and the other
+    traffic have evicted, so the combine reads them from HBM (an explicit
+    eviction write would leave dirty lines whose write-back competes with
+    the combine)."""
     n = len(sets)
+    assert 0 <= lag < n
     for i in range(warmup):
         sets[i % n].step()
     torch.cuda.synchronize()
@@ -254,9 +266,8 @@ def time_kernels(torch, sets, steps, warmup):
     end = torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        s = sets[i % n]
-        s.permute()
-        s.combine_timed(*ev[i])
+        sets[i % n].permute()
+        sets[(i - lag) % n].combine_timed(*ev[i])
     end.record()
     torch.cuda.synchronize()
     com = [a.elapsed_time(b) * 1e3 for a, b in ev]
@@ -458,7 +469,6 @@ def measure_ll(torch, cdl, W, dev, steps):
     ms_d8, _ = time_steps(torch, runs, dispatch_fp8, steps, 5)
     ms, _ = time_steps(torch, runs, fn, steps, 5)
     ms_sep, _ = time_steps(torch, runs, fn_separate, steps, 5)
-    ms_graph = ll_graph_step(torch, lib, runs, steps)
     b = runs[0][0]
     byts = (b.bytes_layout() + 4 * w.L + 4 * w.T * w.k + 2 * b.U * w.H + 2 * b.R * w.H
             + b.bytes_combine())
@@ -466,36 +476,10 @@ def measure_ll(torch, cdl, W, dev, steps):
                         "layout + padded dispatch (one call) + combine)",
             "us_per_step": ms * 1e3, "gbps": byts / (ms * 1e-3) / 1e9,
             "us_per_step_separate_calls": ms_sep * 1e3,
-            "us_per_step_hip_graph": ms_graph * 1e3,
             "us_dispatch_one_call": ms_d16 * 1e3,
             "us_dispatch_fp8_one_call": ms_d8 * 1e3,
             "fp8_format": "UE8M0 exponents packed 4 per int32, column-major per expert",
             "expected_m": cdl.ll_expected_m(w.T, w.num_ranks, w.k, w.E)}
-
-
-def ll_graph_step(torch, lib, runs, steps):
-    """The one-call low-latency step of each run captured once in a HIP graph
-    (on the capture stream), then the graphs replayed alternately: the step
-    without host launch overhead, as a decode loop would run it."""
-    P = ctypes.c_void_p
-    side = torch.cuda.Stream()
-    graphs = []
-    for r in runs:
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            s = P(torch.cuda.current_stream().cuda_stream)
-            lib.cdl_permute_ll(*r[6][:-1], s)
-            lib.cdl_combine(*r[2][:-1], s)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            s = P(torch.cuda.current_stream().cuda_stream)
-            if lib.cdl_permute_ll(*r[6][:-1], s) or lib.cdl_combine(*r[2][:-1], s):
-                raise RuntimeError("low-latency step failed during capture")
-        graphs.append(g)
-    ms, _ = time_steps(torch, graphs, lambda g: g.replay(), steps, 5)
-    return ms
 
 
 def measure_zipf(torch, cdl, W, dev, steps):
@@ -525,6 +509,50 @@ def cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+def host_threads() -> int:
+    """Host cores this process may use: its CPU affinity, capped by
+    OMP_NUM_THREADS when that is set (the GPU machines give one GPU's job a
+    share of the host's cores)."""
+    n = len(os.sched_getaffinity(0))
+    try:
+        cap = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        cap = 0
+    return min(n, cap) if cap > 0 else n
+
+
+def cpu_baseline_all_cores(W, s, threads, budget_s=6.0, max_reps=64):
+    """The oracle's dispatch and combine loops on `threads` host threads
+    (the OpenMP timing build, bit-identical to the oracle; the layout, under
+    0.1% of a step, stays the single-threaded oracle's) on full steps of the
+    timed workload until about budget_s seconds have passed."""
+    import oracle
+
+    xb = W.bf16_bits(s.x_host)
+    ids = s.ids_host.numpy()
+    wts = s.w_host.numpy()
+    times, parts = [], []
+    t_start = time.perf_counter()
+    while len(times) < max_reps and (not times or time.perf_counter() - t_start < budget_s):
+        t0 = time.perf_counter()
+        c, seg, d, r = oracle.layout(ids, 0, s.L)
+        t1 = time.perf_counter()
+        P = oracle.omp_dispatch(xb, d, s.k, int(seg[-1]), threads)
+        t2 = time.perf_counter()
+        oracle.omp_combine(P, d, wts, s.T, s.k, threads)
+        t3 = time.perf_counter()
+        times.append(t3 - t0)
+        parts.append((t1 - t0, t2 - t1, t3 - t2))
+    t = statistics.median(times)
+    return {"value": s.bytes_step() / t / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle loops, OpenMP timing build",
+            "tokens_per_s": s.T / t, "ms_per_step": t * 1e3,
+            "ms_layout_dispatch_combine": [round(statistics.median(p[i] for p in parts) * 1e3, 3)
+                                           for i in range(3)],
+            "sample": "%d full steps of the same T=%d workload on %d threads, %.1f s, median "
+                      "step" % (len(times), s.T, threads, sum(times))}
 
 
 def cpu_baseline(W, s, budget_s=12.0, max_reps=64):
@@ -560,10 +588,13 @@ def cpu_baseline(W, s, budget_s=12.0, max_reps=64):
                           len(times), s.T, sum(times))}
 
 
-def step_spread(torch, sets, fn, steps, warmup, loops=10):
+def step_spread(torch, sets, fn, steps, warmup, loops=10, min_per_loop=20):
     """Median, p10 and p90 (us) of the mean step time of `loops` separate
-    loops of steps // loops steps each (no event inside a loop)."""
-    per = max(steps // loops, 1)
+    loops of max(steps // loops, min_per_loop) steps each (no event inside a
+    loop).  Every loop pays one launch gap at its start, so loops of a few
+    steps would read slower than the steady state; a fixed minimum keeps the
+    spread comparable whatever --steps is."""
+    per = max(steps // loops, min_per_loop)
     vals = sorted(time_steps(torch, sets, fn, per, warmup if i == 0 else 2)[0] * 1e3
                   for i in range(loops))
     q = lambda f: vals[min(int(f * (len(vals) - 1) + 0.5), len(vals) - 1)]
@@ -645,13 +676,17 @@ def main():
             for i in range(args.sets)]
     log("sets ready: R=%s U=%s" % ([s.R for s in sets], [s.U for s in sets]))
 
+    # the spread over separate loops (at least 200 steps of this workload)
+    # runs first: it brings the GPU to its working clocks before the timed
+    # loop, with the timed step's own work
+    spread = step_spread(torch, sets, NormalSet.step, args.steps, args.warmup)
     ms, wall_ms = time_steps(torch, sets, NormalSet.step, args.steps, args.warmup)
     log("cold step: %.2f us (wall %.2f us)" % (ms * 1e3, wall_ms * 1e3))
     warm_ms, _ = time_steps(torch, sets[:1], NormalSet.step, args.steps, args.warmup)
     unfused_ms, _ = time_steps(torch, sets, NormalSet.step_unfused, args.steps, args.warmup)
-    spread = step_spread(torch, sets, NormalSet.step, args.steps, args.warmup)
     kern = time_kernels(torch, sets, args.steps, args.warmup)
-    log("kernels: %s" % kern)
+    cold = time_kernels(torch, sets, args.steps, args.warmup, lag=len(sets) - 1)
+    log("kernels: %s; cold source: %s" % (kern, cold))
     st = int(sum(int(s.status.item()) for s in sets))
     if st:
         raise SystemExit("device status word set: %d" % st)
@@ -660,6 +695,7 @@ def main():
     gbps = step_bytes / (ms * 1e-3) / 1e9
     comb_bytes = statistics.mean(s.bytes_combine() for s in sets)
     comb_gbps = comb_bytes / (kern["combine_us"] * 1e-6) / 1e9
+    cold_gbps = comb_bytes / (cold["combine_us"] * 1e-6) / 1e9
     traffic = committed_traffic()
     ceiling = copy_ceiling(torch, dev, step_bytes)
 
@@ -691,10 +727,19 @@ def main():
                          "gbps": round(step_bytes / (unfused_ms * 1e-3) / 1e9, 2),
                          "calls": "dispatch_layout + dispatch + combine"},
         "kernels_us": {k_: round(v, 3) for k_, v in kern.items()},
+        "kernels_us_cold_source": {k_: round(v, 3) for k_, v in cold.items()},
+        # frac: inside the timed step, where about 59 MB of the combine's reads
+        # (the rows the permute just wrote) come from the Infinity Cache;
+        # frac_cold_source: the same launch over the rows of the set permuted
+        # five steps earlier, evicted by then, so read from HBM
         "roofline": {"kernel": "combine_rows_v16", "bound": "hbm",
                      "achieved": round(comb_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(comb_gbps / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": int(comb_bytes)},
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(comb_bytes),
+                     "source_rows": "in step (Infinity Cache hits)",
+                     "cold_source": "rows permuted %d steps earlier (evicted)" % (len(sets) - 1),
+                     "achieved_cold_source": round(cold_gbps, 2),
+                     "frac_cold_source": round(cold_gbps / PEAK_HBM_GBPS, 4)},
     }
     if not args.no_modes:
         result["modes"] = {
@@ -705,7 +750,11 @@ def main():
         }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(W, sets[0])
+        base = cpu_baseline(W, sets[0])
+        threads = host_threads()
+        log("timing the oracle's loops on %d host threads ..." % threads)
+        base["all_cores"] = cpu_baseline_all_cores(W, sets[0], threads)
+        result["cpu_baseline"] = base
     print(json.dumps(result), flush=True)
 
 

@@ -27,12 +27,22 @@ GCC_FLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-Wall", "-Wextra"]
 
 
+_SRC_OMP = os.path.join(_HERE, "cdl_oracle_omp.c")
+_LIB_OMP = os.path.join(_HERE, "libcdl_oracle_omp.so")
+
+
 def build(force: bool = True) -> str:
-    """Compile the oracle with gcc into ``oracle/libcdl_oracle.so``."""
+    """Compile the oracle with gcc into ``oracle/libcdl_oracle.so``, and its
+    all-core timing build (the same loops over tokens with OpenMP, for the
+    benchmark's CPU baseline only) into ``oracle/libcdl_oracle_omp.so``."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", *GCC_FLAGS, "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
+    if force or not os.path.exists(_LIB_OMP):
+        tmp = _LIB_OMP + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *GCC_FLAGS, "-fopenmp", "-o", tmp, _SRC, _SRC_OMP, "-lm"])
+        os.replace(tmp, _LIB_OMP)
     return _LIB
 
 
@@ -386,3 +396,54 @@ def combine_f64(y_bits: np.ndarray, map_: np.ndarray, weights: np.ndarray,
 
 def expected_m(T: int, num_ranks: int, k: int, E: int) -> int:
     return int(lib().oracle_expected_m(T, num_ranks, k, E))
+
+
+# ---------------------------------------------------------------------------
+# all-core timing build (benchmark CPU baseline only; never used for parity)
+# ---------------------------------------------------------------------------
+
+_lib_omp = None
+
+
+def lib_omp():
+    """The OpenMP timing build of the dispatch and combine loops."""
+    global _lib_omp
+    if _lib_omp is None:
+        if not os.path.exists(_LIB_OMP):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_OMP)
+        L.oracle_omp_dispatch.argtypes = [_u16p, _i64, _i64, _i32, _i32p, _u16p, _i32]
+        L.oracle_omp_dispatch.restype = None
+        L.oracle_omp_combine.argtypes = [_u16p, _i64, _i64, _i32p, _f32p, _i64, _i32, _u16p,
+                                         _i32]
+        L.oracle_omp_combine.restype = _i64
+        _lib_omp = L
+    return _lib_omp
+
+
+def omp_dispatch(x_bits: np.ndarray, src2dst: np.ndarray, k: int, rows: int,
+                 threads: int) -> np.ndarray:
+    """dispatch() on `threads` host threads (timing build; same rows)."""
+    x = _c(x_bits, np.uint16)
+    T, H = x.shape
+    P = np.zeros((rows, H), np.uint16)
+    lib_omp().oracle_omp_dispatch(x.reshape(-1), T, H, k, _c(src2dst, np.int32), P.reshape(-1),
+                                  int(threads))
+    return P
+
+
+def omp_combine(y_bits: np.ndarray, map_: np.ndarray, weights: np.ndarray, T: int, k: int,
+                threads: int) -> np.ndarray:
+    """combine() on `threads` host threads (timing build; same bits)."""
+    y = _c(y_bits, np.uint16)
+    H = y.shape[-1]
+    y2 = y.reshape(-1, H) if y.size else np.zeros((0, H), np.uint16)
+    out = np.zeros((T, H), np.uint16)
+    bad = lib_omp().oracle_omp_combine(y2.reshape(-1), y2.shape[0], H, _c(map_, np.int32),
+                                       _c(weights, np.float32).reshape(-1), T, k,
+                                       out.reshape(-1), int(threads))
+    if bad < 0:
+        raise MemoryError("oracle_omp_combine failed")
+    if bad:
+        raise ValueError("map holds %d entries beyond y_rows" % bad)
+    return out

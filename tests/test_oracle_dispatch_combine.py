@@ -260,3 +260,21 @@ def test_combine_empty():
     out = oracle.combine(np.zeros((0, 16), np.uint16), np.full(6, -1, np.int32),
                          np.ones((3, 2), np.float32), 3, 2)
     assert np.all(out == 0)
+
+
+def test_all_core_timing_build_matches_the_oracle():
+    """The OpenMP build the benchmark times on every host core computes what
+    the single-threaded oracle does, bit for bit (so its timing measures the
+    same work): dispatch rows and combine outputs at several thread counts,
+    with invalid slots, a token without a valid slot and a ragged T."""
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=301, H=640)
+    x, ids, wts = W.make_inputs(w)
+    ids[7, :] = -1                                  # a token with no valid slot
+    xb = W.bf16_bits(x)
+    _, seg, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(seg[-1])
+    P = oracle.dispatch(xb, d, w.k, R)
+    want = oracle.combine(P, d, wts.numpy(), w.T, w.k)
+    for threads in (1, 3, 8):
+        assert np.array_equal(oracle.omp_dispatch(xb, d, w.k, R, threads), P)
+        assert np.array_equal(oracle.omp_combine(P, d, wts.numpy(), w.T, w.k, threads), want)
