@@ -5,6 +5,8 @@ and the top-k-weighted gather-combine, as HIP kernels behind the C ABI in
 seeded synthetic inputs.
 """
 from .api import (  # noqa: F401
+    CDL_ERR_SCRATCH,
+    NOALLOC_SCRATCH_BYTES,
     CDL_STATUS_LL_OVERFLOW,
     CDL_STATUS_MAP_RANGE,
     CDL_STATUS_REORDER_OVERFLOW,

@@ -35,6 +35,8 @@ CDL_STATUS_ROWS_OVERFLOW = 1
 CDL_STATUS_LL_OVERFLOW = 2
 CDL_STATUS_MAP_RANGE = 4
 CDL_STATUS_REORDER_OVERFLOW = 8
+CDL_ERR_SCRATCH = -7
+NOALLOC_SCRATCH_BYTES = 1 << 20
 FP8_GROUP = 128
 FP8_SCALE_UE8M0 = 1
 FP8_SCALE_COLMAJOR = 2
@@ -71,6 +73,9 @@ def library():
         L.cdl_permute.argtypes = [vp, i64, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, i64, vp,
                                   i64, vp, vp, sz, vp]
         L.cdl_permute.restype = ctypes.c_int
+        L.cdl_permute_noalloc.argtypes = [vp, i64, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp,
+                                          i64, vp, i64, vp, vp]
+        L.cdl_permute_noalloc.restype = ctypes.c_int
         L.cdl_permute_fp8.argtypes = [vp, i64, i64, i32, vp, i32, i32, i32, vp, vp, vp, vp, i64,
                                       vp, vp, i32, i64, vp, vp, sz, vp]
         L.cdl_fp8_scale_bytes.argtypes = [i64, i64, i32, i64]

@@ -37,7 +37,15 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "cdl.h"
+
+// Scratch of cdl_permute_noalloc: the layout's superblock counts.  Each GPU
+// holds its own copy of the array at its own address; host code uses that
+// address (looked up with hipGetSymbolAddress), never the array's name.
+static __device__ __align__(256) unsigned char scratch[CDL_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -2040,6 +2048,62 @@ int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_
     return run_layout<kRowsBf16>(a, ws, (hipStream_t)stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void *> g_scratch[kMaxScratchDevices];     // device address per device
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up (with that device
+// current) on the first call there.
+int scratch_address(hipStream_t s, void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CDL_ERR_HIP;
+    if (dev >= kMaxScratchDevices) return CDL_ERR_UNSUPPORTED;
+    if (s) {
+        hipDevice_t sdev = -1;
+        if (hipStreamGetDevice(s, &sdev) != hipSuccess) return CDL_ERR_HIP;
+        if (sdev != dev) return CDL_ERR_UNSUPPORTED;
+    }
+    void *p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CDL_ERR_HIP;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return CDL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int cdl_permute_noalloc(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                        const int32_t *topk_ids, int32_t expert_begin, int32_t L,
+                        int32_t alignment, int32_t *counts, int64_t *seg_indptr, int32_t *src2dst,
+                        int32_t *reorder_topk_ids, int64_t reorder_cap, uint16_t *out,
+                        int64_t cap_rows, int32_t *status, void *stream)
+{
+    int rc = check_tk(T, k);
+    if (rc != CDL_OK) return rc;
+    if (L < 1 || L > CDL_MAX_LOCAL_EXPERTS) return CDL_ERR_BAD_SIZE;
+    const size_t need = layout_ws_bytes(T, k, L);
+    if (need > (size_t)CDL_NOALLOC_SCRATCH_BYTES) return CDL_ERR_SCRATCH;
+    void *ws = nullptr;
+    rc = scratch_address((hipStream_t)stream, &ws);
+    if (rc != CDL_OK) return rc;
+    return cdl_permute(x, T, H, k, topk_ids, expert_begin, L, alignment, counts, seg_indptr,
+                       src2dst, reorder_topk_ids, reorder_cap, out, cap_rows, status, ws,
+                       (size_t)CDL_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 int cdl_permute_fp8_tensor(const uint16_t *x, int64_t T, int64_t H, int32_t k,
                            const int32_t *topk_ids, int32_t expert_begin, int32_t L,
                            int32_t alignment, int32_t *counts, int64_t *seg_indptr,
@@ -2462,6 +2526,7 @@ const char *cdl_status_string(int code)
     case CDL_ERR_WORKSPACE: return "workspace smaller than required";
     case CDL_ERR_TOO_LARGE: return "sizes need 2^31 or more slots or rows";
     case CDL_ERR_HIP: return "HIP kernel launch failed";
+    case CDL_ERR_SCRATCH: return "the call needs more scratch than the static buffer of cdl_permute_noalloc holds";
     default: return "unknown cdl status code";
     }
 }

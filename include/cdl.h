@@ -21,7 +21,9 @@
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on that stream and returns; nothing is
  *     synchronised and no host copy of a device value is made.
- *   - The library never allocates or frees memory and holds no global state;
+ *   - The library never allocates or frees memory and holds no global state
+ *     (one exception: cdl_permute_noalloc keeps its scratch in a static device
+ *     array per GPU and caches that array's address per device);
  *     the caller owns every buffer (including the layout workspace) and the
  *     "handle" that links a dispatch to its combine is the caller-owned set of
  *     arrays (src2dst, seg_indptr, counts, ll_src2dst).  Calls are
@@ -62,6 +64,7 @@ extern "C" {
 #define CDL_ERR_WORKSPACE (-4)      /* workspace smaller than required */
 #define CDL_ERR_TOO_LARGE (-5)      /* T*k (or a row index) needs >= 2^31 */
 #define CDL_ERR_HIP (-6)            /* a kernel launch failed */
+#define CDL_ERR_SCRATCH (-7)        /* cdl_permute_noalloc: more scratch than its static buffer */
 
 /* device status bits */
 #define CDL_STATUS_ROWS_OVERFLOW 1  /* a destination row >= cap_rows */
@@ -174,6 +177,30 @@ int cdl_permute(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_
                 int64_t *seg_indptr, int32_t *src2dst, int32_t *reorder_topk_ids,
                 int64_t reorder_cap, uint16_t *out, int64_t cap_rows, int32_t *status, void *ws,
                 size_t ws_bytes, void *stream);
+
+/*
+ * cdl_permute_noalloc -- cdl_permute for callers that cannot allocate: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, outputs and errors as cdl_permute, without the
+ * workspace: the layout's scratch (the superblock counts) lives in a static
+ * device array of CDL_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends.  Its device address is looked up once per
+ * device (hipGetSymbolAddress, with that device current) on the first call
+ * there; no call allocates or frees memory.  Calls whose
+ * cdl_dispatch_layout_workspace_size(T, k, L) exceeds the buffer return
+ * CDL_ERR_SCRATCH before any work (realistic shapes fit: 4096 tokens of
+ * top-8 over 32 experts need 4.3 KB).  `stream` must belong to the current
+ * device (CDL_ERR_UNSUPPORTED otherwise).  The buffer needs no clearing
+ * between calls; it keeps the last call's contents.  Calls that overlap on
+ * one GPU (other streams, other host threads) share that GPU's buffer and
+ * race: order them (one stream, or events).
+ */
+#define CDL_NOALLOC_SCRATCH_BYTES (1 << 20)
+int cdl_permute_noalloc(const uint16_t *x, int64_t T, int64_t H, int32_t k,
+                        const int32_t *topk_ids, int32_t expert_begin, int32_t L,
+                        int32_t alignment, int32_t *counts, int64_t *seg_indptr, int32_t *src2dst,
+                        int32_t *reorder_topk_ids, int64_t reorder_cap, uint16_t *out,
+                        int64_t cap_rows, int32_t *status, void *stream);
 
 /*
  * cdl_permute_fp8 -- cdl_permute with the per-token, per-128-group fp8

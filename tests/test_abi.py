@@ -431,3 +431,21 @@ def test_fp8_calls_refuse_a_narrow_out_q_before_any_launch(no_launch):
         with pytest.raises(ValueError, match="out_q"):
             cdl.dispatch_fp8(x, lay, out_q=bad)
     assert no_launch.launched == []
+
+
+def test_permute_noalloc_refuses_before_any_hip_call():
+    """cdl_permute_noalloc checks its sizes, and that the layout's scratch
+    fits its static buffer, on the host before any HIP call (so this runs
+    without a GPU)."""
+    lib = cdl.library()
+    f = lib.cdl_permute_noalloc
+    T, k, L = 1 << 22, 64, 2048
+    assert lib.cdl_dispatch_layout_workspace_size(T, k, L) > cdl.NOALLOC_SCRATCH_BYTES
+    assert f(FAKE, T, 128, k, FAKE, 0, L, 1, FAKE, FAKE, FAKE, FAKE, T * k, FAKE, 1, NULL,
+             NULL) == cdl.CDL_ERR_SCRATCH
+    assert f(FAKE, 8, 128, 0, FAKE, 0, 4, 1, FAKE, FAKE, FAKE, FAKE, 8, FAKE, 1, NULL,
+             NULL) == ESIZE
+    assert f(FAKE, 8, 128, 2, FAKE, 0, 0, 1, FAKE, FAKE, FAKE, FAKE, 16, FAKE, 1, NULL,
+             NULL) == ESIZE
+    assert "scratch" in cdl.status_string(cdl.CDL_ERR_SCRATCH)
+    assert lib.cdl_dispatch_layout_workspace_size(4096, 8, 32) <= cdl.NOALLOC_SCRATCH_BYTES
