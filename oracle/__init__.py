@@ -21,7 +21,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "cdl_oracle.c")
-_LIB = os.path.join(_HERE, "libcdl_oracle.so")
+# CDL_ORACLE_LIB names another build of cdl_oracle.c to load instead (the
+# sanitizer test runs the pins against an ASan/UBSan build that way)
+_LIB = os.environ.get("CDL_ORACLE_LIB") or os.path.join(_HERE, "libcdl_oracle.so")
 
 GCC_FLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
              "-fno-fast-math", "-Wall", "-Wextra"]
