@@ -732,7 +732,7 @@ def main():
         # (the rows the permute just wrote) come from the Infinity Cache;
         # frac_cold_source: the same launch over the rows of the set permuted
         # five steps earlier, evicted by then, so read from HBM
-        "roofline": {"kernel": "combine_rows_v16", "bound": "hbm",
+        "roofline": {"kernel": "combine_rows_pipe", "bound": "hbm",
                      "achieved": round(comb_gbps, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(comb_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": int(comb_bytes),

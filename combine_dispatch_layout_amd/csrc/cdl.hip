@@ -1523,46 +1523,67 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
 // combine: gather + weighted fp32 reduce
 // ---------------------------------------------------------------------------
 
-constexpr int kCombThreads = 128;
-constexpr int kCombUnroll = 7;       // chunks per lane per pass: 7 x 128 = 896, one row at H = 7168
+// Chunks per lane and slots in flight of the combine.
+constexpr int kCombChunks = 2;
+constexpr int kCombDepth = 2;
+constexpr int kCombMaxThreads = 1024;
 
-// One workgroup per token.  acc = fma(w_j, y_j, acc) over the valid slots j in
-// ascending order from +0 (v_fma_f32 is correctly rounded), one bf16 rounding.
-__global__ __launch_bounds__(kCombThreads) void combine_rows_v16(
+// Threads of a combine workgroup: enough lanes for a row at kCombChunks
+// chunks each, rounded up to a whole wave (448 at H = 7168; rows longer than
+// kCombMaxThreads * kCombChunks chunks take several passes).
+inline unsigned comb_threads(int64_t chunks)
+{
+    const int64_t lanes = (chunks + kCombChunks - 1) / kCombChunks;
+    const int64_t t = (lanes + kWave - 1) / kWave * kWave;
+    return (unsigned)(t < kCombMaxThreads ? t : kCombMaxThreads);
+}
+
+// One workgroup per token, kCombChunks 16-byte chunks per lane, with the rows
+// of up to kCombDepth valid slots in flight at once: buffer d holds the d-th
+// next valid slot, and each is reloaded with the next valid slot as soon as
+// it has been added.  acc = fma(w_j, y_j, acc) over the valid slots j in
+// ascending order from +0 (v_fma_f32 is correctly rounded), one bf16
+// rounding.  45 VGPRs, so 8 waves per SIMD.  Measured at T = 4096,
+// H = 7168, top-8 over 32 of 256 experts, against one slot at a time with
+// 7 chunks per lane on 128 threads (105 VGPRs): 20.4 -> 19.6 us inside the
+// step, 27.8 -> 25.6 us when the rows come from HBM.  The lanes past the row
+// end read and write nothing (buffer range).
+__global__ __launch_bounds__(kCombMaxThreads) void combine_rows_pipe(
     const u32x4 *__restrict__ y, int64_t y_rows, int64_t chunks, const int32_t *__restrict__ map,
     const float *__restrict__ wts, int32_t k, u32x4 *__restrict__ out,
     int32_t *__restrict__ status)
 {
     const int64_t t = blockIdx.x;
+    const int nthr = blockDim.x;
     // lane j < k of each wave holds slot j's row and weight (readlane below:
-    // no dependent load per slot)
+    // no dependent load per slot); `valid` lists the slots with a row
     const int lane = threadIdx.x & (kWave - 1);
     const int32_t mlane = lane < k ? map[t * k + lane] : -1;
     const float wlane = lane < k ? wts[t * k + lane] : 0.0f;
+    const bool bad = lane < k && mlane >= 0 && (int64_t)mlane >= y_rows;
+    if (__ballot(bad) != 0 && threadIdx.x == 0) set_status(status, CDL_STATUS_MAP_RANGE);
+    const uint64_t valid = __ballot(lane < k && mlane >= 0 && (int64_t)mlane < y_rows);
     const uint32_t row_bytes = (uint32_t)(chunks * 16);
     const uint32_t voff = threadIdx.x * 16u;
     const rsrc_t orow = make_rsrc(out + t * chunks, row_bytes);
-    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)kCombThreads * kCombUnroll) {
+    for (int64_t c0 = 0; c0 < chunks; c0 += (int64_t)nthr * kCombChunks) {
         const uint32_t pass = (uint32_t)(c0 * 16);
-        float acc[kCombUnroll][8];
+        const uint32_t stride = (uint32_t)nthr * 16u;
+        float acc[kCombChunks][8];
 #pragma unroll
-        for (int u = 0; u < kCombUnroll; ++u)
+        for (int u = 0; u < kCombChunks; ++u)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[u][e] = 0.0f;
-        for (int j = 0; j < k; ++j) {
+        auto load = [&](int j, u32x4 (&v)[kCombChunks]) {
             const int32_t r = __builtin_amdgcn_readlane(mlane, j);
-            if (r < 0) continue;
-            if ((int64_t)r >= y_rows) {
-                if (c0 == 0 && threadIdx.x == 0) set_status(status, CDL_STATUS_MAP_RANGE);
-                continue;
-            }
-            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), j));
             const rsrc_t yr = make_rsrc(y + (int64_t)r * chunks, row_bytes);
-            u32x4 v[kCombUnroll];
 #pragma unroll
-            for (int u = 0; u < kCombUnroll; ++u) v[u] = buf_ld16_stream(yr, voff, pass + u * kCombThreads * 16);
+            for (int u = 0; u < kCombChunks; ++u) v[u] = buf_ld16_stream(yr, voff, pass + u * stride);
+        };
+        auto accum = [&](int j, const u32x4 (&v)[kCombChunks]) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wlane), j));
 #pragma unroll
-            for (int u = 0; u < kCombUnroll; ++u) {
+            for (int u = 0; u < kCombChunks; ++u) {
                 acc[u][0] = fmaf(wj, bf16_lo(v[u].x), acc[u][0]);
                 acc[u][1] = fmaf(wj, bf16_hi(v[u].x), acc[u][1]);
                 acc[u][2] = fmaf(wj, bf16_lo(v[u].y), acc[u][2]);
@@ -1572,13 +1593,47 @@ __global__ __launch_bounds__(kCombThreads) void combine_rows_v16(
                 acc[u][6] = fmaf(wj, bf16_lo(v[u].w), acc[u][6]);
                 acc[u][7] = fmaf(wj, bf16_hi(v[u].w), acc[u][7]);
             }
-        }
+        };
+        uint64_t m = valid;
+        u32x4 buf[kCombDepth][kCombChunks];
+        int js[kCombDepth];
 #pragma unroll
-        for (int u = 0; u < kCombUnroll; ++u)
+        for (int d = 0; d < kCombDepth; ++d) {
+            js[d] = -1;
+            if (m) {
+                js[d] = __builtin_ctzll(m);
+                m &= m - 1;
+                load(js[d], buf[d]);
+            }
+        }
+        bool more = js[0] >= 0;
+        while (more) {
+#pragma unroll
+            for (int d = 0; d < kCombDepth; ++d) {
+                if (more && js[d] >= 0) {
+                    accum(js[d], buf[d]);
+                    js[d] = -1;
+                    if (m) {
+                        js[d] = __builtin_ctzll(m);
+                        m &= m - 1;
+                        load(js[d], buf[d]);
+                    }
+                } else {
+                    more = false;
+                }
+            }
+        }
+        // The whole offset goes in the VGPR operand, soffset = 0: the
+        // compiler then keeps the next VALU write of the 16-byte store's data
+        // registers one wait state away (with an SGPR soffset it reused them
+        // at once, and on gfx950 the last four lanes of each 16 then stored
+        // the new values now and then: wrong sums in about one token in ten)
+#pragma unroll
+        for (int u = 0; u < kCombChunks; ++u)
             buf_st16_stream(orow,
-                        u32x4{pack_bf16_rne(acc[u][0], acc[u][1]), pack_bf16_rne(acc[u][2], acc[u][3]),
-                              pack_bf16_rne(acc[u][4], acc[u][5]), pack_bf16_rne(acc[u][6], acc[u][7])},
-                        voff, pass + u * kCombThreads * 16);
+                            u32x4{pack_bf16_rne(acc[u][0], acc[u][1]), pack_bf16_rne(acc[u][2], acc[u][3]),
+                                  pack_bf16_rne(acc[u][4], acc[u][5]), pack_bf16_rne(acc[u][6], acc[u][7])},
+                            voff + pass + u * stride, 0);
     }
 }
 
@@ -1647,10 +1702,13 @@ __global__ __launch_bounds__(kWideMaxThreads) void combine_rows_wide(
             acc[6] = fmaf(wj, bf16_lo(v[j].w), acc[6]);
             acc[7] = fmaf(wj, bf16_hi(v[j].w), acc[7]);
         }
+        // soffset = 0 (the offset in the VGPR operand), as in
+        // combine_rows_pipe: the compiler then spaces the next VALU write of
+        // the store's data registers
         buf_st16_stream(orow,
                         u32x4{pack_bf16_rne(acc[0], acc[1]), pack_bf16_rne(acc[2], acc[3]),
                               pack_bf16_rne(acc[4], acc[5]), pack_bf16_rne(acc[6], acc[7])},
-                        voff, pass);
+                        voff + pass, 0);
     }
 }
 
@@ -2477,12 +2535,13 @@ static int run_combine(const uint16_t *y, int64_t y_rows, int64_t H, const int32
             combine_rows_wide<<<dim3((unsigned)T), dim3(nt), 0, s>>>(
                 (const u32x4 *)y, y_rows, chunks, map, topk_weights, k, (u32x4 *)out, status);
     } else if (H % 8 == 0 && aligned(y, 16) && aligned(out, 16)) {
+        const dim3 block(comb_threads(H / 8));
         if (timed)   // the launch itself carries the events
-            hipExtLaunchKernelGGL(combine_rows_v16, dim3((unsigned)T), dim3(kCombThreads), 0, s, start,
-                                  stop, 0, (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k,
+            hipExtLaunchKernelGGL(combine_rows_pipe, dim3((unsigned)T), block, 0, s, start, stop, 0,
+                                  (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k,
                                   (u32x4 *)out, status);
         else
-            combine_rows_v16<<<dim3((unsigned)T), dim3(kCombThreads), 0, s>>>(
+            combine_rows_pipe<<<dim3((unsigned)T), block, 0, s>>>(
                 (const u32x4 *)y, y_rows, H / 8, map, topk_weights, k, (u32x4 *)out, status);
     } else {
         if (timed)

@@ -959,6 +959,35 @@ def test_combine_small_batch_kernel(T, k, H):
     assert np.all(got[T:] == 0x7F7F)
 
 
+@pytest.mark.parametrize("T,k,H", [(600, 8, 264), (700, 8, 4096), (600, 8, 7168), (520, 64, 512),
+                                   (530, 3, 20480), (600, 1, 8), (515, 8, 7176)])
+def test_combine_pipelined_kernel(T, k, H):
+    """Batches past 512 tokens (or k > 8) take the combine that keeps the
+    rows of two valid slots in flight, two chunks per lane, on a workgroup
+    sized to the row: one ragged wave (H = 264: 33 chunks), rows that need
+    several passes (H = 20480: 2560 chunks over 1024 lanes), tokens with many
+    valid slots (k = 64, about half of them valid) so the two buffers are
+    refilled many times, and a row whose length is not a whole number of
+    waves.  Bits as the oracle's; rows past T untouched."""
+    announce("combine pipelined T=%d k=%d H=%d" % (T, k, H))
+    g = torch.Generator().manual_seed(T * 17 + k * 5 + H)
+    R = max(1, (T * k) // 2)
+    y = torch.randn(R, H, generator=g).to(torch.bfloat16)
+    m = torch.randint(-R // 2, R, (T * k,), generator=g, dtype=torch.int32)
+    m[m < 0] = -1
+    m[:k] = torch.arange(k, dtype=torch.int32) % R          # one token with every slot valid
+    wts = torch.randn(T, k, generator=g).softmax(-1)
+    outbuf = bf16_filled(T + 2, H, 0x7F7F)
+    st = status_word()
+    cdl.combine(y.to(DEV), m.to(DEV), wts.to(DEV), out=outbuf[:T], status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    got = bits16(outbuf)
+    want = oracle.combine(W.bf16_bits(y), m.numpy(), wts.numpy(), T, k)
+    assert np.array_equal(got[:T], want)
+    assert np.all(got[T:] == 0x7F7F)
+
+
 def test_permute_rejects_unsupported_shapes():
     ids = torch.zeros(2, 1, dtype=torch.int32, device=DEV)
     with pytest.raises(cdl.CdlError):
