@@ -604,6 +604,86 @@ __device__ __forceinline__ void store_fp8_parts(u32x4 (&v)[NCH], int k, int lane
     }
 }
 
+// A row pass of fp8 rows, chunk by chunk: chunk u is quantised and stored to
+// every destination before chunk u + 1, and the load of chunk u + kFp8Part is
+// issued as soon as chunk u is quantised (its registers are free then).  The
+// caller loads chunks [0, kFp8Part) of the pass.  The wave thus keeps
+// kFp8Part chunks of loads in flight, and its stores drain while it
+// quantises the next chunks, instead of quantising a part, then storing it,
+// then waiting for the next part.  Destinations: bit j of dmask is set when
+// slot j's row (lane j of dlane) is stored; only those are visited.
+template <int NCH>
+__device__ __forceinline__ void store_scales_masked(uint32_t sw, int lane, int64_t c0, int64_t chunks,
+                                                    const Fp8Out &o, int32_t dlane, uint64_t dmask)
+{
+    const int i = lane & 15;
+    const int64_t g = c0 / 16 + 4 * i + (lane >> 4);      // this lane's group
+    const bool active = i < NCH && g < chunks / 16;
+    const bool packed = (o.flags & CDL_FP8_SCALE_PACKED) != 0;
+    const bool colmajor = (o.flags & CDL_FP8_SCALE_COLMAJOR) != 0;
+    const int64_t words = packed ? (o.groups + 3) / 4 : o.groups;
+    const int64_t col = packed ? g / 4 : g;
+    const int64_t lane_off = colmajor ? col * o.ld * 4 + (packed ? (g & 3) : 0) : (packed ? g : g * 4);
+    for (uint64_t m = dmask; m; m &= m - 1) {
+        const int32_t dst = __builtin_amdgcn_readlane(dlane, (int)__builtin_ctzll(m));
+        int64_t base;
+        if (colmajor) {
+            const int32_t rpm = (int32_t)o.rows_per_mat;
+            const int32_t mat = dst / rpm;
+            base = ((int64_t)mat * words * o.ld + (dst - mat * rpm)) * 4;
+        } else {
+            base = (int64_t)dst * words * 4;
+        }
+        if (!active) continue;
+        uint8_t *p = o.s + base + lane_off;
+        if (packed)
+            __builtin_nontemporal_store((uint8_t)sw, p);
+        else
+            __builtin_nontemporal_store(sw, reinterpret_cast<uint32_t *>(p));
+    }
+}
+
+template <int NCH>
+__device__ __forceinline__ void quant_store_pass(u32x4 (&v)[NCH], int lane, int64_t c0, int64_t chunks,
+                                                 const Fp8Out &o, bool ue8m0, int32_t dlane,
+                                                 uint64_t dmask, rsrc_t xr, uint32_t voff, uint32_t pass)
+{
+    uint32_t sw = 0;
+    const uint32_t q_bytes = (uint32_t)(chunks * 8);
+    // The first two destinations get a fixed number of store instructions
+    // per chunk (a missing one stores through an empty range: no memory
+    // access), so the compiler's wait counts for the chunk loads still in
+    // flight stay exact; with a loop of unknown length before them it must
+    // assume the loop stored nothing, and each wait for a load would also
+    // wait for the stores issued since.  More destinations (a tenth of the
+    // tokens of top-8 over 32 of 256 experts) take a loop after the two.
+    const uint64_t m1 = dmask & (dmask - 1);
+    const int32_t d0 = dmask ? __builtin_amdgcn_readlane(dlane, (int)__builtin_ctzll(dmask)) : -1;
+    const int32_t d1 = m1 ? __builtin_amdgcn_readlane(dlane, (int)__builtin_ctzll(m1)) : -1;
+    const rsrc_t o0 = make_rsrc(o.q + (d0 >= 0 ? (int64_t)d0 * chunks : 0), d0 >= 0 ? q_bytes : 0u);
+    const rsrc_t o1 = make_rsrc(o.q + (d1 >= 0 ? (int64_t)d1 * chunks : 0), d1 >= 0 ? q_bytes : 0u);
+    const uint64_t rest = m1 & (m1 - 1);
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+        float sc;
+        int ex;
+        const u32x2 q = quant_chunk(v[u], ue8m0, &sc, &ex);
+        // lane 16r + i keeps the scale of chunk i (see store_pass_scales)
+        const uint32_t w = scale_word(o, sc, ex);
+        sw = (lane & 15) == u ? w : sw;
+        if (u + kFp8Part < NCH) v[u + kFp8Part] = buf_ld16(xr, voff, pass + (u + kFp8Part) * kWave * 16);
+        const uint32_t qoff = (uint32_t)(c0 * 8) + u * kWave * 8;
+        buf_st8_stream(o0, q, (uint32_t)lane * 8u, qoff);
+        buf_st8_stream(o1, q, (uint32_t)lane * 8u, qoff);
+        for (uint64_t m = rest; m; m &= m - 1) {
+            const int32_t dst = __builtin_amdgcn_readlane(dlane, (int)__builtin_ctzll(m));
+            const rsrc_t oq = make_rsrc(o.q + (int64_t)dst * chunks, q_bytes);
+            buf_st8_stream(oq, q, (uint32_t)lane * 8u, qoff);
+        }
+    }
+    store_scales_masked<NCH>(sw, lane, c0, chunks, o, dlane, dmask);
+}
+
 // ---------------------------------------------------------------------------
 // layout kernel B (+ fused row scatter): the permute
 // ---------------------------------------------------------------------------
@@ -774,17 +854,13 @@ __device__ __forceinline__ void store_token_rows(const PermuteArgs &a, u32x4 (&v
                 for (int u = 0; u < NC; ++u) buf_st16(o, v[u], voff, pass + u * kWave * 16);
             }
         } else {
-            auto dst_of = [&](int j, bool report) -> int64_t {
-                const int32_t d = __builtin_amdgcn_readlane(dlane, j);
-                if (d < 0) return -1;
-                if ((int64_t)d >= a.cap_rows) {
-                    if (report && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
-                    return -1;
-                }
-                return d;
-            };
+            // rows at or beyond the capacity are dropped (reported once)
+            const bool has = lane < k && dlane >= 0;
+            const bool fits = has && (int64_t)dlane < a.cap_rows;
+            if (c0 == 0 && __ballot(has && !fits) != 0 && lane == 0)
+                set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
             const bool ue8m0 = (a.fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            store_fp8_parts<0>(v, k, lane, c0, a.chunks, a.fp8, ue8m0, dst_of, xr, voff, pass);
+            quant_store_pass(v, lane, c0, a.chunks, a.fp8, ue8m0, dlane, __ballot(fits), xr, voff, pass);
         }
     }
 }
@@ -1084,21 +1160,22 @@ __global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
 // row stores then began while the other waves were still reading, 38.9 ->
 // 40.7 us per prefill step, and the extra wave per workgroup of fp8 rows no
 // longer fit the GPU at once.)
+// The layout of workgroup blk (TPB tokens) by one wave: tot and cur are
+// the wave's LDS arrays of L entries; with dsts != nullptr the destination
+// of the workgroup's slot rel is also left in dsts[rel].
 template <int TPB>
-__global__ __launch_bounds__(kWave) void layout_wave_kernel(PermuteArgs a)
+__device__ __forceinline__ void layout_one_wave(const PermuteArgs &a, int64_t blk, int32_t *tot,
+                                                int32_t *cur, int32_t *dsts)
 {
     constexpr int kLB = 16;              // layout operands per lane per batch
-    extern __shared__ int32_t lds[];
     const int L = a.L;
-    int32_t *tot = lds;                  // totals
-    int32_t *cur = lds + L;              // next destination row of each expert
     const int lane = threadIdx.x & (kWave - 1);
     const int k = a.k;
-    const int64_t blk = blockIdx.x;
     const int64_t t_begin = blk * TPB;
     const int64_t t_end = t_begin + TPB < a.T ? t_begin + TPB : a.T;
     const int64_t slot_begin = t_begin * k;
     const int nslots = (int)((t_end > t_begin ? t_end - t_begin : 0) * k);
+    const int64_t nblk = (a.T + TPB - 1) / TPB;
 
     {
         const int64_t s_me = blk >> a.sbb_shift;
@@ -1173,7 +1250,7 @@ __global__ __launch_bounds__(kWave) void layout_wave_kernel(PermuteArgs a)
                     a.seg_indptr[e] = excl;
                 }
                 cur[e] += excl;
-                if (padded > cnt && (int64_t)(e % gridDim.x) == blk) {
+                if (padded > cnt && (int64_t)(e % nblk) == blk) {
                     for (int64_t r = excl + cnt; r < excl + padded && r < a.reorder_cap; ++r) a.reorder[r] = -1;
                 }
             }
@@ -1206,9 +1283,93 @@ __global__ __launch_bounds__(kWave) void layout_wave_kernel(PermuteArgs a)
                 const int64_t i = slot_begin + rel;
                 a.src2dst[i] = dst;
                 if (dst >= 0 && (int64_t)dst < a.reorder_cap) a.reorder[dst] = e;
+                if (dsts) dsts[rel] = dst;
             }
         }
     }
+}
+
+template <int TPB>
+__global__ __launch_bounds__(kWave) void layout_wave_kernel(PermuteArgs a)
+{
+    extern __shared__ int32_t lds[];
+    layout_one_wave<TPB>(a, blockIdx.x, lds, lds + a.L, nullptr);
+}
+
+// The fused fp8 permute for batches with superblock counts (the count kernel
+// ran first) and rows of one pass (H <= 7168): TPB row waves and one layout
+// wave per workgroup.  A row wave loads its token's row as soon as it knows
+// the token has a local slot and quantises it chunk by chunk as the chunks
+// arrive (the loads of the second half issued as the first half's registers
+// free up), keeping the e4m3 bytes (8 per chunk per lane) until the
+// destinations are known.  The layout wave meanwhile derives the workgroup's
+// destinations (layout_one_wave) into LDS.  After the workgroup's one
+// barrier the row waves store their bytes and scales.  The quantisation,
+// about a quarter of each SIMD's time, thus overlaps the layout's latency
+// instead of following it.
+template <int TPB>
+__global__ __launch_bounds__((TPB + 1) * kWave) void permute_fp8_split_kernel(PermuteArgs a)
+{
+    constexpr int NCH = kMaxChunksFp8;
+    extern __shared__ int32_t lds[];
+    const int L = a.L;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = wave_id();
+    const int k = a.k;
+    const int64_t blk = blockIdx.x;
+    const int64_t t = blk * TPB + wave;
+    const bool row_wave = wave < TPB;
+    const bool real = row_wave && t < a.T;
+    const Fp8Out &o = a.fp8;
+    const bool ue8m0 = (o.flags & CDL_FP8_SCALE_UE8M0) != 0;
+    bool tok_valid = false;
+    u32x2 q[NCH];
+    uint32_t sw = 0;
+    if (!row_wave) {
+        layout_one_wave<TPB>(a, blk, lds, lds + L, lds + 2 * L);
+    } else {
+        // lane j < k holds the local expert of slot j; a wave past the last
+        // token reads an empty range
+        const rsrc_t r_tok = make_rsrc(a.ids + (real ? t * k : 0), real ? (uint32_t)k * 4u : 0u);
+        const int32_t le = local_expert(buf_ld4(r_tok, (uint32_t)lane * 4u, 0), a.expert_begin, L);
+        tok_valid = real && __ballot(lane < k && le >= 0) != 0;
+        if (tok_valid) {
+            const uint32_t voff = (uint32_t)lane * 16u;
+            const rsrc_t xr = make_rsrc(a.x + t * a.chunks, (uint32_t)(a.chunks * 16));
+            u32x4 v[NCH];
+            load_fp8_first_parts(v, xr, voff, 0);
+#pragma unroll
+            for (int u = 0; u < NCH; ++u) {
+                // chunks past the row (H < 7168) are neither quantised nor stored
+                if ((int64_t)u * kWave < a.chunks) {
+                    float sc;
+                    int ex;
+                    q[u] = quant_chunk(v[u], ue8m0, &sc, &ex);
+                    const uint32_t w = scale_word(o, sc, ex);
+                    sw = (lane & 15) == u ? w : sw;
+                } else {
+                    q[u] = u32x2{0u, 0u};
+                }
+                if (u + kFp8Part < NCH) v[u + kFp8Part] = buf_ld16(xr, voff, (u + kFp8Part) * kWave * 16);
+            }
+        }
+    }
+    __syncthreads();
+    if (!tok_valid) return;
+    const int32_t dlane = lane < k ? lds[2 * L + wave * k + lane] : -1;
+    const bool has = lane < k && dlane >= 0;
+    const bool fits = has && (int64_t)dlane < a.cap_rows;
+    if (__ballot(has && !fits) != 0 && lane == 0) set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
+    const uint64_t dmask = __ballot(fits);
+    const uint32_t q_bytes = (uint32_t)(a.chunks * 8);
+    for (uint64_t m = dmask; m; m &= m - 1) {
+        const int32_t dst = __builtin_amdgcn_readlane(dlane, (int)__builtin_ctzll(m));
+        const rsrc_t oq = make_rsrc(o.q + (int64_t)dst * a.chunks, q_bytes);
+#pragma unroll
+        for (int u = 0; u < NCH; ++u)
+            if ((int64_t)u * kWave < a.chunks) buf_st8_stream(oq, q[u], (uint32_t)lane * 8u, u * kWave * 8);
+    }
+    store_scales_masked<NCH>(sw, lane, 0, a.chunks, o, dlane, dmask);
 }
 
 // ---------------------------------------------------------------------------
@@ -1247,17 +1408,12 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
             for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         }
         if (FP8) {
-            auto dst_of = [&](int j, bool report) -> int64_t {
-                const int32_t dd = __builtin_amdgcn_readlane(dlane, j);
-                if (dd < 0) return -1;
-                if ((int64_t)dd >= cap_rows) {
-                    if (report && lane == 0) set_status(status, CDL_STATUS_ROWS_OVERFLOW);
-                    return -1;
-                }
-                return dd;
-            };
+            const bool has = lane < k && dlane >= 0;
+            const bool fits = has && (int64_t)dlane < cap_rows;
+            if (c0 == 0 && __ballot(has && !fits) != 0 && lane == 0)
+                set_status(status, CDL_STATUS_ROWS_OVERFLOW);
             const bool ue8m0 = (fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            store_fp8_parts<0>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of, xr, voff, pass);
+            quant_store_pass(v, lane, c0, chunks, fp8, ue8m0, dlane, __ballot(fits), xr, voff, pass);
             continue;
         }
         for (int j = 0; j < k; ++j) {
@@ -1504,9 +1660,9 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
             for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         }
         if (FP8) {
-            auto dst_of = [&](int j, bool) -> int64_t { return __builtin_amdgcn_readlane(rlane, j); };
             const bool ue8m0 = (fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            store_fp8_parts<0>(v, k, lane, c0, chunks, fp8, ue8m0, dst_of, xr, voff, pass);
+            quant_store_pass(v, lane, c0, chunks, fp8, ue8m0, rlane, __ballot(lane < k && rlane >= 0), xr,
+                             voff, pass);
             continue;
         }
         for (int j = 0; j < k; ++j) {
@@ -1972,9 +2128,28 @@ inline void launch_layout_wave(const PermuteArgs &a, const Plan &p, hipStream_t 
     }
 }
 
+// fp8 rows of one pass with superblock counts: a layout wave beside the
+// row waves (permute_fp8_split_kernel)
+inline void launch_fp8_split(const PermuteArgs &a, const Plan &p, hipStream_t s)
+{
+    const size_t lds = (size_t)(2 * a.L + p.tpb * a.k) * sizeof(int32_t);
+    const dim3 grid((unsigned)(p.nblocks > 0 ? p.nblocks : 1));
+    switch (p.tpb) {
+    case 1: permute_fp8_split_kernel<1><<<grid, dim3(2 * kWave), lds, s>>>(a); break;
+    case 2: permute_fp8_split_kernel<2><<<grid, dim3(3 * kWave), lds, s>>>(a); break;
+    default: permute_fp8_split_kernel<4><<<grid, dim3(5 * kWave), lds, s>>>(a); break;
+    }
+}
+
 template <int MODE>
 int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
 {
+    if constexpr (MODE == kRowsFp8) {
+        if (!a.self_count && a.chunks <= (int64_t)kMaxChunksFp8 * kWave) {
+            launch_fp8_split(a, p, s);
+            return launch_status();
+        }
+    }
     if constexpr (MODE == kLayoutOnly) {
         if (a.self_count)
             launch_permute_tpb<MODE, false>(a, p, s);
