@@ -214,15 +214,19 @@ __device__ __forceinline__ uint32_t group_amax_bits(u32x4 v)
     return row_umax((uint32_t)(m.x > m.y ? m.x : m.y) << 16);
 }
 
-// Groups with amax >= kFastQuotientMinAmax divide by the scale with one
+// Groups with amax >= 2^-96 (kFastQuotientMinBits) divide by the scale with one
 // correctly rounded reciprocal y = 1/s per group and Markstein's correction
 // step per element: q0 = x*y, the exact residual r = q0*s - x, q = q0 - r*y
-// (the negation is a source modifier of the second fma).  For x = +-0 the
-// residual is +0 and q keeps the sign of x, so the clamp to [-448, 448] is
-// one v_med3_f32.  An exhaustive check over every bf16 amax and every bf16 x
-// with |x| <= amax (about 1.06e9 pairs, tests/fast_quotient_check.c) finds
-// the e4m3fn code of this quotient equal to that of the correctly rounded
-// x / s whenever amax >= 3.3e-32; below 2^-96 the exact path divides.
+// (the negation is a source modifier of the second fma; for x = +-0 the
+// residual is +0 and q keeps the sign of x).  No clamp to [-448, 448]
+// follows: with |x| <= amax, |q| <= 448 + 2^-15 (the float above 448, when
+// fl(amax / 448) rounded down), and v_cvt_pk_fp8_f32 rounds every magnitude
+// up to 464 to 448 (measured on gfx950; NaN only above 464), so the bytes are
+// those of the clamped quotient.  An exhaustive check over every bf16 amax
+// and every bf16 x with |x| <= amax (about 1.06e9 pairs,
+// tests/fast_quotient_check.c) finds the e4m3fn code of this quotient equal
+// to that of the correctly rounded x / s whenever amax >= 3.3e-32, and |q|
+// never above 448 + 2^-15; below 2^-96 the exact path divides.
 constexpr uint32_t kFastQuotientMinBits = 0x0F800000u;   // bits of 2^-96
 static_assert(__builtin_bit_cast(float, kFastQuotientMinBits) == 0x1p-96f, "fast-path threshold");
 
@@ -296,7 +300,10 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, bool ue8m0, float *scale, 
     const uint32_t ab = group_amax_bits(v);
     // one exact path for the whole wave when any group needs it (a uniform
     // branch: the fast path below carries no exec-mask bookkeeping)
-    const bool special = ab >= (kBf16ExpMask << 16) || (!ue8m0 && ab < kFastQuotientMinBits);
+    // non-finite (ab >= the infinity pattern) or, for fp32 scales, tiny: one
+    // unsigned range check
+    const uint32_t lo = ue8m0 ? 0u : kFastQuotientMinBits;
+    const bool special = ab - lo >= (kBf16ExpMask << 16) - lo;
     if (__builtin_expect(__ballot(special) != 0, 0)) return quant_chunk_exact(v, ue8m0, scale, scale_exp);
     const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
                         bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
@@ -324,7 +331,7 @@ __device__ __forceinline__ u32x2 quant_chunk(u32x4 v, bool ue8m0, float *scale, 
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float q0 = f[e] * y;
-            q[e] = __builtin_amdgcn_fmed3f(fmaf(-fmaf(q0, s, -f[e]), y, q0), -448.0f, 448.0f);
+            q[e] = fmaf(-fmaf(q0, s, -f[e]), y, q0);
         }
         *scale = s;
         *scale_exp = 0;

@@ -14,8 +14,12 @@
  *              (Markstein's correction step with the residual negated: the
  *              exact residual q0*s - x is computed, and its negation enters
  *              the second fma as a source modifier; for x = +-0 the
- *              residual is +0 and the result keeps the sign of x, so the
- *              clamp to [-448, 448] is a plain median of three).
+ *              residual is +0 and the result keeps the sign of x);
+ *   code       the kernels convert q without clamping it: the conversion
+ *              instruction rounds every magnitude up to 464 to 448 (NaN
+ *              only above 464), which equals e4m3fn_rne(clamp(q)) as long
+ *              as |q| <= 464.  This program checks that bound (the largest
+ *              |q| is printed) and compares e4m3fn_rne(clamp(q)).
  * The definitions are s = fl(amax / 448), y = fl(1 / s) and
  * e4m3fn_rne(clamp(fl(x / s), -448, 448)).
  *
@@ -64,6 +68,7 @@ int main(void)
 {
     const float threshold = 0x1p-96f;
     long long pairs = 0, bad_fast = 0, bad_below = 0, bad_scale = 0, bad_rcp = 0, groups = 0;
+    float qmax = 0.0f;                 /* largest |q| with amax >= 2^-96 */
     for (uint32_t ab = 1; ab < 0x7F80; ++ab) {          /* every positive finite bf16 amax */
         const float a = bf((uint16_t)ab);
         volatile float s = a / 448.0f;
@@ -92,6 +97,8 @@ int main(void)
                 volatile float r = fmaf(q0, s, -xx);
                 const float q = fmaf(-r, y, q0);
                 ++pairs;
+                if (a >= threshold && fabsf(q) > qmax)
+                    qmax = fabsf(q);
                 if (oracle_e4m3fn_rne(clampq(exact)) != oracle_e4m3fn_rne(clampq(q))) {
                     if (a >= threshold)
                         ++bad_fast;
@@ -105,5 +112,6 @@ int main(void)
            bad_scale, bad_rcp);
     printf("pairs %lld: e4m3 code differs for %lld with amax >= 2^-96 and %lld below\n", pairs,
            bad_fast, bad_below);
-    return bad_fast == 0 && bad_scale == 0 && bad_rcp == 0 ? 0 : 1;
+    printf("largest |q| with amax >= 2^-96: %.9g (448 + 2^-15 = %.9g)\n", qmax, 448.0 + 0x1p-15);
+    return bad_fast == 0 && bad_scale == 0 && bad_rcp == 0 && qmax <= 464.0f ? 0 : 1;
 }

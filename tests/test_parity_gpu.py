@@ -1379,3 +1379,46 @@ def test_permute_fp8_tensor_aligned(A):
     assert np.array_equal(npy(lay.seg_indptr), s_) and np.array_equal(npy(lay.src2dst), d)
     assert np.array_equal(npy(lay.reorder_topk_ids), r)
     assert np.array_equal(u8(q), want)
+
+
+def test_fp8_quotient_just_above_448():
+    """Groups whose scale fl(amax / 448) rounds down, so that the quotient of
+    x = +-amax is 448 + 2^-15 (2464 of the bf16 amax values do this): the
+    kernels convert the quotient without a clamp, and the conversion must
+    still give the code of 448 (0x7E / 0xFE), as the oracle's clamp does.
+    The split permute (3000 tokens), the one-kernel permute of a small batch
+    (64 tokens) and the scatter from a layout."""
+    ab = np.arange(1, 0x7F80, dtype=np.uint32)
+    a = (ab << 16).view(np.float32)
+    s = (a / np.float32(448)).astype(np.float32)
+    q = (a / s).astype(np.float32)
+    pick = ab[(q > 448) & (a >= np.float32(2.0 ** -96))]
+    assert len(pick) == 2464 and q[(a >= np.float32(2.0 ** -96))].max() == np.float32(448 + 2.0 ** -15)
+    T, H = 3000, 1024
+    G = H // 128
+    rng = np.random.default_rng(11)
+    amax = pick[rng.integers(len(pick), size=(T, G))]
+    # magnitudes below amax (bf16 patterns of positive values are ordered),
+    # random signs, and +-amax at two places of every group
+    mag = (rng.random((T, G, 128)) * amax[..., None]).astype(np.uint32)
+    xb = (mag | (rng.integers(2, size=mag.shape, dtype=np.uint32) << 15)).astype(np.uint16)
+    xb[:, :, 5] = amax
+    xb[:, :, 77] = amax | 0x8000
+    xb = xb.reshape(T, H)
+    ids = torch.zeros(T, 1, dtype=torch.int32)
+    x = W.bits_to_bf16(xb).to(DEV)
+    announce("fp8 quotient 448 + 2^-15")
+    _, _, d, _ = oracle.layout(ids.numpy(), 0, 1)
+    Q, S = oracle.dispatch_fp8(xb, d, 1, T)
+    assert np.all(Q.reshape(T, G, 128)[:, :, 5] == 0x7E) and np.all(Q.reshape(T, G, 128)[:, :, 77] == 0xFE)
+    st = status_word()
+    lay, q1, s1 = cdl.permute_fp8(x, ids.to(DEV), 0, 1, rows=T, status=st)
+    q2, s2 = cdl.dispatch_fp8(x, lay, status=st)
+    lay3, q3, s3 = cdl.permute_fp8(x[:64].contiguous(), ids[:64].to(DEV), 0, 1, rows=64, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for qq, ss in ((q1, s1), (q2, s2)):
+        assert np.array_equal(u8(qq), Q)
+        assert np.array_equal(npy(ss).view(np.uint32), S.view(np.uint32))
+    assert np.array_equal(u8(q3), Q[:64])
+    assert np.array_equal(npy(s3).view(np.uint32), S.view(np.uint32)[:64])
