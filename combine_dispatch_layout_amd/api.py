@@ -329,10 +329,6 @@ def permute_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
         _need(status, "status", torch.int32)
     _same_device(x.device, topk_ids=lay.topk_ids, out_q=out_q, out_scales=out_scales,
                  status=status, workspace=ws)
-    if workspace is None and scale_flags & FP8_SCALE_COLMAJOR:
-        # room for the row-major staging of column-major scales
-        ws = torch.empty(permute_fp8_workspace_size(T, k, L, H, scale_flags, out_q.shape[0]),
-                         dtype=torch.uint8, device=x.device)
     rc = library().cdl_permute_fp8(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,
                                    lay.alignment, _ptr(lay.counts), _ptr(lay.seg_indptr),
                                    _ptr(lay.src2dst), _ptr(lay.reorder_buf),
@@ -420,10 +416,9 @@ def rank_layout(topk_ids: torch.Tensor, num_experts: int, num_ranks: int,
 
 def permute_fp8_workspace_size(T: int, k: int, L: int, H: int, scale_flags: int,
                                rows: int) -> int:
-    """Workspace bytes with which permute_fp8 (rows = output rows) and
-    permute_ll_fp8 (rows = L * cap) stage column-major scales row-major and
-    turn them around in a second kernel; the layout workspace size for
-    row-major formats."""
+    """Workspace bytes for permute_fp8 (rows = output rows) and
+    permute_ll_fp8 (rows = L * cap) in a scale format: the layout workspace
+    size for every valid format."""
     n = library().cdl_permute_fp8_workspace_size(T, k, L, H, scale_flags, rows)
     if n == 0:
         raise CdlError(-3, "cdl_permute_fp8_workspace_size")
@@ -645,9 +640,6 @@ def permute_ll_fp8(x: torch.Tensor, topk_ids: torch.Tensor, expert_begin: int,
     ll_map = torch.empty(T * k, dtype=torch.int32, device=x.device)
     if status is not None:
         _need(status, "status", torch.int32)
-    if workspace is None and scale_flags & FP8_SCALE_COLMAJOR:
-        ws = torch.empty(permute_fp8_workspace_size(T, k, L, H, scale_flags, L * int(cap)),
-                         dtype=torch.uint8, device=x.device)
     _same_device(x.device, topk_ids=lay.topk_ids, out_q=out_q, out_scales=out_scales,
                  status=status, workspace=ws)
     rc = library().cdl_permute_ll_fp8(_ptr(x), T, H, k, _ptr(lay.topk_ids), lay.expert_begin, L,

@@ -388,49 +388,11 @@ struct Fp8Out {
     int64_t ld;            // column stride of a column-major matrix
 };
 
-// The scales of one row pass reach memory with one store per destination
-// row: lane 16r + i (i < the pass's chunks per lane) collects the scale of
-// its wave's chunk u = i in DPP row r, which is group c0/16 + 4i + r of the
-// pass starting at chunk c0, as the 32-bit word to store (the fp32 scale, or
-// the exponent byte log2(p) + 127 of a packed format).  A destination row's
-// pass scales are then written by one instruction of up to 56 lanes (dword
-// stores, byte stores when packed), instead of one 4-lane store per chunk.
+// The 32-bit word a scale is stored as: the fp32 scale, or the exponent byte
+// log2(p) + 127 of a packed format.
 __device__ __forceinline__ uint32_t scale_word(const Fp8Out &o, float p, int e)
 {
     return (o.flags & CDL_FP8_SCALE_PACKED) ? (uint32_t)(e + 127) : __float_as_uint(p);
-}
-
-template <int NCH, typename DstFn>
-__device__ __forceinline__ void store_pass_scales(uint32_t sw, int k, int lane, int64_t c0,
-                                                  int64_t chunks, const Fp8Out &o, DstFn dst_of)
-{
-    const int i = lane & 15;
-    const int64_t g = c0 / 16 + 4 * i + (lane >> 4);      // this lane's group
-    const bool active = i < NCH && g < chunks / 16;
-    const bool packed = (o.flags & CDL_FP8_SCALE_PACKED) != 0;
-    const bool colmajor = (o.flags & CDL_FP8_SCALE_COLMAJOR) != 0;
-    const int64_t words = packed ? (o.groups + 3) / 4 : o.groups;
-    const int64_t col = packed ? g / 4 : g;
-    // byte offset of this lane's scale inside a destination row's scales
-    const int64_t lane_off = colmajor ? col * o.ld * 4 + (packed ? (g & 3) : 0) : (packed ? g : g * 4);
-    for (int j = 0; j < k; ++j) {
-        const int32_t dst = uniform((int32_t)dst_of(j, false));
-        if (dst < 0) continue;
-        int64_t base;                 // first byte of the destination row's scales
-        if (colmajor) {
-            const int32_t rpm = (int32_t)o.rows_per_mat;
-            const int32_t mat = dst / rpm;
-            base = ((int64_t)mat * words * o.ld + (dst - mat * rpm)) * 4;
-        } else {
-            base = (int64_t)dst * words * 4;
-        }
-        if (!active) continue;
-        uint8_t *p = o.s + base + lane_off;
-        if (packed)
-            __builtin_nontemporal_store((uint8_t)sw, p);
-        else
-            __builtin_nontemporal_store(sw, reinterpret_cast<uint32_t *>(p));
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -531,84 +493,22 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
     for (int e = threadIdx.x; e < L; e += kCountThreads) row[e] = hist[e];
 }
 
-// Quantises chunks [U0, U0 + NQ) of a lane's pass (chunk u of the pass is row
-// chunk c0 + u*64 + lane) and stores the e4m3fn bytes and the group scales to
-// every destination row dst_of(j) >= 0, j < k.  A row pass is quantised in
-// parts so that only NQ chunks of quantisation temporaries are live at a
-// time while all of the pass's loads were issued together.  dst_of(j, first)
-// returns -1 to skip a slot; `first` is true for the first part of the first
-// pass, where capacity faults are reported.
 // fp8 rows and scales are stored non-temporally: nothing in this library
 // reads them back (unlike the bf16 permuted rows, which the combine re-reads
 // from the Infinity Cache), and back-to-back fp8 dispatches measured faster
 // without the dirty lines they would leave there (scatter 20.7 -> 18.9 us at
-// T = 4096, H = 7168).
-template <int U0, int NQ, int NCH, typename DstFn>
-__device__ __forceinline__ void store_fp8_part(const u32x4 (&v)[NCH], int k, int lane, int64_t c0,
-                                               int64_t chunks, const Fp8Out &o, bool ue8m0,
-                                               DstFn dst_of, uint32_t &sw)
-{
-    u32x2 q[NQ];
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-        float sc;
-        int ex;
-        q[u] = quant_chunk(v[U0 + u], ue8m0, &sc, &ex);
-        // lane 16r + i keeps the scale of chunk i (see store_pass_scales)
-        const uint32_t w = scale_word(o, sc, ex);
-        sw = (lane & 15) == U0 + u ? w : sw;
-    }
-    const uint32_t q_bytes = (uint32_t)(chunks * 8);
-    for (int j = 0; j < k; ++j) {
-        // readfirstlane: the row is wave-uniform, but a status report inside
-        // dst_of hides that from the compiler (the descriptors must be scalar)
-        const int64_t dst = uniform((int32_t)dst_of(j, c0 == 0 && U0 == 0));
-        if (dst < 0) continue;
-        const rsrc_t oq = make_rsrc(o.q + dst * chunks, q_bytes);
-#pragma unroll
-        for (int u = 0; u < NQ; ++u)
-            buf_st8_stream(oq, q[u], (uint32_t)lane * 8u, (uint32_t)(c0 * 8) + (U0 + u) * kWave * 8);
-    }
-}
-
-// All chunks of a pass, kFp8Part at a time, with at most kFp8Ahead parts of
-// loads in flight: the caller loads the first kFp8Ahead parts, and the loads
-// of part p + kFp8Ahead are issued once part p is stored.  If every wave
-// asked for its whole row at once, the rows would all arrive near the end of
-// the read phase and the waves would then quantise together and store
-// together; with a short window the three phases overlap.
+// T = 4096, H = 7168).  Column-major scales are the exception (see
+// store_scales_masked).
+//
+// The first kFp8Part chunks of a row pass are loaded before the layout or
+// the wait for them; the rest follow as those chunks are quantised.
 constexpr int kFp8Part = 7;
-constexpr int kFp8Ahead = 1;
-template <int NCH>
-__device__ __forceinline__ void load_fp8_part(u32x4 (&v)[NCH], int part, rsrc_t xr, uint32_t voff,
-                                              uint32_t pass)
-{
-#pragma unroll
-    for (int u = 0; u < NCH; ++u)
-        if (u / kFp8Part == part) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
-}
 template <int NCH>
 __device__ __forceinline__ void load_fp8_first_parts(u32x4 (&v)[NCH], rsrc_t xr, uint32_t voff, uint32_t pass)
 {
 #pragma unroll
     for (int u = 0; u < NCH; ++u)
-        if (u < kFp8Ahead * kFp8Part) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
-}
-template <int U0, int NCH, typename DstFn>
-__device__ __forceinline__ void store_fp8_parts(u32x4 (&v)[NCH], int k, int lane, int64_t c0,
-                                                int64_t chunks, const Fp8Out &o, bool ue8m0,
-                                                DstFn dst_of, rsrc_t xr, uint32_t voff, uint32_t pass,
-                                                uint32_t sw = 0)
-{
-    if constexpr (U0 < NCH) {
-        constexpr int NQ = NCH - U0 < kFp8Part ? NCH - U0 : kFp8Part;
-        store_fp8_part<U0, NQ>(v, k, lane, c0, chunks, o, ue8m0, dst_of, sw);
-        constexpr int next = U0 / kFp8Part + kFp8Ahead;
-        if constexpr (next * kFp8Part < NCH) load_fp8_part(v, next, xr, voff, pass);
-        store_fp8_parts<U0 + NQ>(v, k, lane, c0, chunks, o, ue8m0, dst_of, xr, voff, pass, sw);
-    } else {
-        store_pass_scales<NCH>(sw, k, lane, c0, chunks, o, dst_of);
-    }
+        if (u < kFp8Part) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
 }
 
 // A row pass of fp8 rows, chunk by chunk: chunk u is quantised and stored to
@@ -619,6 +519,18 @@ __device__ __forceinline__ void store_fp8_parts(u32x4 (&v)[NCH], int k, int lane
 // quantises the next chunks, instead of quantising a part, then storing it,
 // then waiting for the next part.  Destinations: bit j of dmask is set when
 // slot j's row (lane j of dlane) is stored; only those are visited.
+// The scales of one row pass reach memory with one store per destination
+// row: lane 16r + i (i < the pass's chunks per lane) holds the scale of its
+// wave's chunk u = i in DPP row r, which is group c0/16 + 4i + r of the pass
+// starting at chunk c0, as the 32-bit word to store (the fp32 scale, or the
+// exponent byte log2(p) + 127 of a packed format).  A destination row's pass
+// scales are then written by one instruction of up to 56 lanes (dword
+// stores, byte stores when packed).  Column-major scales are stored with the
+// temporal policy: each lane writes one word of a line that 32 rows share,
+// and the L2 merges those pieces before they reach memory; streamed, every
+// piece went out by itself (T = 4096, H = 7168, top-8 over 32 of 256
+// experts, padded to 128: packed UE8M0 22.6 -> 20.2 us, fp32 29.9 -> 21.5
+// us; row-major 19.2 us).
 template <int NCH>
 __device__ __forceinline__ void store_scales_masked(uint32_t sw, int lane, int64_t c0, int64_t chunks,
                                                     const Fp8Out &o, int32_t dlane, uint64_t dmask)
@@ -643,10 +555,16 @@ __device__ __forceinline__ void store_scales_masked(uint32_t sw, int lane, int64
         }
         if (!active) continue;
         uint8_t *p = o.s + base + lane_off;
-        if (packed)
+        if (colmajor) {
+            if (packed)
+                *p = (uint8_t)sw;
+            else
+                *reinterpret_cast<uint32_t *>(p) = sw;
+        } else if (packed) {
             __builtin_nontemporal_store((uint8_t)sw, p);
-        else
+        } else {
             __builtin_nontemporal_store(sw, reinterpret_cast<uint32_t *>(p));
+        }
     }
 }
 
@@ -675,7 +593,7 @@ __device__ __forceinline__ void quant_store_pass(u32x4 (&v)[NCH], int lane, int6
         float sc;
         int ex;
         const u32x2 q = quant_chunk(v[u], ue8m0, &sc, &ex);
-        // lane 16r + i keeps the scale of chunk i (see store_pass_scales)
+        // lane 16r + i keeps the scale of chunk i (see store_scales_masked)
         const uint32_t w = scale_word(o, sc, ex);
         sw = (lane & 15) == u ? w : sw;
         if (u + kFp8Part < NCH) v[u + kFp8Part] = buf_ld16(xr, voff, pass + (u + kFp8Part) * kWave * 16);
@@ -1900,105 +1818,6 @@ __global__ __launch_bounds__(128) void combine_rows_u16(
 }
 
 // ---------------------------------------------------------------------------
-// column-major scales from a row-major staging copy
-// ---------------------------------------------------------------------------
-
-// Written directly, a column-major scale matrix takes one 4-byte store per
-// row and scale word, each in a different 128-byte line, and a line's 32 rows
-// come from workgroups on every XCD: at the end of the kernel the L2s write
-// back tens of thousands of partial lines (about 9 us at 4096 tokens of
-// H = 7168 top-8).  The fused fp8 permutes therefore stage row-major words
-// (`words` 32-bit words per row: fp32 scales, or four packed exponent bytes)
-// and this kernel turns 64 x 64 tiles of them around through LDS, so that
-// both its reads and its writes are whole lines.  Only rows the dispatch
-// wrote are copied: in normal mode the rows [seg_indptr[e], seg_indptr[e] +
-// counts[e]) of each expert (not the alignment padding), in low-latency mode
-// the slots below masked_m; other
-// entries of the output keep their contents, and so do the unused bytes of a
-// last packed word (tail_bytes = groups % 4 used bytes, 0 when full).
-constexpr int kTileRows = 64, kTileWords = 64;
-
-__global__ __launch_bounds__(256) void scales_colmajor_kernel(
-    const uint32_t *__restrict__ stage, int64_t rows, int64_t words, int64_t rows_per_mat,
-    int64_t ld, uint32_t *__restrict__ out, const int64_t *__restrict__ seg_indptr,
-    const int32_t *__restrict__ counts, int32_t L, int32_t alignment,
-    const int32_t *__restrict__ masked_m, int32_t tail_bytes)
-{
-    __shared__ uint32_t tile[kTileWords][kTileRows + 1];
-    __shared__ int32_t use[kTileRows];
-    extern __shared__ int64_t seg_lds[];          // [L + 1] when padded
-    const int64_t r0 = (int64_t)blockIdx.x * kTileRows;
-    const int64_t w0 = (int64_t)blockIdx.y * kTileWords;
-    const int tid = threadIdx.x;
-    const bool padded = !masked_m && alignment > 1;
-    if (padded) {
-        for (int i = tid; i <= L; i += 256) seg_lds[i] = seg_indptr[i];
-        __syncthreads();
-    }
-    if (tid < kTileRows) {
-        const int64_t r = r0 + tid;
-        bool ok = r < rows;
-        if (ok && masked_m) {
-            const int64_t e = r / rows_per_mat;
-            ok = r - e * rows_per_mat < (int64_t)masked_m[e];
-        } else if (ok && !padded) {
-            ok = r < seg_indptr[L];
-        } else if (ok) {
-            // the expert whose padded segment holds r: the last e with
-            // seg_indptr[e] <= r (nondecreasing from 0), searched in LDS
-            ok = r < seg_lds[L];
-            if (ok) {
-                int lo = 0, hi = L - 1;
-                while (lo < hi) {
-                    const int mid = (lo + hi + 1) / 2;
-                    if (seg_lds[mid] <= r) lo = mid; else hi = mid - 1;
-                }
-                ok = r < seg_lds[lo] + counts[lo];
-            }
-        }
-        use[tid] = ok ? 1 : 0;
-    }
-    const int any = __syncthreads_or(tid < kTileRows ? use[tid] : 0);
-    if (!any) return;
-    // rows in, words along the threads: all 16 loads of a thread issued
-    // before the first is used, through one descriptor for the tile's rows
-    // (an unused entry reads past its range: 0, no memory touched)
-    constexpr int kPer = kTileRows * kTileWords / 256;
-    const int64_t nr = rows - r0 < kTileRows ? rows - r0 : kTileRows;
-    const rsrc_t rs = make_rsrc(stage + r0 * words, (uint32_t)(nr * words * 4));
-    uint32_t vals[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int i = tid + j * 256;
-        const int rr = i / kTileWords, ww = i % kTileWords;
-        const bool ok = use[rr] && w0 + ww < words;
-        vals[j] = (uint32_t)buf_ld4(rs, ok ? (uint32_t)((rr * words + w0 + ww) * 4) : 0xFFFFFFFFu, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-        const int i = tid + j * 256;
-        tile[i % kTileWords][i / kTileWords] = vals[j];
-    }
-    __syncthreads();
-    // words out, rows along the threads (consecutive rows of one matrix are
-    // consecutive in a column)
-    for (int i = tid; i < kTileRows * kTileWords; i += 256) {
-        const int ww = i / kTileRows, rr = i % kTileRows;
-        const int64_t w = w0 + ww;
-        if (!use[rr] || w >= words) continue;
-        const int64_t r = r0 + rr;
-        const int64_t mat = (int32_t)r / (int32_t)rows_per_mat;
-        const int64_t o = (mat * words + w) * ld + (r - mat * rows_per_mat);
-        if (tail_bytes && w == words - 1) {
-            uint8_t *ob = reinterpret_cast<uint8_t *>(out + o);
-            for (int b = 0; b < tail_bytes; ++b) ob[b] = (uint8_t)(tile[ww][rr] >> (8 * b));
-        } else {
-            out[o] = tile[ww][rr];
-        }
-    }
-}
-
-// ---------------------------------------------------------------------------
 // host helpers
 // ---------------------------------------------------------------------------
 
@@ -2195,18 +2014,6 @@ int run_layout(PermuteArgs a, void *ws, hipStream_t s)
     return launch_permute<MODE>(a, p, s);
 }
 
-// Small batches whose fp8 rows are split over kFp8WavesSmall waves (a
-// self-counted batch of at most kAllRowsMaxTokens tokens and 2 tokens per
-// workgroup) write column-major scales in place: their few scale rows cost
-// less than the launch of the transpose (low-latency fp8 dispatch of 128
-// tokens, packed column-major UE8M0 scales: 8.9 us in place, 12.1 us staged).
-inline bool fp8_small_batch(int64_t T, int32_t k, int32_t L)
-{
-    const Plan p = make_plan(T, k, L, kMaxTpbFp8);
-    const bool self = p.n <= (int64_t)kSelfCountIds * kWave * p.tpb;
-    return self && T > 0 && T <= kAllRowsMaxTokens && p.tpb <= 2;
-}
-
 PermuteArgs layout_args(const int32_t *topk_ids, int64_t T, int32_t k, int32_t expert_begin,
                         int32_t L, int32_t alignment, int32_t *counts, int64_t *seg_indptr,
                         int32_t *src2dst, int32_t *reorder, int64_t reorder_cap, int32_t *status)
@@ -2380,41 +2187,13 @@ size_t cdl_fp8_scale_bytes(int64_t rows, int64_t H, int32_t scale_flags, int64_t
     return (size_t)scale_bytes(rows, H, scale_flags, rows_per_mat);
 }
 
-static int64_t scale_words(int64_t H, int32_t flags)
-{
-    const int64_t G = H / CDL_FP8_GROUP;
-    return (flags & CDL_FP8_SCALE_PACKED) ? (G + 3) / 4 : G;
-}
-
 size_t cdl_permute_fp8_workspace_size(int64_t T, int32_t k, int32_t L, int64_t H,
                                       int32_t scale_flags, int64_t rows)
 {
     if (check_tk(T, k) != CDL_OK || L < 1 || L > CDL_MAX_LOCAL_EXPERTS) return 0;
     if (H < CDL_FP8_GROUP || H > CDL_MAX_HIDDEN || H % CDL_FP8_GROUP != 0 || rows < 0) return 0;
     if (!valid_scale_flags(scale_flags)) return 0;
-    const size_t base = layout_ws_bytes(T, k, L);
-    if (!(scale_flags & CDL_FP8_SCALE_COLMAJOR)) return base;
-    const size_t stage = (size_t)rows * (size_t)scale_words(H, scale_flags) * 4;
-    return base + ((stage + 255) & ~(size_t)255);
-}
-
-// The column-major scales of a staged dispatch (scales_colmajor_kernel).
-static int launch_scales_colmajor(const void *stage, int64_t rows, int64_t H, int32_t flags,
-                                  int64_t rows_per_mat, void *out, const int64_t *seg_indptr,
-                                  const int32_t *counts, int32_t L, int32_t alignment,
-                                  const int32_t *masked_m, hipStream_t s)
-{
-    if (rows <= 0) return CDL_OK;
-    const int64_t words = scale_words(H, flags);
-    const int64_t G = H / CDL_FP8_GROUP;
-    const int32_t tail = (flags & CDL_FP8_SCALE_PACKED) ? (int32_t)(G % 4) : 0;
-    const dim3 grid((unsigned)((rows + kTileRows - 1) / kTileRows),
-                    (unsigned)((words + kTileWords - 1) / kTileWords));
-    const size_t lds = (!masked_m && alignment > 1) ? (size_t)(L + 1) * sizeof(int64_t) : 0;
-    scales_colmajor_kernel<<<grid, dim3(256), lds, s>>>(
-        (const uint32_t *)stage, rows, words, rows_per_mat, (rows_per_mat + 3) / 4 * 4,
-        (uint32_t *)out, seg_indptr, counts, L, alignment, masked_m, tail);
-    return launch_status();
+    return layout_ws_bytes(T, k, L);
 }
 
 int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const int32_t *topk_ids,
@@ -2438,21 +2217,8 @@ int cdl_permute_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k, const in
     a.x = (const u32x4 *)x;
     a.chunks = H / 8;
     a.cap_rows = cap_rows;
-    const bool staged = (scale_flags & CDL_FP8_SCALE_COLMAJOR) && cap_rows > 0 &&
-                        !fp8_small_batch(T, k, L) &&
-                        ws_bytes >= cdl_permute_fp8_workspace_size(T, k, L, H, scale_flags, cap_rows);
-    if (!staged) {
-        a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap_rows);
-        return run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
-    }
-    // row-major staging after the layout's part of the workspace, then the
-    // column-major matrix (one matrix of cap_rows rows)
-    void *stage = (uint8_t *)ws + layout_ws_bytes(T, k, L);
-    a.fp8 = make_fp8_out(out_q, stage, scale_flags & ~CDL_FP8_SCALE_COLMAJOR, H, cap_rows);
-    rc = run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
-    if (rc != CDL_OK) return rc;
-    return launch_scales_colmajor(stage, cap_rows, H, scale_flags, cap_rows, out_scales, seg_indptr,
-                                  counts, L, alignment, nullptr, (hipStream_t)stream);
+    a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap_rows);
+    return run_layout<kRowsFp8>(a, ws, (hipStream_t)stream);
 }
 
 static int check_rank_layout_sizes(int64_t T, int32_t k, int32_t E, int32_t R, int32_t rpn)
@@ -2630,22 +2396,8 @@ int cdl_permute_ll_fp8(const uint16_t *x, int64_t T, int64_t H, int32_t k,
     if (H % CDL_FP8_GROUP != 0 || !valid_scale_flags(scale_flags)) return CDL_ERR_UNSUPPORTED;
     if (cap > 0 && !out_scales) return CDL_ERR_NULL_POINTER;
     if (cap > 0 && (!aligned(out_q, 8) || !aligned(out_scales, 4))) return CDL_ERR_UNSUPPORTED;
-    const int64_t rows = (int64_t)L * cap;
-    const bool staged = (scale_flags & CDL_FP8_SCALE_COLMAJOR) && rows > 0 &&
-                        !fp8_small_batch(T, k, L) &&
-                        ws_bytes >= cdl_permute_fp8_workspace_size(T, k, L, H, scale_flags, rows);
-    if (!staged) {
-        a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap);
-        return run_layout<kRowsLLFp8>(a, ws, (hipStream_t)stream);
-    }
-    // row-major staging of the L * cap padded rows, then one column-major
-    // matrix per expert
-    void *stage = (uint8_t *)ws + layout_ws_bytes(T, k, L);
-    a.fp8 = make_fp8_out(out_q, stage, scale_flags & ~CDL_FP8_SCALE_COLMAJOR, H, cap);
-    rc = run_layout<kRowsLLFp8>(a, ws, (hipStream_t)stream);
-    if (rc != CDL_OK) return rc;
-    return launch_scales_colmajor(stage, rows, H, scale_flags, cap, out_scales, nullptr, nullptr, L,
-                                  1, masked_m, (hipStream_t)stream);
+    a.fp8 = make_fp8_out(out_q, out_scales, scale_flags, H, cap);
+    return run_layout<kRowsLLFp8>(a, ws, (hipStream_t)stream);
 }
 
 

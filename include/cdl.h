@@ -242,17 +242,13 @@ int cdl_permute_fp8_tensor(const uint16_t *x, int64_t T, int64_t H, int32_t k,
                            void *ws, size_t ws_bytes, void *stream);
 
 /*
- * cdl_permute_fp8_workspace_size -- workspace bytes with which
- * cdl_permute_fp8 (rows = cap_rows) and cdl_permute_ll_fp8 (rows = L * cap)
- * write column-major scales through a row-major staging copy in the
- * workspace and a second kernel that turns 64 x 64 tiles around, so that
- * every write is a whole line (written in place, each row's scales land in a
- * different line per scale word and the lines are shared by rows from every
- * XCD).  A workspace of only cdl_dispatch_layout_workspace_size bytes is
- * still accepted and the scales are then written in place; the results are
- * the same.  Small batches (at most 512 tokens and T*k <= 1024) always write
- * in place: their few scale rows cost less than the second launch.  Equal to cdl_dispatch_layout_workspace_size for row-major
- * formats; 0 for invalid arguments (H not a multiple of 128, bad flags).
+ * cdl_permute_fp8_workspace_size -- workspace bytes for cdl_permute_fp8
+ * (rows = cap_rows) and cdl_permute_ll_fp8 (rows = L * cap) in the given
+ * scale format: cdl_dispatch_layout_workspace_size(T, k, L) for every valid
+ * format (column-major scales are written in place, each scale word with the
+ * temporal cache policy so that the L2 merges the words a line receives from
+ * 32 rows before they reach memory).  0 for invalid arguments (H not a
+ * multiple of 128, bad flags).
  */
 size_t cdl_permute_fp8_workspace_size(int64_t T, int32_t k, int32_t L, int64_t H,
                                       int32_t scale_flags, int64_t rows);

@@ -252,15 +252,14 @@ def test_graph_replay_low_latency_step():
         check_layout(lay_g, ids, w.expert_begin, w.L)
 
 
-@pytest.mark.parametrize("flags,cap,T,staged", [(0, 1024, 128, True), (UE_ | CM_ | PK_, 1024, 128, True),
+@pytest.mark.parametrize("flags,cap,T,own_ws", [(0, 1024, 128, True), (UE_ | CM_ | PK_, 1024, 128, True),
                                                 (UE_ | CM_ | PK_, 1024, 128, False),
                                                 (UE_ | CM_, 5, 100, True), (UE_ | CM_, 5, 100, False),
                                                 (CM_, 256, 2500, True), (0, 256, 2500, True)])
-def test_permute_ll_fp8_parity(flags, cap, T, staged):
+def test_permute_ll_fp8_parity(flags, cap, T, own_ws):
     """One-call LL fp8 dispatch; T = 2500 takes the count kernel and 4 tokens
-    per permute workgroup (the fp8 plan).  Column-major scales are staged in
-    the workspace and turned around by a second kernel, or (staged = False,
-    only the layout's workspace) written in place."""
+    per permute workgroup (the fp8 plan).  The binding's own workspace, or
+    (own_ws = False) one of the layout's size passed in."""
     w = W.WORKLOADS["ll_decode"]
     if T != w.T:
         w = w.scaled(T=T, H=512)
@@ -271,7 +270,7 @@ def test_permute_ll_fp8_parity(flags, cap, T, staged):
     q = torch.zeros(w.L, cap, w.H, dtype=torch.uint8, device=DEV)
     sb = torch.full((max(S.size, 1),), 0xEE, dtype=torch.uint8, device=DEV)
     st = status_word()
-    ws = None if staged else torch.empty(cdl.layout_workspace_size(w.T, w.k, w.L),
+    ws = None if own_ws else torch.empty(cdl.layout_workspace_size(w.T, w.k, w.L),
                                          dtype=torch.uint8, device=DEV)
     lay, q, sb, gmm, gll = cdl.permute_ll_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, cap,
                                               scale_flags=flags, out_q=q, out_scales=sb, status=st,
@@ -899,7 +898,7 @@ def test_permute_fp8_small_batch_rows_over_waves(T, H):
     chunks per lane: one group (only wave 0 has chunks), ragged packing
     (9 groups), one full 7168-wide pass, and two passes (65 groups).  Normal
     permute (fp32 scales, canary rows) and low-latency permute (packed
-    column-major UE8M0 scales staged in the workspace) against the oracle."""
+    column-major UE8M0 scales) against the oracle."""
     w = W.WORKLOADS["ll_decode"].scaled(T=T, H=H)
     announce("fp8 small batch over waves T=%d H=%d" % (T, H))
     x, ids, wts = W.make_inputs(w)
@@ -1075,7 +1074,7 @@ def test_full_size_dsv3_aligned_and_deepgemm_fp8():
     H = 7168, 32 of 256 experts, top-8, segments padded to 128 rows, output
     sized to the padded row count): the bf16 permute (padding rows untouched)
     and the fp8 permute in the DeepGEMM format (packed column-major UE8M0
-    scales staged in the workspace), bit for bit against the oracle."""
+    scales), bit for bit against the oracle."""
     w = W.WORKLOADS["dsv3_prefill"]
     A = 128
     announce("full dsv3_prefill aligned 128 + DeepGEMM fp8")
@@ -1236,13 +1235,13 @@ def test_fp8_scale_formats_parity(flags):
     sb = filled_scales(nbytes)
     st = status_word()
     cdl.dispatch_fp8(x.to(DEV), lay, out_q=q, out_scales=sb, status=st, scale_flags=flags)
-    # fused permute (column-major formats: staged row-major, then turned
-    # around by a second kernel) ...
+    # fused permute (T = 517 counts itself: one kernel) with the binding's
+    # workspace ...
     q2 = torch.zeros(cap, w.H, dtype=torch.uint8, device=DEV)
     sb2 = filled_scales(nbytes)
     cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q2, out_scales=sb2,
                     status=st, scale_flags=flags)
-    # ... and with only the layout's workspace: written in place
+    # ... and with one of only the layout's size
     q3 = torch.zeros(cap, w.H, dtype=torch.uint8, device=DEV)
     sb3 = filled_scales(nbytes)
     ws = torch.empty(cdl.layout_workspace_size(w.T, w.k, w.L), dtype=torch.uint8, device=DEV)
@@ -1255,15 +1254,18 @@ def test_fp8_scale_formats_parity(flags):
     assert np.array_equal(raw_bytes(sb3), S)
 
 
+@pytest.mark.parametrize("H", [1152, 7296])
 @pytest.mark.parametrize("flags", [CM, UE | CM | PK])
 @pytest.mark.parametrize("A", [1, 128])
-def test_permute_fp8_colmajor_staged(flags, A):
-    """Column-major scales staged in the workspace at the fp8 dispatch shape
-    (4096 tokens, count kernel) and with segments padded to 128 rows: every
-    real row's scales land in its column, padding rows, rows past R and the
-    TMA padding of each column keep the fill."""
-    w = W.WORKLOADS["fp8_dispatch"].scaled(H=1152)                   # 9 groups: ragged packing
-    announce("fp8 colmajor staged flags=%d A=%d" % (flags, A))
+def test_permute_fp8_colmajor_large(flags, A, H):
+    """Column-major scales at the fp8 dispatch shape (4096 tokens, count
+    kernel), with segments padded to 128 rows or not: the split permute
+    (H = 1152, 9 groups: ragged packing) and the one-kernel permute of rows
+    of two passes (H = 7296, 57 groups).  Every real row's scales land in its
+    column; padding rows, rows past R and the TMA padding of each column keep
+    the fill."""
+    w = W.WORKLOADS["fp8_dispatch"].scaled(H=H)
+    announce("fp8 colmajor flags=%d A=%d H=%d" % (flags, A, H))
     x, ids, wts = W.make_inputs(w)
     _, s_, d, _ = oracle.layout_aligned(ids.numpy(), w.expert_begin, w.L, A)
     cap = int(s_[-1]) + 5

@@ -5,8 +5,8 @@ reading (a group's amax skips NaN, an infinite amax gives an infinite fp32
 scale or a power-of-two scale capped at 2^127, a NaN quotient becomes the
 e4m3fn NaN code with the sign of x, the per-tensor cast saturates +-inf).
 Here the kernels must match that reading bit for bit on every fp8 path:
-the unfused and fused normal dispatches in every scale format (in place and
-staged), the low-latency dispatches, and the per-tensor cast.  Groups
+the unfused and fused normal dispatches in every scale format, the
+low-latency dispatches, and the per-tensor cast.  Groups
 without a non-finite value in the same rows and waves must be unaffected.
 """
 import numpy as np
@@ -71,9 +71,9 @@ def raw(t):
 @pytest.mark.parametrize("flags", FORMATS)
 @pytest.mark.parametrize("T", [300, 4096])
 def test_fp8_nonfinite_normal_paths(flags, T):
-    """Unfused scatter, fused permute (staged column-major scales when the
-    workspace allows) and fused permute with only the layout workspace
-    (scales in place): every byte and scale as the oracle gives them."""
+    """Unfused scatter, fused permute with the binding's workspace and with
+    one of only the layout's size: every byte and scale as the oracle gives
+    them."""
     w = W.WORKLOADS["fp8_dispatch"].scaled(T=T, H=1152 if T < 1000 else 7168)
     announce("fp8 non-finite normal T=%d flags=%d" % (T, flags))
     x, xb, ids, _ = planted_rows(w)
