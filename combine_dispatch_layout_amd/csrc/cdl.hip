@@ -97,8 +97,6 @@ __device__ __forceinline__ int32_t buf_ld4(rsrc_t r, uint32_t voff, uint32_t sof
     return (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
-__device__ __forceinline__ int32_t uniform(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-
 // Index of the calling wave in its workgroup, as a wave-uniform (scalar)
 // value: the compiler does not infer that threadIdx.x / 64 is uniform, and a
 // buffer resource derived from a non-uniform value costs a readfirstlane
@@ -173,45 +171,34 @@ __device__ __forceinline__ void set_status(int32_t *status, int32_t bit)
 }
 
 // ---------------------------------------------------------------------------
-// fp8 group quantisation of one 16-byte chunk (8 bf16) held by a lane; the
-// 16 lanes of a DPP row hold one group of 128 elements.
+// fp8 group quantisation in the pair layout: a lane holds 32 contiguous bytes
+// of a row (16 bf16, two 16-byte chunks: chunks 2l and 2l + 1 of a block of
+// 128), so the 8 lanes of a DPP half row hold one group of 128 elements.  A
+// lane computes its group's scale and reciprocal once per 16 elements, the
+// group amax takes three DPP steps, and the 16 e4m3fn bytes leave in one
+// 16-byte store.  Measured against one chunk per lane (16 lanes a group) at
+// T = 4096, H = 7168, top-8 over 32 of 256 experts: fp8 permute 19.4 ->
+// 18.0 us.
 // ---------------------------------------------------------------------------
 
 // Group amax.  Magnitudes of floats order like their bit patterns, so the
 // maximum is taken on integers (no NaN canonicalisation, and the DPP moves
-// fuse into the max): per lane over the eight bf16 magnitudes in 16-bit
-// halves, then over the 16 lanes of a DPP row (lanes 16r .. 16r+15), which
-// hold one 128-element group: quad_perm swaps at distance 1 and 2 give each
-// quad its maximum, row_half_mirror pairs the two quads of each half row,
-// row_mirror the two halves.  About 12 VALU ops, no LDS traffic.
+// fuse into the max): per lane over its 16 bf16 magnitudes in 16-bit halves,
+// then over the 8 lanes of a half row (lanes 8j .. 8j+7): quad_perm swaps at
+// distance 1 and 2 give each quad its maximum, row_half_mirror pairs the two
+// quads.
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_umax_step(uint32_t a)
 {
     const uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, CTRL, 0xF, 0xF, false);
     return a > b ? a : b;
 }
-// The maximum over the 16 lanes of a DPP row of one 32-bit value per lane.
-__device__ __forceinline__ uint32_t row_umax(uint32_t a)
+__device__ __forceinline__ uint32_t half_row_umax(uint32_t a)
 {
     a = dpp_umax_step<0xB1>(a);    // quad_perm [1,0,3,2]
     a = dpp_umax_step<0x4E>(a);    // quad_perm [2,3,0,1]
-    a = dpp_umax_step<0x141>(a);   // row_half_mirror
-    a = dpp_umax_step<0x140>(a);   // row_mirror
+    a = dpp_umax_step<0x141>(a);   // row_half_mirror: the other quad of the 8 lanes
     return a;
-}
-
-// Bit pattern of the group's largest magnitude (a NaN pattern orders above
-// every other): its bf16 magnitude in the upper half of a binary32.
-__device__ __forceinline__ uint32_t group_amax_bits(u32x4 v)
-{
-    using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
-    const u16x2 m0 = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
-    const u16x2 m1 = __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu);
-    const u16x2 m2 = __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu);
-    const u16x2 m3 = __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu);
-    const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(m0, m1),
-                                              __builtin_elementwise_max(m2, m3));
-    return row_umax((uint32_t)(m.x > m.y ? m.x : m.y) << 16);
 }
 
 // Groups with amax >= 2^-96 (kFastQuotientMinBits) divide by the scale with one
@@ -230,7 +217,7 @@ __device__ __forceinline__ uint32_t group_amax_bits(u32x4 v)
 constexpr uint32_t kFastQuotientMinBits = 0x0F800000u;   // bits of 2^-96
 static_assert(__builtin_bit_cast(float, kFastQuotientMinBits) == 0x1p-96f, "fast-path threshold");
 
-// Exact path of one chunk, taken by the whole wave when any of its groups is
+// Exact path of a pair, taken by the whole wave when any of its groups is
 // tiny (amax < 2^-96) or holds a non-finite value; it gives the same bytes as
 // the fast paths for every other group.  Non-finite values (the pages say
 // nothing of them; the oracle states the same reading):
@@ -242,101 +229,119 @@ static_assert(__builtin_bit_cast(float, kFastQuotientMinBits) == 0x1p-96f, "fast
 //     the E8M0 NaN code;
 //   * an element whose quotient is NaN (or infinite, with unclamped
 //     power-of-two scaling) becomes the e4m3fn NaN code with x's sign.
-__device__ __forceinline__ u32x2 quant_chunk_exact(u32x4 v, bool ue8m0, float *scale, int *scale_exp)
+__device__ __forceinline__ u32x4 quant_pair_exact(u32x4 a, u32x4 b, bool ue8m0, float *scale)
 {
-    const uint32_t h[8] = {v.x & 0xFFFFu, v.x >> 16, v.y & 0xFFFFu, v.y >> 16,
-                           v.z & 0xFFFFu, v.z >> 16, v.w & 0xFFFFu, v.w >> 16};
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    uint32_t h[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        h[2 * i] = w[i] & 0xFFFFu;
+        h[2 * i + 1] = w[i] >> 16;
+    }
     uint32_t m = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 16; ++e) {
         const uint32_t mag = h[e] & 0x7FFFu;
         if (mag <= kBf16ExpMask && mag > m) m = mag;
     }
-    const float a = __uint_as_float(row_umax(m << 16));
-    float q[8];
+    const float am = __uint_as_float(half_row_umax(m << 16));
+    float q[16];
     if (ue8m0) {
         int e = -127;
-        if (a > 0.0f) {
+        if (am > 0.0f) {
             int ex = 0;
-            const float mt = frexpf(a, &ex);
-            e = a == __builtin_huge_valf() ? 127 : ex - 9 + (mt > 0.875f ? 1 : 0);
+            const float mt = frexpf(am, &ex);
+            e = am == __builtin_huge_valf() ? 127 : ex - 9 + (mt > 0.875f ? 1 : 0);
             e = e < -127 ? -127 : e;
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = ldexpf(__uint_as_float(h[i] << 16), -e);
+        for (int i = 0; i < 16; ++i) q[i] = ldexpf(__uint_as_float(h[i] << 16), -e);
         *scale = ldexpf(1.0f, e);
-        *scale_exp = e;
     } else {
-        const float s = a / 448.0f;                     // correctly rounded
+        const float sc = am / 448.0f;                    // correctly rounded
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 16; ++i) {
             const float x = __uint_as_float(h[i] << 16);
-            const float d = a > 0.0f ? x / s : x;
+            const float d = am > 0.0f ? x / sc : x;
             q[i] = d > 448.0f ? 448.0f : (d < -448.0f ? -448.0f : d);
         }
-        *scale = s;
-        *scale_exp = 0;
+        *scale = sc;
     }
-    uint32_t b[8];
+    uint32_t bt[16];
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-        const uint32_t p = pack2_e4m3(__builtin_isfinite(q[i]) ? q[i] : 0.0f,
-                                      __builtin_isfinite(q[i + 1]) ? q[i + 1] : 0.0f);
-        b[i] = __builtin_isfinite(q[i]) ? (p & 0xFFu) : e4m3_nan_of(h[i]);
-        b[i + 1] = __builtin_isfinite(q[i + 1]) ? (p >> 8) : e4m3_nan_of(h[i + 1]);
+    for (int i = 0; i < 16; i += 2) {
+        const uint32_t pk = pack2_e4m3(__builtin_isfinite(q[i]) ? q[i] : 0.0f,
+                                       __builtin_isfinite(q[i + 1]) ? q[i + 1] : 0.0f);
+        bt[i] = __builtin_isfinite(q[i]) ? (pk & 0xFFu) : e4m3_nan_of(h[i]);
+        bt[i + 1] = __builtin_isfinite(q[i + 1]) ? (pk >> 8) : e4m3_nan_of(h[i + 1]);
     }
-    return u32x2{b[0] | b[1] << 8 | b[2] << 16 | b[3] << 24, b[4] | b[5] << 8 | b[6] << 16 | b[7] << 24};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o[i] = bt[4 * i] | bt[4 * i + 1] << 8 | bt[4 * i + 2] << 16 | bt[4 * i + 3] << 24;
+    return u32x4{o[0], o[1], o[2], o[3]};
 }
 
-// Returns the 8 e4m3fn bytes of the chunk; *scale receives the group scale
-// and *scale_exp its exponent (power-of-two scales only).
+// Returns the 16 e4m3fn bytes of the lane's pair; *scale receives the group
+// scale (fp32, or the power of two of UE8M0 scales).  Lanes past the row
+// (in_row false) never send the wave to the exact path; their bytes are not
+// stored.
 //
 // Power-of-two (UE8M0) scales: p is the smallest power of two >= 2^-127 with
 // 448 * p >= amax.  With amax = m * 2^ex, m in [0.5, 1) (frexp), that is
 // 2^(ex - 9) when m <= 0.875 (448 = 0.875 * 2^9) and 2^(ex - 8) otherwise;
 // x / p is then an exact power-of-two scaling and needs no clamp.
-__device__ __forceinline__ u32x2 quant_chunk(u32x4 v, bool ue8m0, float *scale, int *scale_exp)
+__device__ __forceinline__ u32x4 quant_pair(u32x4 a, u32x4 b, bool ue8m0, bool in_row, float *scale)
 {
-    const uint32_t ab = group_amax_bits(v);
-    // one exact path for the whole wave when any group needs it (a uniform
-    // branch: the fast path below carries no exec-mask bookkeeping)
-    // non-finite (ab >= the infinity pattern) or, for fp32 scales, tiny: one
-    // unsigned range check
+    using u16x2 = unsigned short __attribute__((ext_vector_type(2)));
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    const uint32_t ab = half_row_umax((uint32_t)(m.x > m.y ? m.x : m.y) << 16);
     const uint32_t lo = ue8m0 ? 0u : kFastQuotientMinBits;
-    const bool special = ab - lo >= (kBf16ExpMask << 16) - lo;
-    if (__builtin_expect(__ballot(special) != 0, 0)) return quant_chunk_exact(v, ue8m0, scale, scale_exp);
-    const float f[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
-                        bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
-    const float a = __uint_as_float(ab);
-    float q[8];
+    // one exact path for the whole wave when any group needs it (a uniform
+    // branch: the fast path below carries no exec-mask bookkeeping):
+    // non-finite (ab >= the infinity pattern) or, for fp32 scales, tiny; one
+    // unsigned range check
+    const bool special = in_row && ab - lo >= (kBf16ExpMask << 16) - lo;
+    if (__builtin_expect(__ballot(special) != 0, 0)) return quant_pair_exact(a, b, ue8m0, scale);
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        f[2 * i] = bf16_lo(w[i]);
+        f[2 * i + 1] = bf16_hi(w[i]);
+    }
+    const float am = __uint_as_float(ab);
+    float q[16];
     if (ue8m0) {
         int ex = 0;
-        const float m = frexpf(a, &ex);
-        int e = a > 0.0f ? ex - 9 + (m > 0.875f ? 1 : 0) : -127;
+        const float mt = frexpf(am, &ex);
+        int e = am > 0.0f ? ex - 9 + (mt > 0.875f ? 1 : 0) : -127;
         e = e < -127 ? -127 : e;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) q[i] = ldexpf(f[i], -e);
+        for (int i = 0; i < 16; ++i) q[i] = ldexpf(f[i], -e);
         *scale = ldexpf(1.0f, e);
-        *scale_exp = e;
     } else {
-        // s = fl(a / 448) = fl((a * 2^-6) / 7) by one correction step with
-        // fl(1/7); y = fl(1 / s) by one correction step from v_rcp_f32 (within
-        // 1 ulp); both exact for every bf16 a >= 2^-96 (exhaustive CPU check)
+        // sc = fl(amax / 448) = fl((amax * 2^-6) / 7) by one correction step
+        // with fl(1/7); y = fl(1 / sc) by one correction step from v_rcp_f32
+        // (within 1 ulp); both exact for every bf16 amax >= 2^-96 (exhaustive
+        // CPU check)
         const float c7 = 1.0f / 7.0f;
-        const float t = a * 0x1p-6f;
+        const float t = am * 0x1p-6f;
         const float s0 = t * c7;
-        const float s = fmaf(fmaf(-s0, 7.0f, t), c7, s0);
-        const float r0 = __builtin_amdgcn_rcpf(s);
-        const float y = fmaf(fmaf(-s, r0, 1.0f), r0, r0);
+        const float sc = fmaf(fmaf(-s0, 7.0f, t), c7, s0);
+        const float r0 = __builtin_amdgcn_rcpf(sc);
+        const float y = fmaf(fmaf(-sc, r0, 1.0f), r0, r0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float q0 = f[e] * y;
-            q[e] = fmaf(-fmaf(q0, s, -f[e]), y, q0);
+        for (int i = 0; i < 16; ++i) {
+            const float q0 = f[i] * y;
+            q[i] = fmaf(-fmaf(q0, sc, -f[i]), y, q0);
         }
-        *scale = s;
-        *scale_exp = 0;
+        *scale = sc;
     }
-    return u32x2{pack4_e4m3(q[0], q[1], q[2], q[3]), pack4_e4m3(q[4], q[5], q[6], q[7])};
+    return u32x4{pack4_e4m3(q[0], q[1], q[2], q[3]), pack4_e4m3(q[4], q[5], q[6], q[7]),
+                 pack4_e4m3(q[8], q[9], q[10], q[11]), pack4_e4m3(q[12], q[13], q[14], q[15])};
 }
 
 // Per-tensor cast of one 16-byte chunk (8 bf16) to 8 e4m3fn bytes:
@@ -388,20 +393,13 @@ struct Fp8Out {
     int64_t ld;            // column stride of a column-major matrix
 };
 
-// The 32-bit word a scale is stored as: the fp32 scale, or the exponent byte
-// log2(p) + 127 of a packed format.
-__device__ __forceinline__ uint32_t scale_word(const Fp8Out &o, float p, int e)
-{
-    return (o.flags & CDL_FP8_SCALE_PACKED) ? (uint32_t)(e + 127) : __float_as_uint(p);
-}
-
 // ---------------------------------------------------------------------------
 // layout plan
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxChunks = 14;          // 16-byte chunks a lane holds per pass (bf16 rows): 14 x 64 = 896, one row at H = 7168
 constexpr int kMaxChunksFp8 = 14;       // the same for rows quantised on the way (one pass at
-                                        // H = 7168; quantised kFp8Part chunks at a time)
+                                        // H = 7168, 7 pairs of chunks per lane)
 constexpr int kCountThreads = 256;
 constexpr int kSelfCountIds = 8;        // ids per thread when workgroups count every slot
 constexpr int kFp8WavesSmall = 7;       // waves per token for fp8 rows of small self-counted
@@ -498,48 +496,49 @@ __global__ __launch_bounds__(kCountThreads) void layout_count_kernel(
 // from the Infinity Cache), and back-to-back fp8 dispatches measured faster
 // without the dirty lines they would leave there (scatter 20.7 -> 18.9 us at
 // T = 4096, H = 7168).  Column-major scales are the exception (see
-// store_scales_masked).
+// store_scales_pairs).
 //
-// The first kFp8Part chunks of a row pass are loaded before the layout or
-// the wait for them; the rest follow as those chunks are quantised.
-constexpr int kFp8Part = 7;
+// fp8 row passes hold the row in the pair layout (quant_pair): a pass of a
+// wave starting at chunk c0 spans NCH * 64 chunks, and lane l keeps chunks
+// c0 + 128p + 2l and c0 + 128p + 2l + 1 in v[2p] and v[2p + 1].  The first
+// kFp8AheadPairs pairs are loaded before the layout or the wait for it; the
+// rest follow as pairs are quantised.  Row offsets sit in the VGPR operand,
+// which the range check covers.
+constexpr int kFp8AheadPairs = 4;
 template <int NCH>
-__device__ __forceinline__ void load_fp8_first_parts(u32x4 (&v)[NCH], rsrc_t xr, uint32_t voff, uint32_t pass)
+__device__ __forceinline__ void load_fp8_first_parts(u32x4 (&v)[NCH], rsrc_t xr, int lane, int64_t c0)
 {
+    static_assert(NCH % 2 == 0, "a pass holds whole pairs");
+    const uint32_t voff = (uint32_t)lane * 32u + (uint32_t)(c0 * 16);
 #pragma unroll
-    for (int u = 0; u < NCH; ++u)
-        if (u < kFp8Part) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
+    for (int p = 0; p < NCH / 2; ++p) {
+        if (p < kFp8AheadPairs) {
+            v[2 * p] = buf_ld16(xr, voff + p * 2048, 0);
+            v[2 * p + 1] = buf_ld16(xr, voff + p * 2048 + 16u, 0);
+        }
+    }
 }
 
-// A row pass of fp8 rows, chunk by chunk: chunk u is quantised and stored to
-// every destination before chunk u + 1, and the load of chunk u + kFp8Part is
-// issued as soon as chunk u is quantised (its registers are free then).  The
-// caller loads chunks [0, kFp8Part) of the pass.  The wave thus keeps
-// kFp8Part chunks of loads in flight, and its stores drain while it
-// quantises the next chunks, instead of quantising a part, then storing it,
-// then waiting for the next part.  Destinations: bit j of dmask is set when
-// slot j's row (lane j of dlane) is stored; only those are visited.
-// The scales of one row pass reach memory with one store per destination
-// row: lane 16r + i (i < the pass's chunks per lane) holds the scale of its
-// wave's chunk u = i in DPP row r, which is group c0/16 + 4i + r of the pass
-// starting at chunk c0, as the 32-bit word to store (the fp32 scale, or the
-// exponent byte log2(p) + 127 of a packed format).  A destination row's pass
-// scales are then written by one instruction of up to 56 lanes (dword
-// stores, byte stores when packed).  Column-major scales are stored with the
-// temporal policy: each lane writes one word of a line that 32 rows share,
-// and the L2 merges those pieces before they reach memory; streamed, every
-// piece went out by itself (T = 4096, H = 7168, top-8 over 32 of 256
-// experts, padded to 128: packed UE8M0 22.6 -> 20.2 us, fp32 29.9 -> 21.5
-// us; row-major 19.2 us).
-template <int NCH>
-__device__ __forceinline__ void store_scales_masked(uint32_t sw, int lane, int64_t c0, int64_t chunks,
-                                                    const Fp8Out &o, int32_t dlane, uint64_t dmask)
+// The scales of a pass in the pair layout starting at chunk c0: lane 8j + p
+// (p < NP) holds the fp32 bits of the scale of group c0 / 16 + 8p + j, so a
+// destination row's scales of the pass leave in one store of up to 56 lanes
+// (dword stores; byte stores of the exponent e + 127 of the power of two
+// 2^e >= 2^-127, its bits >> 23, when packed).  Column-major scales are
+// stored with the temporal policy: each lane writes one word of a line that
+// 32 rows share, and the L2 merges those pieces before they reach memory;
+// streamed, every piece went out by itself (T = 4096, H = 7168, top-8 over
+// 32 of 256 experts, padded to 128: packed UE8M0 22.6 -> 20.2 us, fp32
+// 29.9 -> 21.5 us; row-major 19.2 us).
+template <int NP>
+__device__ __forceinline__ void store_scales_pairs(uint32_t sw, int lane, int64_t c0, int64_t chunks,
+                                                   const Fp8Out &o, int32_t dlane, uint64_t dmask)
 {
-    const int i = lane & 15;
-    const int64_t g = c0 / 16 + 4 * i + (lane >> 4);      // this lane's group
-    const bool active = i < NCH && g < chunks / 16;
+    const int pp = lane & 7;
+    const int64_t g = c0 / 16 + (int64_t)pp * 8 + (lane >> 3);
+    const bool active = pp < NP && g < chunks / 16;
     const bool packed = (o.flags & CDL_FP8_SCALE_PACKED) != 0;
     const bool colmajor = (o.flags & CDL_FP8_SCALE_COLMAJOR) != 0;
+    const uint32_t word = packed ? sw >> 23 : sw;
     const int64_t words = packed ? (o.groups + 3) / 4 : o.groups;
     const int64_t col = packed ? g / 4 : g;
     const int64_t lane_off = colmajor ? col * o.ld * 4 + (packed ? (g & 3) : 0) : (packed ? g : g * 4);
@@ -554,30 +553,42 @@ __device__ __forceinline__ void store_scales_masked(uint32_t sw, int lane, int64
             base = (int64_t)dst * words * 4;
         }
         if (!active) continue;
-        uint8_t *p = o.s + base + lane_off;
+        uint8_t *q = o.s + base + lane_off;
         if (colmajor) {
             if (packed)
-                *p = (uint8_t)sw;
+                *q = (uint8_t)word;
             else
-                *reinterpret_cast<uint32_t *>(p) = sw;
+                *reinterpret_cast<uint32_t *>(q) = word;
         } else if (packed) {
-            __builtin_nontemporal_store((uint8_t)sw, p);
+            __builtin_nontemporal_store((uint8_t)word, q);
         } else {
-            __builtin_nontemporal_store(sw, reinterpret_cast<uint32_t *>(p));
+            __builtin_nontemporal_store(word, reinterpret_cast<uint32_t *>(q));
         }
     }
 }
 
+// A row pass of fp8 rows, pair by pair: pair p is quantised and stored to
+// every destination before pair p + 1, and the load of pair
+// p + kFp8AheadPairs is issued as soon as pair p is quantised (its registers
+// are free then).  The caller loads the first pairs (load_fp8_first_parts).
+// The wave thus keeps kFp8AheadPairs pairs of loads in flight, and its
+// stores drain while it quantises the next pairs.  Destinations: bit j of
+// dmask is set when slot j's row (lane j of dlane) is stored; only those are
+// visited.  Pairs past the row end are quantised all the same (their loads
+// return zeros) and their stores fall outside the range: a branch around
+// them would leave the compiler's wait counts for the loads in flight
+// inexact (see below).
 template <int NCH>
 __device__ __forceinline__ void quant_store_pass(u32x4 (&v)[NCH], int lane, int64_t c0, int64_t chunks,
                                                  const Fp8Out &o, bool ue8m0, int32_t dlane,
-                                                 uint64_t dmask, rsrc_t xr, uint32_t voff, uint32_t pass)
+                                                 uint64_t dmask, rsrc_t xr)
 {
+    constexpr int NP = NCH / 2;
     uint32_t sw = 0;
     const uint32_t q_bytes = (uint32_t)(chunks * 8);
     // The first two destinations get a fixed number of store instructions
-    // per chunk (a missing one stores through an empty range: no memory
-    // access), so the compiler's wait counts for the chunk loads still in
+    // per pair (a missing one stores through an empty range: no memory
+    // access), so the compiler's wait counts for the pair loads still in
     // flight stay exact; with a loop of unknown length before them it must
     // assume the loop stored nothing, and each wait for a load would also
     // wait for the stores issued since.  More destinations (a tenth of the
@@ -588,25 +599,29 @@ __device__ __forceinline__ void quant_store_pass(u32x4 (&v)[NCH], int lane, int6
     const rsrc_t o0 = make_rsrc(o.q + (d0 >= 0 ? (int64_t)d0 * chunks : 0), d0 >= 0 ? q_bytes : 0u);
     const rsrc_t o1 = make_rsrc(o.q + (d1 >= 0 ? (int64_t)d1 * chunks : 0), d1 >= 0 ? q_bytes : 0u);
     const uint64_t rest = m1 & (m1 - 1);
+    const uint32_t loff = (uint32_t)lane * 32u + (uint32_t)(c0 * 16);
+    // 16-byte stores take their whole offset in the VGPR operand (see
+    // combine_rows_pipe)
+    const uint32_t soff = (uint32_t)lane * 16u + (uint32_t)(c0 * 8);
 #pragma unroll
-    for (int u = 0; u < NCH; ++u) {
+    for (int p = 0; p < NP; ++p) {
         float sc;
-        int ex;
-        const u32x2 q = quant_chunk(v[u], ue8m0, &sc, &ex);
-        // lane 16r + i keeps the scale of chunk i (see store_scales_masked)
-        const uint32_t w = scale_word(o, sc, ex);
-        sw = (lane & 15) == u ? w : sw;
-        if (u + kFp8Part < NCH) v[u + kFp8Part] = buf_ld16(xr, voff, pass + (u + kFp8Part) * kWave * 16);
-        const uint32_t qoff = (uint32_t)(c0 * 8) + u * kWave * 8;
-        buf_st8_stream(o0, q, (uint32_t)lane * 8u, qoff);
-        buf_st8_stream(o1, q, (uint32_t)lane * 8u, qoff);
+        const u32x4 q = quant_pair(v[2 * p], v[2 * p + 1], ue8m0, c0 + p * 128 + 2 * lane < chunks, &sc);
+        // lane 8j + p keeps the scale of pair p (see store_scales_pairs)
+        sw = (lane & 7) == p ? __float_as_uint(sc) : sw;
+        if (p + kFp8AheadPairs < NP) {
+            v[2 * (p + kFp8AheadPairs)] = buf_ld16(xr, loff + (p + kFp8AheadPairs) * 2048, 0);
+            v[2 * (p + kFp8AheadPairs) + 1] = buf_ld16(xr, loff + (p + kFp8AheadPairs) * 2048 + 16u, 0);
+        }
+        buf_st16_stream(o0, q, soff + p * 1024, 0);
+        buf_st16_stream(o1, q, soff + p * 1024, 0);
         for (uint64_t m = rest; m; m &= m - 1) {
             const int32_t dst = __builtin_amdgcn_readlane(dlane, (int)__builtin_ctzll(m));
             const rsrc_t oq = make_rsrc(o.q + (int64_t)dst * chunks, q_bytes);
-            buf_st8_stream(oq, q, (uint32_t)lane * 8u, qoff);
+            buf_st16_stream(oq, q, soff + p * 1024, 0);
         }
     }
-    store_scales_masked<NCH>(sw, lane, c0, chunks, o, dlane, dmask);
+    store_scales_pairs<NP>(sw, lane, c0, chunks, o, dlane, dmask);
 }
 
 // ---------------------------------------------------------------------------
@@ -718,7 +733,7 @@ __device__ __forceinline__ void store_token_rows(const PermuteArgs &a, u32x4 (&v
     for (int64_t c0 = c_first; c0 < a.chunks; c0 += (int64_t)WPT * NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
         if (c0 > c_first && kFp8Mode) {
-            load_fp8_first_parts(v, xr, voff, pass);
+            load_fp8_first_parts(v, xr, lane, c0);
         } else if (c0 > c_first) {
 #pragma unroll
             for (int u = 0; u < NC; ++u) v[u] = buf_ld16_stream(xr, voff, pass + u * kWave * 16);
@@ -785,7 +800,7 @@ __device__ __forceinline__ void store_token_rows(const PermuteArgs &a, u32x4 (&v
             if (c0 == 0 && __ballot(has && !fits) != 0 && lane == 0)
                 set_status(a.status, CDL_STATUS_ROWS_OVERFLOW);
             const bool ue8m0 = (a.fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            quant_store_pass(v, lane, c0, a.chunks, a.fp8, ue8m0, dlane, __ballot(fits), xr, voff, pass);
+            quant_store_pass(v, lane, c0, a.chunks, a.fp8, ue8m0, dlane, __ballot(fits), xr);
         }
     }
 }
@@ -904,7 +919,7 @@ __global__ __launch_bounds__(TPB *WPT *kWave) void permute_kernel(PermuteArgs a)
     const rsrc_t xr = make_rsrc(a.x + (tok_valid ? t * a.chunks : 0), tok_valid ? row_bytes : 0u);
     if (MODE != kLayoutOnly) {
         if (kFp8Mode) {
-            load_fp8_first_parts(v, xr, voff, hoff);
+            load_fp8_first_parts(v, xr, lane, c_first);
         } else {
             // source rows are read once: streaming loads leave the Infinity
             // Cache to the permuted rows, which the combine reads back
@@ -1229,13 +1244,14 @@ __global__ __launch_bounds__(kWave) void layout_wave_kernel(PermuteArgs a)
 // free up), keeping the e4m3 bytes (8 per chunk per lane) until the
 // destinations are known.  The layout wave meanwhile derives the workgroup's
 // destinations (layout_one_wave) into LDS.  After the workgroup's one
-// barrier the row waves store their bytes and scales.  The quantisation,
+// barrier the row waves store their bytes and scales.  Rows are held in the
+// pair layout (quant_pair).  The quantisation,
 // about a quarter of each SIMD's time, thus overlaps the layout's latency
 // instead of following it.
 template <int TPB>
 __global__ __launch_bounds__((TPB + 1) * kWave) void permute_fp8_split_kernel(PermuteArgs a)
 {
-    constexpr int NCH = kMaxChunksFp8;
+    constexpr int NP = kMaxChunksFp8 / 2;     // 128-chunk blocks of a row, one pair per lane each
     extern __shared__ int32_t lds[];
     const int L = a.L;
     const int lane = threadIdx.x & (kWave - 1);
@@ -1248,7 +1264,7 @@ __global__ __launch_bounds__((TPB + 1) * kWave) void permute_fp8_split_kernel(Pe
     const Fp8Out &o = a.fp8;
     const bool ue8m0 = (o.flags & CDL_FP8_SCALE_UE8M0) != 0;
     bool tok_valid = false;
-    u32x2 q[NCH];
+    u32x4 q[NP];
     uint32_t sw = 0;
     if (!row_wave) {
         layout_one_wave<TPB>(a, blk, lds, lds + L, lds + 2 * L);
@@ -1259,23 +1275,31 @@ __global__ __launch_bounds__((TPB + 1) * kWave) void permute_fp8_split_kernel(Pe
         const int32_t le = local_expert(buf_ld4(r_tok, (uint32_t)lane * 4u, 0), a.expert_begin, L);
         tok_valid = real && __ballot(lane < k && le >= 0) != 0;
         if (tok_valid) {
-            const uint32_t voff = (uint32_t)lane * 16u;
+            // pair layout (quant_pair): block p, lane l holds chunks
+            // 128p + 2l and 128p + 2l + 1; the whole offset sits in the VGPR
+            // operand, which the range check covers
+            const uint32_t voff = (uint32_t)lane * 32u;
             const rsrc_t xr = make_rsrc(a.x + t * a.chunks, (uint32_t)(a.chunks * 16));
-            u32x4 v[NCH];
-            load_fp8_first_parts(v, xr, voff, 0);
+            u32x4 va[NP], vb[NP];
 #pragma unroll
-            for (int u = 0; u < NCH; ++u) {
-                // chunks past the row (H < 7168) are neither quantised nor stored
-                if ((int64_t)u * kWave < a.chunks) {
+            for (int p = 0; p < kFp8AheadPairs; ++p) {
+                va[p] = buf_ld16(xr, voff + p * 2048, 0);
+                vb[p] = buf_ld16(xr, voff + p * 2048 + 16u, 0);
+            }
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                // blocks past the row (H < 7168) are neither quantised nor stored
+                if ((int64_t)p * 128 < a.chunks) {
                     float sc;
-                    int ex;
-                    q[u] = quant_chunk(v[u], ue8m0, &sc, &ex);
-                    const uint32_t w = scale_word(o, sc, ex);
-                    sw = (lane & 15) == u ? w : sw;
+                    q[p] = quant_pair(va[p], vb[p], ue8m0, (int64_t)p * 128 + 2 * lane < a.chunks, &sc);
+                    sw = (lane & 7) == p ? __float_as_uint(sc) : sw;
                 } else {
-                    q[u] = u32x2{0u, 0u};
+                    q[p] = u32x4{0u, 0u, 0u, 0u};
                 }
-                if (u + kFp8Part < NCH) v[u + kFp8Part] = buf_ld16(xr, voff, (u + kFp8Part) * kWave * 16);
+                if (p + kFp8AheadPairs < NP) {
+                    va[p + kFp8AheadPairs] = buf_ld16(xr, voff + (p + kFp8AheadPairs) * 2048, 0);
+                    vb[p + kFp8AheadPairs] = buf_ld16(xr, voff + (p + kFp8AheadPairs) * 2048 + 16u, 0);
+                }
             }
         }
     }
@@ -1290,11 +1314,12 @@ __global__ __launch_bounds__((TPB + 1) * kWave) void permute_fp8_split_kernel(Pe
     for (uint64_t m = dmask; m; m &= m - 1) {
         const int32_t dst = __builtin_amdgcn_readlane(dlane, (int)__builtin_ctzll(m));
         const rsrc_t oq = make_rsrc(o.q + (int64_t)dst * a.chunks, q_bytes);
+        // the whole offset in the VGPR operand (see combine_rows_pipe)
 #pragma unroll
-        for (int u = 0; u < NCH; ++u)
-            if ((int64_t)u * kWave < a.chunks) buf_st8_stream(oq, q[u], (uint32_t)lane * 8u, u * kWave * 8);
+        for (int p = 0; p < NP; ++p)
+            if ((int64_t)p * 128 < a.chunks) buf_st16_stream(oq, q[p], (uint32_t)lane * 16u + p * 1024, 0);
     }
-    store_scales_masked<NCH>(sw, lane, 0, a.chunks, o, dlane, dmask);
+    store_scales_pairs<NP>(sw, lane, 0, a.chunks, o, dlane, dmask);
 }
 
 // ---------------------------------------------------------------------------
@@ -1327,7 +1352,7 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
         const uint32_t pass = (uint32_t)(c0 * 16);
         u32x4 v[NC];
         if (FP8) {
-            load_fp8_first_parts(v, xr, voff, pass);
+            load_fp8_first_parts(v, xr, lane, c0);
         } else {
 #pragma unroll
             for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
@@ -1338,7 +1363,7 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
             if (c0 == 0 && __ballot(has && !fits) != 0 && lane == 0)
                 set_status(status, CDL_STATUS_ROWS_OVERFLOW);
             const bool ue8m0 = (fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            quant_store_pass(v, lane, c0, chunks, fp8, ue8m0, dlane, __ballot(fits), xr, voff, pass);
+            quant_store_pass(v, lane, c0, chunks, fp8, ue8m0, dlane, __ballot(fits), xr);
             continue;
         }
         for (int j = 0; j < k; ++j) {
@@ -1579,15 +1604,14 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_ll(
         const uint32_t pass = (uint32_t)(c0 * 16);
         u32x4 v[NC];
         if (FP8) {
-            load_fp8_first_parts(v, xr, voff, pass);
+            load_fp8_first_parts(v, xr, lane, c0);
         } else {
 #pragma unroll
             for (int u = 0; u < NC; ++u) v[u] = buf_ld16(xr, voff, pass + u * kWave * 16);
         }
         if (FP8) {
             const bool ue8m0 = (fp8.flags & CDL_FP8_SCALE_UE8M0) != 0;
-            quant_store_pass(v, lane, c0, chunks, fp8, ue8m0, rlane, __ballot(lane < k && rlane >= 0), xr,
-                             voff, pass);
+            quant_store_pass(v, lane, c0, chunks, fp8, ue8m0, rlane, __ballot(lane < k && rlane >= 0), xr);
             continue;
         }
         for (int j = 0; j < k; ++j) {
