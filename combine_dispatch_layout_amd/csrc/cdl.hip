@@ -708,6 +708,19 @@ struct PermuteArgs {
     int32_t *ll_src2dst;
 };
 
+// The per-tensor scale s of the fp8 cast modes (the device scalar, 1 when
+// none is given) and, for a power of two whose inverse is a normal float,
+// that inverse (0 otherwise): such an s is applied by the exact product
+// x * inv, any other by a correctly rounded division.
+__device__ __forceinline__ void tensor_cast_scale(const PermuteArgs &a, float *s, float *inv)
+{
+    const float sv = a.tensor_scale ? *a.tensor_scale : 1.0f;
+    const uint32_t sb = __float_as_uint(sv);
+    const uint32_t ef = (sb >> 23) & 0xFFu;
+    *s = sv;
+    *inv = ((sb & 0x807FFFFFu) == 0 && ef >= 1 && ef <= 253) ? __uint_as_float((254u - ef) << 23) : 0.0f;
+}
+
 // Step 4 of the permutes: the wave's token row (its first pass already
 // loaded into v; fp8 modes: the first part) goes to the destinations held
 // in lanes (lane j < k: slot j's row, -1 for none), pass by pass; wave h of a
@@ -721,15 +734,8 @@ __device__ __forceinline__ void store_token_rows(const PermuteArgs &a, u32x4 (&v
     constexpr bool kFp8Mode = MODE == kRowsFp8 || MODE == kRowsLLFp8;
     const int k = a.k;
     const uint32_t row_bytes = (uint32_t)(a.chunks * 16);
-    // per-tensor cast: a power-of-two scale is applied by its exact inverse
-    // (cast_inv != 0), any other by a correctly rounded division
     float cast_s = 1.0f, cast_inv = 1.0f;      // kRowsFp8Cast1: s = 1
-    if constexpr (MODE == kRowsFp8Tensor) {
-        cast_s = a.tensor_scale ? *a.tensor_scale : 1.0f;
-        const uint32_t sb = __float_as_uint(cast_s);
-        const uint32_t ef = (sb >> 23) & 0xFFu;
-        cast_inv = ((sb & 0x807FFFFFu) == 0 && ef >= 1 && ef <= 253) ? __uint_as_float((254u - ef) << 23) : 0.0f;
-    }
+    if constexpr (MODE == kRowsFp8Tensor) tensor_cast_scale(a, &cast_s, &cast_inv);
     for (int64_t c0 = c_first; c0 < a.chunks; c0 += (int64_t)WPT * NC * kWave) {
         const uint32_t pass = (uint32_t)(c0 * 16);
         if (c0 > c_first && kFp8Mode) {
@@ -1236,9 +1242,9 @@ __global__ __launch_bounds__(kWave) void layout_wave_kernel(PermuteArgs a)
     layout_one_wave<TPB>(a, blockIdx.x, lds, lds + a.L, nullptr);
 }
 
-// The fused fp8 permute for batches with superblock counts (the count kernel
-// ran first) and rows of one pass (H <= 7168): TPB row waves and one layout
-// wave per workgroup.  A row wave loads its token's row as soon as it knows
+// The fused fp8 permutes (groups of 128 with scales, or the per-tensor cast)
+// for batches with superblock counts (the count kernel ran first) and rows
+// of one pass (H <= 7168): TPB row waves and one layout wave per workgroup.  A row wave loads its token's row as soon as it knows
 // the token has a local slot and quantises it chunk by chunk as the chunks
 // arrive (the loads of the second half issued as the first half's registers
 // free up), keeping the e4m3 bytes (8 per chunk per lane) until the
@@ -1248,9 +1254,11 @@ __global__ __launch_bounds__(kWave) void layout_wave_kernel(PermuteArgs a)
 // pair layout (quant_pair).  The quantisation,
 // about a quarter of each SIMD's time, thus overlaps the layout's latency
 // instead of following it.
-template <int TPB>
+template <int TPB, int MODE>
 __global__ __launch_bounds__((TPB + 1) * kWave) void permute_fp8_split_kernel(PermuteArgs a)
 {
+    static_assert(MODE == kRowsFp8 || MODE == kRowsFp8Tensor || MODE == kRowsFp8Cast1, "fp8 row modes");
+    constexpr bool kGroups = MODE == kRowsFp8;
     constexpr int NP = kMaxChunksFp8 / 2;     // 128-chunk blocks of a row, one pair per lane each
     extern __shared__ int32_t lds[];
     const int L = a.L;
@@ -1286,13 +1294,26 @@ __global__ __launch_bounds__((TPB + 1) * kWave) void permute_fp8_split_kernel(Pe
                 va[p] = buf_ld16(xr, voff + p * 2048, 0);
                 vb[p] = buf_ld16(xr, voff + p * 2048 + 16u, 0);
             }
+            // per-tensor cast: the scale (kRowsFp8Tensor) read once per wave
+            float cast_s = 1.0f, cast_inv = 1.0f;
+            if constexpr (MODE == kRowsFp8Tensor) tensor_cast_scale(a, &cast_s, &cast_inv);
 #pragma unroll
             for (int p = 0; p < NP; ++p) {
                 // blocks past the row (H < 7168) are neither quantised nor stored
                 if ((int64_t)p * 128 < a.chunks) {
-                    float sc;
-                    q[p] = quant_pair(va[p], vb[p], ue8m0, (int64_t)p * 128 + 2 * lane < a.chunks, &sc);
-                    sw = (lane & 7) == p ? __float_as_uint(sc) : sw;
+                    if constexpr (kGroups) {
+                        float sc;
+                        q[p] = quant_pair(va[p], vb[p], ue8m0, (int64_t)p * 128 + 2 * lane < a.chunks, &sc);
+                        sw = (lane & 7) == p ? __float_as_uint(sc) : sw;
+                    } else if (MODE == kRowsFp8Cast1 || cast_inv != 0.0f) {
+                        const u32x2 c0 = cast_chunk_fp8<true>(va[p], cast_s, cast_inv);
+                        const u32x2 c1 = cast_chunk_fp8<true>(vb[p], cast_s, cast_inv);
+                        q[p] = u32x4{c0.x, c0.y, c1.x, c1.y};
+                    } else {
+                        const u32x2 c0 = cast_chunk_fp8<false>(va[p], cast_s, cast_inv);
+                        const u32x2 c1 = cast_chunk_fp8<false>(vb[p], cast_s, cast_inv);
+                        q[p] = u32x4{c0.x, c0.y, c1.x, c1.y};
+                    }
                 } else {
                     q[p] = u32x4{0u, 0u, 0u, 0u};
                 }
@@ -1319,7 +1340,7 @@ __global__ __launch_bounds__((TPB + 1) * kWave) void permute_fp8_split_kernel(Pe
         for (int p = 0; p < NP; ++p)
             if ((int64_t)p * 128 < a.chunks) buf_st16_stream(oq, q[p], (uint32_t)lane * 16u + p * 1024, 0);
     }
-    store_scales_pairs<NP>(sw, lane, 0, a.chunks, o, dlane, dmask);
+    if constexpr (kGroups) store_scales_pairs<NP>(sw, lane, 0, a.chunks, o, dlane, dmask);
 }
 
 // ---------------------------------------------------------------------------
@@ -1980,23 +2001,28 @@ inline void launch_layout_wave(const PermuteArgs &a, const Plan &p, hipStream_t 
 
 // fp8 rows of one pass with superblock counts: a layout wave beside the
 // row waves (permute_fp8_split_kernel)
-inline void launch_fp8_split(const PermuteArgs &a, const Plan &p, hipStream_t s)
+template <int MODE>
+void launch_fp8_split(const PermuteArgs &a, const Plan &p, hipStream_t s)
 {
     const size_t lds = (size_t)(2 * a.L + p.tpb * a.k) * sizeof(int32_t);
     const dim3 grid((unsigned)(p.nblocks > 0 ? p.nblocks : 1));
     switch (p.tpb) {
-    case 1: permute_fp8_split_kernel<1><<<grid, dim3(2 * kWave), lds, s>>>(a); break;
-    case 2: permute_fp8_split_kernel<2><<<grid, dim3(3 * kWave), lds, s>>>(a); break;
-    default: permute_fp8_split_kernel<4><<<grid, dim3(5 * kWave), lds, s>>>(a); break;
+    case 1: permute_fp8_split_kernel<1, MODE><<<grid, dim3(2 * kWave), lds, s>>>(a); break;
+    case 2: permute_fp8_split_kernel<2, MODE><<<grid, dim3(3 * kWave), lds, s>>>(a); break;
+    default: permute_fp8_split_kernel<4, MODE><<<grid, dim3(5 * kWave), lds, s>>>(a); break;
     }
 }
 
 template <int MODE>
 int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
 {
-    if constexpr (MODE == kRowsFp8) {
-        if (!a.self_count && a.chunks <= (int64_t)kMaxChunksFp8 * kWave) {
-            launch_fp8_split(a, p, s);
+    if constexpr (MODE == kRowsFp8 || MODE == kRowsFp8Tensor || MODE == kRowsFp8Cast1) {
+        // rows of one pass held as whole pairs of chunks (H % 128 == 0 for
+        // groups; the per-tensor cast takes any H % 8 == 0, and a row of an
+        // odd number of chunks keeps the one-chunk path: a 16-byte store must
+        // not straddle the row end)
+        if (!a.self_count && a.chunks <= (int64_t)kMaxChunksFp8 * kWave && a.chunks % 2 == 0) {
+            launch_fp8_split<MODE>(a, p, s);
             return launch_status();
         }
     }
@@ -2017,7 +2043,9 @@ int launch_permute(PermuteArgs a, const Plan &p, hipStream_t s)
 template <int MODE>
 int run_layout(PermuteArgs a, void *ws, hipStream_t s)
 {
-    constexpr bool kFp8Rows = MODE == kRowsFp8 || MODE == kRowsLLFp8;
+    // fp8 rows (the split kernel takes up to 4 tokens per workgroup)
+    constexpr bool kFp8Rows = MODE == kRowsFp8 || MODE == kRowsLLFp8 || MODE == kRowsFp8Tensor ||
+                              MODE == kRowsFp8Cast1;
     const Plan p = make_plan(a.T, a.k, a.L, kFp8Rows ? kMaxTpbFp8 : kMaxTpbBf16);
     a.sb_counts = (const int32_t *)ws;
     a.S = p.S;

@@ -644,6 +644,10 @@ def test_dispatch_rows_of_other_dtypes(dtype):
 
 @pytest.mark.parametrize("scale", [None, 0.5, 0.37, 3.0])
 @pytest.mark.parametrize("w", [W.WORKLOADS["dsv3_prefill"].scaled(T=1000, H=512),
+                               # an odd number of 16-byte chunks (the one-chunk
+                               # path), and a last block of one pair per row
+                               W.WORKLOADS["dsv3_prefill"].scaled(T=1000, H=520),
+                               W.WORKLOADS["dsv3_prefill"].scaled(T=1000, H=1040),
                                W.WORKLOADS["tiny"],
                                W.WORKLOADS["ll_decode"].scaled(mode="normal", T=100, H=1024),
                                W.WORKLOADS["dsv3_prefill"]],
