@@ -187,6 +187,43 @@ def test_fp8_every_bf16_value_with_unit_scale():
     assert np.all(S.reshape(-1)[:ngroups] == 1.0)
 
 
+@pytest.mark.parametrize("E", [-120, -3, 0, 5, 100])
+def test_fp8_ue8m0_every_bf16_value(E):
+    """UE8M0 scales over every bf16 value: each group holds 127 values of
+    [-448, 448] scaled by 2^E (rounded to bf16) and the anchor 448 * 2^E, so
+    the group's power-of-two scale is 2^E and the conversion sees every
+    quotient the unit-scale test sees (fewer where 2^E * v underflows bf16),
+    at five exponents.  Codes and scales bit-exact."""
+    announce("fp8 UE8M0 exhaustive bf16, scale 2^%d" % E)
+    UE = cdl.FP8_SCALE_UE8M0
+    b = np.arange(1 << 16, dtype=np.uint32)
+    v = oracle.bf16_to_f32_array(b.astype(np.uint16))
+    keep = np.isfinite(v) & (np.abs(v) <= 448.0)
+    scaled = (torch.from_numpy(v[keep].astype(np.float32)) * (2.0 ** E)).to(torch.bfloat16)
+    vals = W.bf16_bits(scaled)
+    anchor = W.bf16_bits((torch.tensor([448.0]) * (2.0 ** E)).to(torch.bfloat16))[0]
+    per = 127
+    ngroups = -(-vals.size // per)
+    pad = np.zeros(ngroups * per, np.uint16)
+    pad[:vals.size] = vals
+    rows = np.concatenate([pad.reshape(ngroups, per), np.full((ngroups, 1), anchor, np.uint16)], 1)
+    H = 128 * 8
+    T = -(-ngroups // 8)
+    xb = np.zeros((T * 8, 128), np.uint16)
+    xb[:ngroups] = rows
+    xb = xb.reshape(T, H)
+    ids = torch.arange(T, dtype=torch.int32).reshape(T, 1)
+    lay = cdl.dispatch_layout(ids.to(DEV), 0, T)
+    q, s = cdl.dispatch_fp8(W.bits_to_bf16(xb).to(DEV), lay, scale_flags=UE)
+    torch.cuda.synchronize()
+    _, _, d, _ = oracle.layout(ids.numpy(), 0, T)
+    Q, S = oracle.dispatch_fp8_fmt(xb, d, 1, T, UE, rows_per_mat=T)
+    assert np.array_equal(u8(q), Q)
+    assert np.array_equal(s.detach().contiguous().cpu().view(torch.uint8).numpy().reshape(-1), S.reshape(-1))
+    sv = s.detach().cpu().numpy().reshape(-1)[:ngroups]
+    assert np.all(sv == np.float32(2.0 ** E))
+
+
 @pytest.mark.parametrize("cap_mode", ["full", "tight"])
 def test_low_latency_parity(cap_mode):
     w = W.WORKLOADS["ll_decode"]
