@@ -739,7 +739,7 @@ __device__ __forceinline__ void tensor_cast_scale(const PermuteArgs &a, float *s
 }
 
 // Step 4 of the permutes: the wave's token row (its first pass already
-// loaded into v; fp8 modes: the first part) goes to the destinations held
+// loaded into v; fp8 modes: its first pairs) goes to the destinations held
 // in lanes (lane j < k: slot j's row, -1 for none), pass by pass; wave h of a
 // token's WPT waves moves the chunks [h * NC * 64, (h + 1) * NC * 64) of
 // each pass of WPT * NC * 64 chunks, starting at chunk c_first.
@@ -831,7 +831,7 @@ __device__ __forceinline__ void store_token_rows(const PermuteArgs &a, u32x4 (&v
 // One workgroup per TPB tokens, WPT waves per token (wave h of a token moves
 // the chunks [h * NC * 64, (h + 1) * NC * 64) of each pass of its row).
 //  0. every thread loads its first batch of layout operands, then the wave
-//     of token t loads its row (all NC chunks per lane; the first part in
+//     of token t loads its row (all NC chunks per lane; the first pairs in
 //     fp8 modes) if the token has a valid slot;
 //  1. tot[e] = all valid slots of e; cur[e] = valid slots of e before this
 //     workgroup's first slot (superblock counts of earlier superblocks plus a
@@ -1261,14 +1261,14 @@ __global__ __launch_bounds__(kWave) void layout_wave_kernel(PermuteArgs a)
 
 // The fused fp8 permutes (groups of 128 with scales, or the per-tensor cast)
 // for batches with superblock counts (the count kernel ran first) and rows
-// of one pass (H <= 7168): TPB row waves and one layout wave per workgroup.  A row wave loads its token's row as soon as it knows
-// the token has a local slot and quantises it chunk by chunk as the chunks
-// arrive (the loads of the second half issued as the first half's registers
-// free up), keeping the e4m3 bytes (8 per chunk per lane) until the
+// of one pass (H <= 7168): TPB row waves and one layout wave per workgroup.
+// A row wave loads its token's row as soon as it knows the token has a local
+// slot, in the pair layout (quant_pair), and converts it pair by pair as the
+// pairs arrive (the loads of the later pairs issued as the first pairs'
+// registers free up), keeping the e4m3 bytes (16 per pair per lane) until the
 // destinations are known.  The layout wave meanwhile derives the workgroup's
 // destinations (layout_one_wave) into LDS.  After the workgroup's one
-// barrier the row waves store their bytes and scales.  Rows are held in the
-// pair layout (quant_pair).  The quantisation,
+// barrier the row waves store their bytes and scales.  The quantisation,
 // about a quarter of each SIMD's time, thus overlaps the layout's latency
 // instead of following it.
 template <int TPB, int MODE>
