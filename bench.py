@@ -321,13 +321,18 @@ def measure_fp8(torch, cdl, sets, steps):
                                  for x in sets)
     perm_bytes = statistics.mean(x.bytes_layout() + 2 * x.U * x.H + x.R * (x.H + 4 * x.H // 128)
                                  for x in sets)
+    # a device copy moving the permute's algorithmic bytes: the streaming
+    # rate of a transfer of this size, launch and ramp included
+    ceiling = copy_ceiling(torch, sets[0].x.device, perm_bytes)
     return {"workload": "fp8_dispatch (T=4096, H=7168, 32 of 256 experts, top-8, e4m3fn "
                         "groups of 128)",
             "permute_fp8_us": ms_p * 1e3, "permute_fp8_gbps": perm_bytes / (ms_p * 1e-3) / 1e9,
             "scatter_fp8_us": ms_s * 1e3, "scatter_fp8_gbps": scat_bytes / (ms_s * 1e-3) / 1e9,
             "permute_fp8_tensor_us": ms_t * 1e3,
             "permute_fp8_tensor_gbps": tens_bytes / (ms_t * 1e-3) / 1e9,
-            "fp8_tensor_format": "per-tensor cast, no scale (w8a8 permuted buffer)"}
+            "fp8_tensor_format": "per-tensor cast, no scale (w8a8 permuted buffer)",
+            "copy_same_bytes": {**ceiling, "permute_fp8_frac_of_copy":
+                                round(ceiling["us"] / (ms_p * 1e3), 4)}}
 
 
 def measure_next_rows(torch, cdl, sets, E, steps):
