@@ -5,8 +5,8 @@ crosses the sizes and options that select those paths (tokens, top-k, local
 experts and their offset, hidden size, alignment, fp8 scale format, per-tensor
 scale, low-latency capacity) so that combinations nobody wrote down are run
 too.  Every case goes through the fused and unfused normal paths, the combine,
-both fp8 formats and the low-latency calls, each compared with the oracle bit
-for bit.  Routing ids are drawn with duplicates, unrouted slots (-1), the
+both fp8 formats, the low-latency calls and the rank layout, each compared
+with the oracle bit for bit.  Routing ids are drawn with duplicates, unrouted slots (-1), the
 FlashInfer invalid id (E) and experts of other ranks; hidden rows are spread
 over binades (and some rows are zero) so that fp8 scales of many exponents
 occur.  Sizes are bounded so that the oracle finishes each case in about a
@@ -217,3 +217,23 @@ def test_random_low_latency(c):
     assert np.array_equal(npy(gmm), mm2) and np.array_equal(npy(gll), ll2)
     assert np.array_equal(u8(q).reshape(-1), Q.reshape(-1))
     assert np.array_equal(sb.cpu().numpy().reshape(-1)[:S.size], S)
+
+
+@pytest.mark.parametrize("c", CONFIGS, ids=_name)
+def test_random_rank_layout(c):
+    """rank_layout over the case's global ids with a rank count that divides
+    E (one workgroup for small batches of top-8 or less over up to 64 ranks,
+    per-workgroup partials and their reduction otherwise)."""
+    T, k, E = c["T"], c["k"], c["E"]
+    rng = np.random.default_rng(c["seed"] + 1)
+    R = int(rng.choice([r for r in (1, 2, 4, 8, 16, 32, 64, 128, 256, 1024) if E % r == 0]))
+    rpn = int(rng.choice([n for n in (1, 2, 4, 8, 16) if R % n == 0]))
+    announce("random rank layout %s R=%d rpn=%d" % (_name(c), R, rpn))
+    _, ids, _ = _inputs(c, 8)
+    rl = cdl.rank_layout(ids.to(DEV), E, R, rpn)
+    torch.cuda.synchronize()
+    pr, pn, pe, ir = oracle.rank_layout(ids.numpy(), E, R, rpn)
+    assert np.array_equal(npy(rl.num_tokens_per_rank), pr)
+    assert np.array_equal(npy(rl.num_tokens_per_rdma_rank), pn)
+    assert np.array_equal(npy(rl.num_tokens_per_expert), pe)
+    assert np.array_equal(npy(rl.is_token_in_rank), ir)
