@@ -10,7 +10,8 @@ with the oracle bit for bit.  Routing ids are drawn with duplicates, unrouted sl
 FlashInfer invalid id (E) and experts of other ranks; hidden rows are spread
 over binades (and some rows are zero) so that fp8 scales of many exponents
 occur.  Sizes are bounded so that the oracle finishes each case in about a
-second.
+second; eight larger cases (1500-4500 tokens, rows up to H = 7168) take the
+count kernel and the launch configurations of the benchmark shapes.
 """
 import numpy as np
 import pytest
@@ -53,7 +54,32 @@ def _configs(n, seed=20261203):
     return out
 
 
-CONFIGS = _configs(96)
+def _large_configs(n, seed=7168):
+    """Batches with the count kernel and rows up to one full pass (H <= 7168):
+    the launch configurations of the benchmark shapes, with random routing
+    parameters.  One local expert in 4 to 16 keeps R, and the oracle's work,
+    near T * k / 8."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.integers(1500, 4501))
+        k = int(rng.choice([4, 6, 8]))
+        E = 256
+        L = int(rng.choice([16, 32, 64]))
+        b = int(rng.integers(0, E - L + 1))
+        A = int(rng.choice([1, 1, 128]))
+        H128 = int(rng.choice([4096, 6144, 7168]))
+        H8 = int(H128 - 16 * rng.integers(0, 4))
+        Hany = int(H8 - rng.integers(0, 8))
+        flags = int(rng.choice(FORMATS))
+        scale = [None, 0.5, 0.37, 3.0, 2.0 ** -6][int(rng.integers(0, 5))]
+        skew = float(rng.choice([0.0, 1.2]))
+        out.append(dict(i=1000 + i, T=T, k=k, E=E, L=L, b=b, A=A, H128=H128, H8=H8, Hany=Hany,
+                        flags=flags, scale=scale, skew=skew, seed=int(rng.integers(1 << 30))))
+    return out
+
+
+CONFIGS = _configs(96) + _large_configs(8)
 
 
 def _name(c):
