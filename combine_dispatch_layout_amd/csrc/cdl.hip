@@ -1445,9 +1445,10 @@ __global__ __launch_bounds__(kRowThreads) void scatter_rows_kernel(
 }
 
 // fp8 rows of one pass (H <= 7168) from a given layout: one wave per token
-// holds its row (convert_held_row), then stores it to every destination.  Without the occupancy bound the compiler kept every
-// pair's temporaries live at once (212 VGPRs, 2 waves per SIMD); bounded it
-// needs 74 and no spills.
+// holds its row (convert_held_row), then stores it to every destination.
+// Without the occupancy bound the compiler kept every pair's temporaries
+// live at once (212 VGPRs, 2 waves per SIMD); bounded it needs 75 and
+// spills nothing.
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(6))) void scatter_fp8_held_kernel(
     const u32x4 *__restrict__ x, int64_t T, int64_t chunks, int32_t k,
     const int32_t *__restrict__ src2dst, Fp8Out o, int64_t cap_rows, int32_t *__restrict__ status)
