@@ -1496,3 +1496,37 @@ def test_fp8_quotient_just_above_448():
         assert np.array_equal(npy(ss).view(np.uint32), S.view(np.uint32))
     assert np.array_equal(u8(q3), Q[:64])
     assert np.array_equal(npy(s3).view(np.uint32), S.view(np.uint32)[:64])
+
+
+@pytest.mark.parametrize("path", ["dispatch", "permute"])
+@pytest.mark.parametrize("H", [1024, 7168, 8320])
+@pytest.mark.parametrize("flags", [0, UE | PK])
+def test_fp8_rows_overflow_flag(path, H, flags):
+    """fp8 rows into a buffer of cap_rows < R rows (the scatter from a given
+    layout, and the permute; 1000 tokens of top-8 take the count kernel, so
+    rows of one pass go through the held-row kernels and H = 8320 through
+    the two-pass ones): CDL_STATUS_ROWS_OVERFLOW, the first cap_rows rows and
+    their row-major scales as the oracle's, nothing written past them."""
+    w = W.WORKLOADS["fp8_dispatch"].scaled(T=1000, H=H)
+    announce("fp8 %s cap < R H=%d flags=%d" % (path, H, flags))
+    x, ids, _ = W.make_inputs(w)
+    _, s, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s[-1])
+    cap = R - 7
+    Q, S = oracle.dispatch_fp8_fmt(W.bf16_bits(x), d, w.k, R, flags, fill=0xEE)
+    nb = cdl.fp8_scale_bytes(cap, H, flags, cap)
+    q = torch.full((R, H), 0xA5, dtype=torch.uint8, device=DEV)
+    sb = torch.full((nb + 64,), 0xEE, dtype=torch.uint8, device=DEV)
+    st = status_word()
+    if path == "dispatch":
+        lay = cdl.dispatch_layout(ids.to(DEV), w.expert_begin, w.L)
+        cdl.dispatch_fp8(x.to(DEV), lay, out_q=q[:cap], out_scales=sb[:nb], status=st,
+                         scale_flags=flags)
+    else:
+        cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q[:cap],
+                        out_scales=sb[:nb], status=st, scale_flags=flags)
+    torch.cuda.synchronize()
+    assert int(st.item()) == cdl.CDL_STATUS_ROWS_OVERFLOW
+    gq, gs = u8(q), raw_bytes(sb)
+    assert np.array_equal(gq[:cap], Q[:cap]) and np.all(gq[cap:] == 0xA5)
+    assert np.array_equal(gs[:nb], S[:nb]) and np.all(gs[nb:] == 0xEE)
