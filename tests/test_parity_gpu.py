@@ -1530,3 +1530,85 @@ def test_fp8_rows_overflow_flag(path, H, flags):
     gq, gs = u8(q), raw_bytes(sb)
     assert np.array_equal(gq[:cap], Q[:cap]) and np.all(gq[cap:] == 0xA5)
     assert np.array_equal(gs[:nb], S[:nb]) and np.all(gs[nb:] == 0xEE)
+
+
+@pytest.mark.parametrize("path,T,H", [("dispatch", 1000, 1024), ("dispatch", 300, 8320),
+                                      ("permute", 1000, 1024), ("permute", 100, 1024),
+                                      ("tensor", 1000, 1024), ("ll", 128, 1024),
+                                      ("ll_onecall", 128, 1024)])
+def test_fp8_outputs_at_minimum_alignment(path, T, H):
+    """The fp8 calls accept e4m3fn rows at 8-byte and scales at 4-byte
+    alignment: outputs placed 8 (rows) and 4 (scales) bytes past a 256-byte
+    boundary give the oracle's bytes, and the bytes around them keep their
+    canaries."""
+    w = W.WORKLOADS["fp8_dispatch"].scaled(T=T, H=H)
+    announce("fp8 minimum alignment %s T=%d H=%d" % (path, T, H))
+    x, ids, _ = W.make_inputs(w)
+    xb = W.bf16_bits(x)
+    _, s, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s[-1])
+    st = status_word()
+    if path in ("ll", "ll_onecall"):
+        cap = 64
+        flags = UE | CM | PK
+        Q, S, _, _, _ = oracle.dispatch_ll_fp8(xb, ids.numpy(), w.expert_begin, w.L, cap, flags,
+                                               fill=0xEE)
+        nq, ns = w.L * cap * H, S.size
+        qbuf = torch.full((nq + 16,), 0xA5, dtype=torch.uint8, device=DEV)
+        qbuf[8:8 + nq] = 0                     # rows past masked_m keep the oracle's zeros
+        sbuf = torch.full((ns + 8,), 0xEE, dtype=torch.uint8, device=DEV)
+        q = qbuf[8:8 + nq].view(w.L, cap, H)
+        sc = sbuf[4:4 + ns]
+        if path == "ll":
+            lay = cdl.dispatch_layout(ids.to(DEV), w.expert_begin, w.L)
+            cdl.dispatch_ll_fp8(x.to(DEV), lay, cap, scale_flags=flags, out_q=q, out_scales=sc,
+                                status=st)
+        else:
+            cdl.permute_ll_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, cap, scale_flags=flags,
+                               out_q=q, out_scales=sc, status=st)
+        Qw, Sw = Q.reshape(-1), S
+    else:
+        rows = R + 3
+        if path == "tensor":
+            Qw = oracle.dispatch_fp8_tensor(xb, d, w.k, rows, fill=0xA5).reshape(-1)
+            Sw = None
+        else:
+            Q, S = oracle.dispatch_fp8(xb, d, w.k, rows)
+            Qw, Sw = Q.reshape(-1), S.reshape(-1).view(np.uint8)
+        nq = rows * H
+        qbuf = torch.full((nq + 16,), 0xA5, dtype=torch.uint8, device=DEV)
+        q = qbuf[8:8 + nq].view(rows, H)
+        if Sw is not None:
+            ns = Sw.size
+            sbuf = torch.full((ns + 8,), 0xEE, dtype=torch.uint8, device=DEV)
+            sc = sbuf[4:4 + ns]
+        if path == "dispatch":
+            lay = cdl.dispatch_layout(ids.to(DEV), w.expert_begin, w.L)
+            cdl.dispatch_fp8(x.to(DEV), lay, out_q=q, out_scales=sc, status=st)
+        elif path == "permute":
+            cdl.permute_fp8(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q, out_scales=sc,
+                            status=st)
+        else:
+            cdl.permute_fp8_tensor(x.to(DEV), ids.to(DEV), w.expert_begin, w.L, out_q=q, status=st)
+    torch.cuda.synchronize()
+    gq = u8(qbuf)
+    if path not in ("ll", "ll_onecall"):
+        assert int(st.item()) == 0
+        # rows past R are not written: the oracle's zeros there stand for the canary
+        gq_rows = gq[8:8 + nq].reshape(-1, H)
+        want = Qw.reshape(-1, H).copy()
+        if path != "tensor":
+            want[R:] = 0xA5
+        assert np.array_equal(gq_rows, want)
+    else:
+        assert np.array_equal(gq[8:8 + nq], Qw)
+    assert np.all(gq[:8] == 0xA5) and np.all(gq[8 + nq:] == 0xA5)
+    if Sw is not None:
+        gs = raw_bytes(sbuf)
+        if path in ("ll", "ll_onecall"):
+            assert np.array_equal(gs[4:4 + ns], Sw)
+        else:
+            ws_ = Sw.reshape(rows, -1).copy()
+            ws_[R:] = 0xEE
+            assert np.array_equal(gs[4:4 + ns], ws_.reshape(-1))
+        assert np.all(gs[:4] == 0xEE) and np.all(gs[4 + ns:] == 0xEE)
