@@ -1612,3 +1612,48 @@ def test_fp8_outputs_at_minimum_alignment(path, T, H):
             ws_[R:] = 0xEE
             assert np.array_equal(gs[4:4 + ns], ws_.reshape(-1))
         assert np.all(gs[:4] == 0xEE) and np.all(gs[4 + ns:] == 0xEE)
+
+
+@pytest.mark.parametrize("off", [16, 2])
+def test_bf16_rows_at_16_and_2_byte_alignment(off):
+    """bf16 rows and outputs placed off bytes past a 256-byte boundary: at 16
+    the vector kernels run, at 2 the dispatch and the combine take their
+    element-wise kernels and the permute (which needs 16-byte rows) refuses
+    the call; results are the oracle's, canaries around the outputs kept."""
+    w = W.WORKLOADS["dsv3_prefill"].scaled(T=700, H=512)
+    announce("bf16 alignment off=%d" % off)
+    x, ids, wts = W.make_inputs(w)
+    xb = W.bf16_bits(x)
+    _, s, d, _ = oracle.layout(ids.numpy(), w.expert_begin, w.L)
+    R = int(s[-1])
+    e = off // 2                                   # offset in bf16 elements
+
+    def placed(rows, fill):
+        buf = bf16_filled(1, rows * w.H + e + 8, fill).view(-1)
+        return buf, buf[e:e + rows * w.H].view(rows, w.H)
+
+    xbuf, xo = placed(w.T, 0)
+    xo.copy_(x.to(DEV))
+    lay = cdl.dispatch_layout(ids.to(DEV), w.expert_begin, w.L)
+    pbuf, P = placed(R, 0x7F7F)
+    st = status_word()
+    cdl.dispatch(xo, lay, out=P, status=st)
+    obuf, out = placed(w.T, 0x7F7F)
+    cdl.combine(P, lay.src2dst, wts.to(DEV), out=out, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    Pw = oracle.dispatch(xb, d, w.k, R)
+    gp, go = bits16(pbuf), bits16(obuf)
+    assert np.array_equal(gp[e:e + R * w.H].reshape(R, w.H), Pw)
+    assert np.all(gp[:e] == 0x7F7F) and np.all(gp[e + R * w.H:] == 0x7F7F)
+    assert np.array_equal(go[e:e + w.T * w.H].reshape(w.T, w.H),
+                          oracle.combine(Pw, d, wts.numpy(), w.T, w.k))
+    assert np.all(go[:e] == 0x7F7F) and np.all(go[e + w.T * w.H:] == 0x7F7F)
+    qbuf, Q = placed(R, 0x7F7F)
+    if off % 16 == 0:
+        cdl.permute(xo, ids.to(DEV), w.expert_begin, w.L, out=Q, status=st)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits16(qbuf)[e:e + R * w.H].reshape(R, w.H), Pw)
+    else:
+        with pytest.raises(cdl.CdlError):
+            cdl.permute(xo, ids.to(DEV), w.expert_begin, w.L, out=Q, status=st)
