@@ -1657,3 +1657,38 @@ def test_bf16_rows_at_16_and_2_byte_alignment(off):
     else:
         with pytest.raises(cdl.CdlError):
             cdl.permute(xo, ids.to(DEV), w.expert_begin, w.L, out=Q, status=st)
+
+
+def test_low_latency_capacity_zero():
+    """cap = 0: every valid slot overflows.  masked_m is all zero,
+    ll_src2dst all -1, the overflow bit is set, no row is written, and the
+    combine over the empty buffer gives +0 for every token (bf16 and fp8
+    rows, one call and separate calls)."""
+    w = W.WORKLOADS["ll_decode"].scaled(H=512)
+    announce("LL cap 0")
+    x, ids, wts = W.make_inputs(w)
+    xd, idd = x.to(DEV), ids.to(DEV)
+    lay = cdl.dispatch_layout(idd, w.expert_begin, w.L)
+    runs = []
+    st = status_word()
+    B, mm, ll = cdl.dispatch_ll(xd, lay, 0, status=st)
+    runs.append((st, mm, ll, B))
+    st = status_word()
+    _, B, mm, ll = cdl.permute_ll(xd, idd, w.expert_begin, w.L, 0, status=st)
+    runs.append((st, mm, ll, B))
+    st = status_word()
+    q, sc, mm, ll = cdl.dispatch_ll_fp8(xd, lay, 0, scale_flags=UE | CM | PK, status=st)
+    runs.append((st, mm, ll, None))
+    st = status_word()
+    _, q, sc, mm, ll = cdl.permute_ll_fp8(xd, idd, w.expert_begin, w.L, 0, scale_flags=UE | CM | PK,
+                                          status=st)
+    runs.append((st, mm, ll, None))
+    torch.cuda.synchronize()
+    for st, mm, ll, B in runs:
+        assert int(st.item()) == cdl.CDL_STATUS_LL_OVERFLOW
+        assert np.all(npy(mm) == 0) and np.all(npy(ll) == -1)
+        if B is not None:
+            assert B.numel() == 0
+            out = cdl.combine(B, ll, wts.to(DEV))
+            torch.cuda.synchronize()
+            assert np.all(bits16(out) == 0)
