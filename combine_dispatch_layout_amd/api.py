@@ -129,12 +129,21 @@ def _check(rc: int, what: str) -> None:
         raise CdlError(rc, what)
 
 
+# Every entry point has its argtypes declared (library()), so pointers pass as
+# plain ints: no ctypes object per argument.
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
+
+
+# torch's raw current-stream query: the stream handle without building a
+# torch.cuda.Stream object (a few microseconds per call otherwise)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(device: torch.device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _need_gpu(t: torch.Tensor, name: str) -> None:
